@@ -1,0 +1,156 @@
+"""CPU oracle for the Routing Mamba routed projections: ctypes wrapper over ``rom_oracle.c``.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's CPU-baseline leg
+are its only users. The HIP product path never imports this package and shares no code with it.
+
+Parity pins: every function here is checked in ``tests/test_oracle_pins.py`` against things other
+than itself (float64 brute force per token, numpy library routines for the sort and for the E=1
+dense special case, closed forms, a hand-worked example under ``tests/golden/``); the tests under
+``tests/test_oracle_mutants.py`` plant mistakes in a copy of the C source and check that a pin
+catches each one. The conventions the page leaves open (tie-break, stable order within an
+expert, the skewed workload's router bias) are pinned only by their own specification.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_DIR, "rom_oracle.c")
+LIBRARY = os.path.join(_DIR, "liborom.so")
+CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-shared", "-fPIC"]
+
+
+def build(source: str = SOURCE, output: str = LIBRARY, extra_flags=()) -> str:
+    """Compile the oracle with gcc (plain C, OpenMP over independent tokens)."""
+    cmd = ["gcc", *CFLAGS, *extra_flags, source, "-o", output + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(output + ".tmp", output)
+    return output
+
+
+_i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
+_f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+_f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+
+class Oracle:
+    """One loaded copy of the oracle library (the real one, or a test's mutant build)."""
+
+    def __init__(self, path: str = LIBRARY):
+        if path == LIBRARY and (not os.path.exists(LIBRARY)
+                                or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE)):
+            build()
+        self.path = path
+        lib = ctypes.CDLL(path)
+        lib.orom_version.restype = ctypes.c_int
+        lib.orom_route.argtypes = [_f32p, _i64, _i64, _f32p, ctypes.c_void_p, _i32, _i32,
+                                   _i32p, _f32p, _f32p, ctypes.c_void_p]
+        lib.orom_route.restype = None
+        lib.orom_sort.argtypes = [_i32p, _i64, _i32, _i32p, _i32p, _i32p, _i32p]
+        lib.orom_sort.restype = ctypes.c_int
+        lib.orom_permute.argtypes = [_f32p, _i64, _i32, _i64, _i32p, _f32p]
+        lib.orom_permute.restype = None
+        lib.orom_in_proj.argtypes = [_f32p, _i64, _i64, _i64, _i32p, _i32, _f32p, _f32p, _i32, _f64p, _f64p]
+        lib.orom_in_proj.restype = None
+        lib.orom_out_proj.argtypes = [_f64p, _f32p, _i64, _i64, _i64, _i32p, _f32p, _i32, _f32p, _i32, _f64p]
+        lib.orom_out_proj.restype = None
+        self.lib = lib
+
+    # -- router -------------------------------------------------------------------------------
+    def route(self, X, W_router, bias=None, top_k: int = 1, want_logits: bool = False):
+        """Returns dict(ids [T][K] int32, prob [T][K] fp32, gap [T] fp32, logits [T][E] fp32 or None)."""
+        X = np.ascontiguousarray(X, dtype=np.float32)
+        Wr = np.ascontiguousarray(W_router, dtype=np.float32)
+        T, dm = X.shape
+        E = Wr.shape[1]
+        assert Wr.shape[0] == dm and 1 <= top_k <= E
+        ids = np.empty((T, top_k), np.int32)
+        prob = np.empty((T, top_k), np.float32)
+        gap = np.empty((T,), np.float32)
+        logits = np.empty((T, E), np.float32) if want_logits else None
+        b = None
+        if bias is not None:
+            b = np.ascontiguousarray(bias, dtype=np.float32)
+            assert b.shape == (E,)
+        self.lib.orom_route(X, T, dm, Wr, None if b is None else b.ctypes.data, E, top_k, ids, prob, gap,
+                            None if logits is None else logits.ctypes.data)
+        return dict(ids=ids, prob=prob, gap=gap, logits=logits)
+
+    # -- grouping -------------------------------------------------------------------------------
+    def sort(self, ids, E: int):
+        """Histogram + stable counting sort of the flattened assignments ids[T][K]."""
+        ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(-1)
+        n = ids.shape[0]
+        counts = np.empty((E,), np.int32)
+        offsets = np.empty((E + 1,), np.int32)
+        perm = np.empty((n,), np.int32)
+        inv_perm = np.empty((n,), np.int32)
+        rc = self.lib.orom_sort(ids, n, E, counts, offsets, perm, inv_perm)
+        if rc != 0:
+            raise ValueError("expert id out of range")
+        return dict(counts=counts, offsets=offsets, perm=perm, inv_perm=inv_perm)
+
+    def permute(self, X, perm, top_k: int = 1):
+        X = np.ascontiguousarray(X, dtype=np.float32)
+        perm = np.ascontiguousarray(perm, dtype=np.int32)
+        out = np.empty((perm.shape[0], X.shape[1]), np.float32)
+        self.lib.orom_permute(X, perm.shape[0], top_k, X.shape[1], perm, out)
+        return out
+
+    # -- projections ----------------------------------------------------------------------------
+    def in_proj(self, X, ids, W_conv, W_gate):
+        """x, z [n][d_inner] in float64 for the n rows of X routed to ids[n][K]."""
+        X = np.ascontiguousarray(X, dtype=np.float32)
+        ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(X.shape[0], -1)
+        Wc = np.ascontiguousarray(W_conv, dtype=np.float32)
+        Wg = np.ascontiguousarray(W_gate, dtype=np.float32)
+        n, dm = X.shape
+        E, di, dm2 = Wc.shape
+        assert dm2 == dm and Wg.shape == Wc.shape
+        assert ids.size == 0 or (ids.min() >= 0 and ids.max() < E)
+        x = np.empty((n, di), np.float64)
+        z = np.empty((n, di), np.float64)
+        self.lib.orom_in_proj(X, n, dm, di, ids, ids.shape[1], Wc, Wg, E, x, z)
+        return x, z
+
+    def out_proj(self, z, h, ids, prob, W_out):
+        """out [n][d_model] in float64 for n tokens: sum_s prob * (SiLU(z) * h) W_out[ids]^T."""
+        z = np.ascontiguousarray(z, dtype=np.float64)
+        h = np.ascontiguousarray(h, dtype=np.float32)
+        n, di = z.shape
+        ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(n, -1)
+        prob = np.ascontiguousarray(prob, dtype=np.float32).reshape(n, -1)
+        Wo = np.ascontiguousarray(W_out, dtype=np.float32)
+        E, dm, di2 = Wo.shape
+        assert di2 == di and h.shape == z.shape and prob.shape == ids.shape
+        assert ids.size == 0 or (ids.min() >= 0 and ids.max() < E)
+        out = np.empty((n, dm), np.float64)
+        self.lib.orom_out_proj(z, h, n, di, dm, ids, prob, ids.shape[1], Wo, E, out)
+        return out
+
+    # -- the whole routed path for a subset of tokens --------------------------------------------
+    def forward_rows(self, inp: dict, rows: Optional[np.ndarray] = None, top_k: int = 1, routed=None):
+        """Route all tokens, then project the given rows (all rows if None). Returns a dict."""
+        r = routed if routed is not None else self.route(inp["X"], inp["W_router"], inp.get("bias"), top_k)
+        srt = self.sort(r["ids"], inp["W_router"].shape[1])
+        rows = np.arange(inp["X"].shape[0]) if rows is None else np.asarray(rows)
+        x, z = self.in_proj(inp["X"][rows], r["ids"][rows], inp["W_conv"], inp["W_gate"])
+        out = self.out_proj(z, inp["h"][rows], r["ids"][rows], r["prob"][rows], inp["W_out"])
+        return dict(route=r, sort=srt, rows=rows, x=x, z=z, out=out)
+
+
+_DEFAULT: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    global _DEFAULT
+    if _DEFAULT is None:
+        _DEFAULT = Oracle()
+    return _DEFAULT

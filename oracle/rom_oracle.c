@@ -1,0 +1,216 @@
+/*
+ * rom_oracle.c -- CPU oracle for the Routing Mamba (RoM) routed projections.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the slow, plain, obviously correct
+ * statement of what the routed projections compute. Only the test suite, the
+ * smoke check and the benchmark's CPU-baseline leg may load it. The product
+ * path (the HIP library) shares no code, header, table or helper with it.
+ *
+ * Source of the method: "Routing Mamba: Scaling State Space Models with
+ * Mixture-of-Experts Projection", landing page on chapterpal.com, Knowl 1
+ * ("RoM uses one sparse routing decision for Mamba projection experts"):
+ *   p_t   = Softmax(x_t W_r)                       over all N experts
+ *   S_t   = indices of the K largest p_t
+ *   r_t,i = p_t,i * 1[i in S_t]                    (no renormalisation over S_t)
+ *   H_t   = sum_i 1[i in S_t] x_t W_in,i           (indicator only, no p scale)
+ *   G_t   = SiLU(sum_i 1[i in S_t] x_t W_g,i)      (indicator only, no p scale)
+ *   O_t   = sum_i r_t,i (Y_t (.) G_t) W_out,i      (scaled by the router probability)
+ * SiLU is the sigmoid-weighted linear unit v * sigmoid(v) (the page's
+ * reference list: Elfwing, Uchibe and Doya, 2018).
+ *
+ * Readings where the page is silent (each is listed in the design notes):
+ *  - Storage: expert matrices are stored transposed, [out][in] (K-contiguous),
+ *    so x_t W_in,i is computed as sum_k X[t][k] * W_conv[i][n][k].
+ *  - Ties in "the K largest": the lowest expert index wins.
+ *  - The router runs in fp32: logits are fp32 sums taken in ascending k, then
+ *    the bias (a synthetic workload device; absent from the page's formula) is
+ *    added. The selection is made on these fp32 logits. The probability is the
+ *    softmax of those fp32 logits evaluated in double, rounded to fp32.
+ *  - The projections accumulate in double (no rounding beyond fp64's).
+ *  - The in-projection returns the pre-activation z; SiLU is applied where
+ *    the gate meets Y, i.e. in the out-projection. h stands in for Y_t.
+ *  - Grouping tokens by expert: a histogram, an exclusive prefix sum and a
+ *    stable counting sort (tokens keep ascending order within an expert).
+ *    The page states no grouping; a dropless grouped computation (Knowl 12:
+ *    no capacity factor, no token dropping) needs one.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (no fast-math, no
+ * FMA contraction, so each sum is the plain left-to-right sum). OpenMP splits
+ * the independent per-token loops across threads; it reorders no sum.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+int orom_version(void) { return 1; }
+
+/* ---------------------------------------------------------------------------
+ * Router (Knowl 1, first paragraph).
+ *
+ * X [T][dm] fp32, Wr [dm][E] fp32, bias [E] or NULL.
+ * Outputs per token t: ids[t][0..K) the K selected experts in order of
+ * decreasing logit (lowest index first on ties), prob[t][0..K) their softmax
+ * probabilities p_t,i (not renormalised), gap[t] = l_(K) - l_(K+1), the
+ * margin of the selection (+inf when K == E), and, if logits != NULL, the
+ * fp32 logits [T][E].
+ */
+void orom_route(const float *X, int64_t T, int64_t dm, const float *Wr, const float *bias,
+                int32_t E, int32_t K, int32_t *ids, float *prob, float *gap, float *logits)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        float *l = (float *)malloc(sizeof(float) * (size_t)E);
+        char *taken = (char *)calloc((size_t)E, 1);
+        const float *x = X + t * dm;
+        for (int32_t j = 0; j < E; ++j) {
+            float acc = 0.0f;
+            for (int64_t k = 0; k < dm; ++k)
+                acc = acc + x[k] * Wr[k * E + j];
+            if (bias)
+                acc = acc + bias[j];
+            l[j] = acc;
+        }
+        if (logits)
+            memcpy(logits + t * E, l, sizeof(float) * (size_t)E);
+
+        /* softmax in double over all E experts */
+        float lmax = l[0];
+        for (int32_t j = 1; j < E; ++j)
+            if (l[j] > lmax) lmax = l[j];
+        double denom = 0.0;
+        for (int32_t j = 0; j < E; ++j)
+            denom += exp((double)l[j] - (double)lmax);
+
+        /* the K largest, lowest index on ties (strict > scanning j upward) */
+        float last = 0.0f;
+        for (int32_t s = 0; s < K; ++s) {
+            int32_t best = -1;
+            for (int32_t j = 0; j < E; ++j) {
+                if (taken[j]) continue;
+                if (best < 0 || l[j] > l[best]) best = j;
+            }
+            taken[best] = 1;
+            ids[t * K + s] = best;
+            prob[t * K + s] = (float)(exp((double)l[best] - (double)lmax) / denom);
+            last = l[best];
+        }
+        /* margin to the best unselected expert */
+        int32_t next = -1;
+        for (int32_t j = 0; j < E; ++j) {
+            if (taken[j]) continue;
+            if (next < 0 || l[j] > l[next]) next = j;
+        }
+        gap[t] = next < 0 ? INFINITY : last - l[next];
+        free(l);
+        free(taken);
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Histogram and stable counting sort of n assignments (n = T*K; assignment a
+ * belongs to token a / K) by expert id.
+ *   counts[e]   = #{a : ids[a] = e}
+ *   offsets[0]  = 0, offsets[e+1] = offsets[e] + counts[e]
+ *   perm[pos]   = a, inv_perm[a] = pos, with pos = offsets[ids[a]] + #{a' < a : ids[a'] = ids[a]}
+ * Returns 0, or -1 if an id lies outside [0, E).
+ */
+int orom_sort(const int32_t *ids, int64_t n, int32_t E, int32_t *counts, int32_t *offsets,
+              int32_t *perm, int32_t *inv_perm)
+{
+    for (int32_t e = 0; e < E; ++e)
+        counts[e] = 0;
+    for (int64_t a = 0; a < n; ++a) {
+        if (ids[a] < 0 || ids[a] >= E) return -1;
+        counts[ids[a]] += 1;
+    }
+    offsets[0] = 0;
+    for (int32_t e = 0; e < E; ++e)
+        offsets[e + 1] = offsets[e] + counts[e];
+    int32_t *next = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    for (int32_t e = 0; e < E; ++e)
+        next[e] = offsets[e];
+    for (int64_t a = 0; a < n; ++a) {
+        int32_t pos = next[ids[a]]++;
+        perm[pos] = (int32_t)a;
+        inv_perm[a] = pos;
+    }
+    free(next);
+    return 0;
+}
+
+/* Permute: Xp[pos] = X[perm[pos] / K], rows of dm floats (slot order). */
+void orom_permute(const float *X, int64_t n, int32_t K, int64_t dm, const int32_t *perm, float *Xp)
+{
+    for (int64_t pos = 0; pos < n; ++pos)
+        memcpy(Xp + pos * dm, X + (int64_t)(perm[pos] / K) * dm, sizeof(float) * (size_t)dm);
+}
+
+/* ---------------------------------------------------------------------------
+ * In-projection (Knowl 1, H_t and the argument of SiLU in G_t) for n tokens.
+ *
+ * X [n][dm]; ids [n][K]; Wc, Wg [E][di][dm] (row n of expert i is column n
+ * of the page's W_in,i / W_g,i). Outputs x_out, z_out [n][di] in double:
+ *   x[t][c] = sum_{s<K} sum_k X[t][k] * Wc[ids[t][s]][c][k]
+ *   z[t][c] = sum_{s<K} sum_k X[t][k] * Wg[ids[t][s]][c][k]
+ * The indicator 1[i in S_t] admits exactly the K selected experts, unscaled.
+ */
+void orom_in_proj(const float *X, int64_t n, int64_t dm, int64_t di, const int32_t *ids, int32_t K,
+                  const float *Wc, const float *Wg, int32_t E, double *x_out, double *z_out)
+{
+    (void)E;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        const float *x = X + t * dm;
+        for (int64_t c = 0; c < di; ++c) {
+            double hx = 0.0, hz = 0.0;
+            for (int32_t s = 0; s < K; ++s) {
+                const int64_t i = ids[t * K + s];
+                const float *wc = Wc + (i * di + c) * dm;
+                const float *wg = Wg + (i * di + c) * dm;
+                for (int64_t k = 0; k < dm; ++k) {
+                    hx += (double)x[k] * (double)wc[k];
+                    hz += (double)x[k] * (double)wg[k];
+                }
+            }
+            x_out[t * di + c] = hx;
+            z_out[t * di + c] = hz;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Out-projection (Knowl 1, O_t) for n tokens, with h standing in for Y_t.
+ *
+ * z [n][di] (pre-activation gate), h [n][di], ids and prob [n][K],
+ * Wo [E][dm][di] (row m of expert i is column m of the page's W_out,i).
+ *   a[t][c]   = SiLU(z[t][c]) * h[t][c],  SiLU(v) = v / (1 + exp(-v))
+ *   out[t][m] = sum_{s<K} prob[t][s] * sum_c a[t][c] * Wo[ids[t][s]][m][c]
+ */
+void orom_out_proj(const double *z, const float *h, int64_t n, int64_t di, int64_t dm,
+                   const int32_t *ids, const float *prob, int32_t K, const float *Wo, int32_t E,
+                   double *out)
+{
+    (void)E;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        double *a = (double *)malloc(sizeof(double) * (size_t)di);
+        for (int64_t c = 0; c < di; ++c) {
+            const double v = z[t * di + c];
+            a[c] = v / (1.0 + exp(-v)) * (double)h[t * di + c];
+        }
+        for (int64_t m = 0; m < dm; ++m) {
+            double o = 0.0;
+            for (int32_t s = 0; s < K; ++s) {
+                const int64_t i = ids[t * K + s];
+                const float *wo = Wo + (i * dm + m) * di;
+                double acc = 0.0;
+                for (int64_t c = 0; c < di; ++c)
+                    acc += a[c] * (double)wo[c];
+                o += (double)prob[t * K + s] * acc;
+            }
+            out[t * dm + m] = o;
+        }
+        free(a);
+    }
+}
