@@ -1,0 +1,140 @@
+/*
+ * rom.h -- C ABI of the MI355X (gfx950) Routing Mamba routed-projection library (librom.so).
+ *
+ * The operations follow "Routing Mamba: Scaling State Space Models with Mixture-of-Experts
+ * Projection" as summarised on its chapterpal.com landing page, Knowl 1 ("RoM uses one sparse
+ * routing decision for Mamba projection experts"):
+ *   p_t = Softmax(x_t W_r) over N experts, S_t = the K largest, r_t,i = p_t,i 1[i in S_t];
+ *   H_t = sum_i 1[i in S_t] x_t W_in,i         G_t = SiLU(sum_i 1[i in S_t] x_t W_g,i);
+ *   O_t = sum_i r_t,i (Y_t (.) G_t) W_out,i.
+ * One router per block, shared by the Conv (input), Gate and Out projections (Knowl 1, and the
+ * authors' rebuttal on the paperhub.cn page, reply to reviewer VBDT), one of eight experts per
+ * token, dropless: no capacity factor and no token dropping (Knowl 12).
+ *
+ * Conventions for every entry point
+ *  - Pointers named in a signature are DEVICE pointers unless marked "host". The caller owns every
+ *    buffer; the library allocates nothing and keeps no state apart from a per-device property
+ *    cache. Tensors are dense, row-major, and 16-byte aligned.
+ *  - Calls enqueue kernels on `stream` (a hipStream_t; NULL is the null stream) and return without
+ *    synchronising. The projections read what rom_route wrote: run them on the same stream, or
+ *    order them after it. No count is ever read back to the host.
+ *  - Arguments are validated before anything is enqueued; on a non-OK return nothing was enqueued,
+ *    except for ROM_ERR_HIP, which reports a failed launch. rom_last_error() gives details.
+ *  - T == 0 is a valid no-op (ROM_OK, nothing enqueued, no buffer touched).
+ *  - Supported range: 1 <= E <= ROM_MAX_EXPERTS, top_k == 1, d_model and d_inner multiples of 64,
+ *    T <= ROM_MAX_TOKENS. dtype is the storage type of X, the expert stacks, z, h and all outputs;
+ *    the router weight and bias are always fp32. bf16 data is accumulated in fp32 on MFMA; fp32
+ *    data is computed in fp32 throughout.
+ *  - Expert matrices are stored transposed relative to the page's x_t W notation, as [out][in]
+ *    (K-contiguous, the nn.Linear layout): W_conv[e] is the page's W_in,e transposed.
+ *  - Results are deterministic: no floating-point atomics; the grouping is a stable counting sort.
+ */
+#ifndef ROM_H
+#define ROM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ROM_ABI_VERSION 1
+#ifndef ROM_API
+#define ROM_API __attribute__((visibility("default")))
+#endif
+#define ROM_MAX_EXPERTS 64
+#define ROM_MAX_TOKENS (1 << 24)
+
+typedef enum {
+    ROM_OK = 0,
+    ROM_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative or inconsistent size, misalignment */
+    ROM_ERR_UNSUPPORTED = 2,        /* valid but outside the supported range (top_k != 1, E > 64, ...) */
+    ROM_ERR_WORKSPACE_TOO_SMALL = 3,
+    ROM_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} rom_status;
+
+typedef enum { ROM_DTYPE_F32 = 0, ROM_DTYPE_BF16 = 1 } rom_dtype;
+
+/*
+ * The routing decision of one block for T tokens (Knowl 1: S_t and r_t,i; for top-1 these are
+ * one expert id and one probability per token), plus the grouping that the grouped projections
+ * use. A host struct of caller-owned DEVICE buffers: rom_route fills the buffers and stamps T, E
+ * and top_k; rom_in_proj and rom_out_proj read them.
+ */
+typedef struct rom_routing {
+    int32_t T, E, top_k;     /* stamped by rom_route; checked by the projections */
+    int32_t reserved;        /* zero */
+    int32_t *expert_id;      /* [T]   e*_t = argmax_j logit_t,j, lowest j on ties */
+    float *prob;             /* [T]   p_t,e*: the full softmax over E experts, not renormalised */
+    int32_t *counts;         /* [E]   tokens routed to each expert (sum = T) */
+    int32_t *offsets;        /* [E+1] exclusive prefix sum of counts; offsets[E] = T */
+    int32_t *perm;           /* [T]   slot -> token: expert-major, ascending token id within an expert */
+    int32_t *inv_perm;       /* [T]   token -> slot (perm[inv_perm[t]] == t) */
+} rom_routing;
+
+/* ROM_ABI_VERSION of the loaded library. */
+ROM_API int rom_abi_version(void);
+
+/* Bytes of device workspace rom_route needs for T tokens and E experts (0 when T == 0). */
+ROM_API size_t rom_route_workspace_bytes(int32_t T, int32_t E);
+
+/*
+ * Router, histogram, stable counting sort and (optionally) permute.
+ * Knowl 1's router: logit_t,j = sum_k X[t][k] * W_router[k][j] (+ bias[j]) in fp32 (bf16 X is
+ * widened exactly); e*_t = argmax_j logit_t,j with the lowest index on ties; prob_t =
+ * 1 / sum_j exp(logit_t,j - logit_t,e*). The grouping (not on the page; a dropless grouped
+ * computation needs it, Knowl 12): counts, offsets, and slot pos(t) = offsets[e*_t] +
+ * #{t' < t : e*_t' = e*_t}, written as perm[pos(t)] = t and inv_perm[t] = pos(t).
+ *
+ *   X         [T][d_model], x_dtype
+ *   W_router  [d_model][E] fp32;  bias [E] fp32 or NULL (a workload device; the page has none)
+ *   top_k     must be 1
+ *   routing   host pointer to a struct whose six device buffers are sized as documented above
+ *   X_perm    NULL, or [T][d_model] x_dtype: receives X_perm[pos] = X[perm[pos]] (the permute)
+ *   workspace device scratch of at least rom_route_workspace_bytes(T, E) bytes; its contents on
+ *             entry do not matter and are clobbered
+ */
+ROM_API rom_status rom_route(const void *X, rom_dtype x_dtype, int32_t T, int32_t d_model,
+                     const float *W_router, const float *bias, int32_t E, int32_t top_k,
+                     rom_routing *routing, void *X_perm, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/*
+ * In-projection experts (Knowl 1, H_t and the argument of SiLU in G_t): for every token t with
+ * expert e = expert_id[t],
+ *   x_out[t][n] = sum_k X[t][k] * W_conv[e][n][k],   z_out[t][n] = sum_k X[t][k] * W_gate[e][n][k]
+ * with no probability scale (the indicator only). Computed as one ragged grouped GEMM over the
+ * expert groups of `routing`; outputs are written in token order. z_out is the pre-activation
+ * gate: SiLU is applied by rom_out_proj.
+ *   X [T][d_model]; W_conv, W_gate [E][d_inner][d_model]; x_out, z_out [T][d_inner]; all dtype.
+ *   X may not alias an output; x_out and z_out may not overlap.
+ */
+ROM_API rom_status rom_in_proj(const void *X, const rom_routing *routing, rom_dtype dtype, int32_t T,
+                       int32_t d_model, int32_t d_inner, const void *W_conv, const void *W_gate,
+                       void *x_out, void *z_out, void *stream);
+
+/*
+ * Out-projection experts (Knowl 1, O_t), with h standing in for the SSM-core output Y_t:
+ *   a[t][n]   = SiLU(z[t][n]) * h[t][n],  SiLU(v) = v / (1 + exp(-v)), in fp32
+ *   out[t][m] = prob[t] * sum_n a[t][n] * W_out[e][m][n],  e = expert_id[t]
+ * The probability scale is r_t,e of Knowl 1 (stated only in that secondary summary: the authors'
+ * own text does not write the formula). For bf16 data, a is rounded to bf16 once before the
+ * MFMA product; accumulation is fp32; out is rounded once.
+ *   z, h [T][d_inner]; W_out [E][d_model][d_inner]; out [T][d_model]; all dtype. out may not alias z or h.
+ */
+ROM_API rom_status rom_out_proj(const void *z, const void *h, const rom_routing *routing, rom_dtype dtype,
+                        int32_t T, int32_t d_model, int32_t d_inner, const void *W_out, void *out,
+                        void *stream);
+
+/* Static description of a status code. */
+ROM_API const char *rom_status_string(rom_status s);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+ROM_API const char *rom_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROM_H */

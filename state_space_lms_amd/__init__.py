@@ -1,0 +1,198 @@
+"""MI355X-native Routing Mamba (RoM) routed projections.
+
+Python binding over ``librom.so``, the gfx950 HIP library whose C ABI is ``include/rom.h``. This module
+only marshals arguments: every step of the routed path (router, histogram, stable counting sort,
+permute, the Conv/Gate in-projection grouped GEMM and the Out-projection grouped GEMM) runs in the
+library's kernels. torch supplies device memory and the current stream. There is no CPU fallback:
+without the built library, or with tensors that are not on a ROCm device, calls raise.
+
+Method: "Routing Mamba: Scaling State Space Models with Mixture-of-Experts Projection", landing page on
+chapterpal.com, Knowl 1 (shared router; indicator-selected Conv and Gate experts; router-probability
+scaled Out experts).
+
+    r = route(X, W_router)                  # one routing decision per block ...
+    x, z = in_proj(X, r, W_conv, W_gate)    # ... shared by the in-projections ...
+    out = out_proj(z, h, r, W_out)          # ... and the out-projection (h stands in for the SSM output)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["route", "in_proj", "out_proj", "Routing", "RomError", "lib", "LIB_PATH", "ABI_VERSION",
+           "route_workspace_bytes"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "librom.so")
+ABI_VERSION = 1
+
+ROM_OK, ROM_ERR_INVALID_ARGUMENT, ROM_ERR_UNSUPPORTED, ROM_ERR_WORKSPACE_TOO_SMALL, ROM_ERR_HIP = range(5)
+ROM_DTYPE_F32, ROM_DTYPE_BF16 = 0, 1
+ABI_SYMBOLS = ("rom_abi_version", "rom_route_workspace_bytes", "rom_route", "rom_in_proj", "rom_out_proj",
+               "rom_status_string", "rom_last_error")
+
+
+class RomError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({detail})")
+        self.status = status
+
+
+class RoutingStruct(ctypes.Structure):
+    """Mirror of ``rom_routing`` in include/rom.h."""
+    _fields_ = [("T", ctypes.c_int32), ("E", ctypes.c_int32), ("top_k", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("expert_id", ctypes.c_void_p), ("prob", ctypes.c_void_p), ("counts", ctypes.c_void_p),
+                ("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p), ("inv_perm", ctypes.c_void_p)]
+
+
+_LIB = None
+_vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+
+
+def lib(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load librom.so (raises if it has not been built: python -m state_space_lms_amd.build)."""
+    global _LIB
+    if _LIB is not None and path == LIB_PATH:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m state_space_lms_amd.build` (needs hipcc)")
+    L = ctypes.CDLL(path)
+    L.rom_abi_version.restype = ctypes.c_int
+    L.rom_route_workspace_bytes.argtypes = [_i32, _i32]
+    L.rom_route_workspace_bytes.restype = _sz
+    L.rom_route.argtypes = [_vp, ctypes.c_int, _i32, _i32, _vp, _vp, _i32, _i32, ctypes.POINTER(RoutingStruct),
+                            _vp, _vp, _sz, _vp]
+    L.rom_route.restype = ctypes.c_int
+    L.rom_in_proj.argtypes = [_vp, ctypes.POINTER(RoutingStruct), ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                              _vp]
+    L.rom_in_proj.restype = ctypes.c_int
+    L.rom_out_proj.argtypes = [_vp, _vp, ctypes.POINTER(RoutingStruct), ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp]
+    L.rom_out_proj.restype = ctypes.c_int
+    L.rom_status_string.argtypes = [ctypes.c_int]
+    L.rom_status_string.restype = ctypes.c_char_p
+    L.rom_last_error.restype = ctypes.c_char_p
+    if L.rom_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"librom ABI version {L.rom_abi_version()} != {ABI_VERSION}")
+    if path == LIB_PATH:
+        _LIB = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != ROM_OK:
+        L = lib()
+        raise RomError(status, where, f"{L.rom_status_string(status).decode()}: {L.rom_last_error().decode()}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ROM_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return ROM_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: bf16 or fp32 only")
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a ROCm device tensor (there is no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else (t.data_ptr() or None)
+
+
+def _stream(device: torch.device, stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def route_workspace_bytes(T: int, E: int) -> int:
+    return int(lib().rom_route_workspace_bytes(T, E))
+
+
+class Routing:
+    """The device buffers of one routing decision (``rom_routing``), reusable across calls of the same T and E."""
+
+    def __init__(self, T: int, E: int, device, top_k: int = 1):
+        device = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.T, self.E, self.top_k, self.device = T, E, top_k, device
+        self.expert_id = torch.empty(T, **i32)
+        self.prob = torch.empty(T, dtype=torch.float32, device=device)
+        self.counts = torch.empty(E, **i32)
+        self.offsets = torch.empty(E + 1, **i32)
+        self.perm = torch.empty(T, **i32)
+        self.inv_perm = torch.empty(T, **i32)
+        self.workspace = torch.empty(max(route_workspace_bytes(T, E), 256), dtype=torch.uint8, device=device)
+        self.x_perm: Optional[torch.Tensor] = None
+        self.struct = RoutingStruct(0, E, top_k, 0, _ptr(self.expert_id), _ptr(self.prob), _ptr(self.counts),
+                                    _ptr(self.offsets), _ptr(self.perm), _ptr(self.inv_perm))
+
+
+def route(X: torch.Tensor, W_router: torch.Tensor, bias: Optional[torch.Tensor] = None, top_k: int = 1,
+          permute: bool = False, routing: Optional[Routing] = None, stream=None) -> Routing:
+    """rom_route: fp32 router, top-1, probability, histogram, stable counting sort (and the permute)."""
+    _dev(X, "X")
+    _dev(W_router, "W_router")
+    if W_router.dtype != torch.float32:
+        raise TypeError("W_router must be fp32")
+    T, dm = X.shape
+    E = W_router.shape[1]
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.float32 or bias.shape != (E,):
+            raise ValueError("bias must be fp32 of shape [E]")
+    r = routing if routing is not None else Routing(T, E, X.device, top_k)
+    if (r.T, r.E) != (T, E):
+        raise ValueError("routing buffers were sized for another T or E")
+    if permute:
+        if r.x_perm is None or r.x_perm.dtype != X.dtype or r.x_perm.shape != X.shape:
+            r.x_perm = torch.empty_like(X)
+    status = lib().rom_route(_ptr(X), _dtype_code(X), T, dm, _ptr(W_router), _ptr(bias), E, top_k,
+                             ctypes.byref(r.struct), _ptr(r.x_perm) if permute else None, _ptr(r.workspace),
+                             r.workspace.numel(), _stream(X.device, stream))
+    _check(status, "rom_route")
+    return r
+
+
+def in_proj(X: torch.Tensor, routing: Routing, W_conv: torch.Tensor, W_gate: torch.Tensor,
+            x_out: Optional[torch.Tensor] = None, z_out: Optional[torch.Tensor] = None,
+            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """rom_in_proj: x = W_conv[e] X, z = W_gate[e] X per token (token order, no probability scale)."""
+    for t, n in ((X, "X"), (W_conv, "W_conv"), (W_gate, "W_gate")):
+        _dev(t, n)
+    T, dm = X.shape
+    E, di, dm2 = W_conv.shape
+    if dm2 != dm or W_gate.shape != W_conv.shape or W_conv.dtype != X.dtype or W_gate.dtype != X.dtype:
+        raise ValueError("W_conv/W_gate must be [E][d_inner][d_model] in X's dtype")
+    if E != routing.E:
+        raise ValueError("expert count differs from the routing's")
+    x_out = torch.empty((T, di), dtype=X.dtype, device=X.device) if x_out is None else _dev(x_out, "x_out")
+    z_out = torch.empty((T, di), dtype=X.dtype, device=X.device) if z_out is None else _dev(z_out, "z_out")
+    status = lib().rom_in_proj(_ptr(X), ctypes.byref(routing.struct), _dtype_code(X), T, dm, di, _ptr(W_conv),
+                               _ptr(W_gate), _ptr(x_out), _ptr(z_out), _stream(X.device, stream))
+    _check(status, "rom_in_proj")
+    return x_out, z_out
+
+
+def out_proj(z: torch.Tensor, h: torch.Tensor, routing: Routing, W_out: torch.Tensor,
+             out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """rom_out_proj: out = p_t * W_out[e] (SiLU(z) * h) per token (token order)."""
+    for t, n in ((z, "z"), (h, "h"), (W_out, "W_out")):
+        _dev(t, n)
+    T, di = z.shape
+    E, dm, di2 = W_out.shape
+    if di2 != di or h.shape != z.shape or h.dtype != z.dtype or W_out.dtype != z.dtype:
+        raise ValueError("W_out must be [E][d_model][d_inner]; z, h [T][d_inner]; one dtype")
+    if E != routing.E:
+        raise ValueError("expert count differs from the routing's")
+    out = torch.empty((T, dm), dtype=z.dtype, device=z.device) if out is None else _dev(out, "out")
+    status = lib().rom_out_proj(_ptr(z), _ptr(h), ctypes.byref(routing.struct), _dtype_code(z), T, dm, di,
+                                _ptr(W_out), _ptr(out), _stream(z.device, stream))
+    _check(status, "rom_out_proj")
+    return out

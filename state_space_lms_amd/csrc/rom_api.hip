@@ -1,0 +1,197 @@
+// rom_api.hip -- the C ABI of librom (declared in include/rom.h): argument validation, status codes,
+// and dispatch to the gfx950 kernels. Every check runs before the first HIP call, so invalid
+// arguments enqueue nothing and need no GPU.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "rom.h"
+#include "rom_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+rom_status fail(rom_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+rom_status hip_fail(hipError_t err, const char *what) {
+    return fail(ROM_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(err), (int)err);
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_size(rom_dtype dt) { return dt == ROM_DTYPE_BF16 ? 2 : 4; }
+
+bool overlap(const void *a, size_t an, const void *b, size_t bn) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + bn && y < x + an;
+}
+
+#define ROM_CHECK_PTR(p, align)                                                                      \
+    do {                                                                                             \
+        if ((p) == nullptr) return fail(ROM_ERR_INVALID_ARGUMENT, "%s is NULL", #p);                 \
+        if (!aligned((p), (align)))                                                                  \
+            return fail(ROM_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", #p, (int)(align));    \
+    } while (0)
+
+rom_status check_dims(int32_t T, int32_t d, const char *dname) {
+    if (T < 0) return fail(ROM_ERR_INVALID_ARGUMENT, "T = %d is negative", T);
+    if (T > ROM_MAX_TOKENS) return fail(ROM_ERR_UNSUPPORTED, "T = %d exceeds ROM_MAX_TOKENS", T);
+    if (d <= 0) return fail(ROM_ERR_INVALID_ARGUMENT, "%s = %d must be positive", dname, d);
+    if (d % 64 != 0) return fail(ROM_ERR_UNSUPPORTED, "%s = %d is not a multiple of 64", dname, d);
+    return ROM_OK;
+}
+
+rom_status check_dtype(int dt) {
+    if (dt != ROM_DTYPE_F32 && dt != ROM_DTYPE_BF16) return fail(ROM_ERR_INVALID_ARGUMENT, "unknown dtype %d", dt);
+    return ROM_OK;
+}
+
+rom_status check_experts(int32_t E, int32_t top_k) {
+    if (E < 1) return fail(ROM_ERR_INVALID_ARGUMENT, "E = %d must be at least 1", E);
+    if (E > ROM_MAX_EXPERTS) return fail(ROM_ERR_UNSUPPORTED, "E = %d exceeds ROM_MAX_EXPERTS (%d)", E, ROM_MAX_EXPERTS);
+    if (top_k < 1 || top_k > E) return fail(ROM_ERR_INVALID_ARGUMENT, "top_k = %d outside [1, E]", top_k);
+    if (top_k != 1) return fail(ROM_ERR_UNSUPPORTED, "top_k = %d: only top-1 routing is implemented", top_k);
+    return ROM_OK;
+}
+
+// The projections' view of a routing struct filled by rom_route.
+rom_status check_routing_for_proj(const rom_routing *r, int32_t T) {
+    if (r == nullptr) return fail(ROM_ERR_INVALID_ARGUMENT, "routing is NULL");
+    if (r->T != T) return fail(ROM_ERR_INVALID_ARGUMENT, "routing->T = %d but T = %d", r->T, T);
+    rom_status s = check_experts(r->E, r->top_k);
+    if (s != ROM_OK) return s;
+    if (T > 0) {
+        ROM_CHECK_PTR(r->offsets, 4);
+        ROM_CHECK_PTR(r->perm, 4);
+        ROM_CHECK_PTR(r->prob, 4);
+    }
+    return ROM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rom_abi_version(void) { return ROM_ABI_VERSION; }
+
+size_t rom_route_workspace_bytes(int32_t T, int32_t E) {
+    if (T <= 0 || E <= 0) return 0;
+    const size_t b = (size_t)E * (size_t)rom::route_workgroups(T) * sizeof(int32_t);
+    return (b + 255) & ~(size_t)255;
+}
+
+rom_status rom_route(const void *X, rom_dtype x_dtype, int32_t T, int32_t d_model, const float *W_router,
+                     const float *bias, int32_t E, int32_t top_k, rom_routing *routing, void *X_perm,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+    g_last_error[0] = '\0';
+    rom_status s;
+    if ((s = check_dtype(x_dtype)) != ROM_OK) return s;
+    if ((s = check_dims(T, d_model, "d_model")) != ROM_OK) return s;
+    if ((s = check_experts(E, top_k)) != ROM_OK) return s;
+    if (routing == nullptr) return fail(ROM_ERR_INVALID_ARGUMENT, "routing is NULL");
+    if (T == 0) {
+        routing->T = 0;
+        routing->E = E;
+        routing->top_k = top_k;
+        return ROM_OK;
+    }
+    ROM_CHECK_PTR(X, 16);
+    ROM_CHECK_PTR(W_router, 16);
+    if (bias != nullptr && !aligned(bias, 4)) return fail(ROM_ERR_INVALID_ARGUMENT, "bias is not 4-byte aligned");
+    ROM_CHECK_PTR(routing->expert_id, 4);
+    ROM_CHECK_PTR(routing->prob, 4);
+    ROM_CHECK_PTR(routing->counts, 4);
+    ROM_CHECK_PTR(routing->offsets, 4);
+    ROM_CHECK_PTR(routing->perm, 4);
+    ROM_CHECK_PTR(routing->inv_perm, 4);
+    if (X_perm != nullptr) {
+        if (!aligned(X_perm, 16)) return fail(ROM_ERR_INVALID_ARGUMENT, "X_perm is not 16-byte aligned");
+        const size_t xb = (size_t)T * d_model * elem_size(x_dtype);
+        if (overlap(X, xb, X_perm, xb)) return fail(ROM_ERR_INVALID_ARGUMENT, "X_perm overlaps X");
+    }
+    const size_t need = rom_route_workspace_bytes(T, E);
+    if (T > rom::kRouteSmallT) {
+        if (workspace == nullptr) return fail(ROM_ERR_WORKSPACE_TOO_SMALL, "workspace is NULL (%zu bytes needed)", need);
+        if (!aligned(workspace, 4)) return fail(ROM_ERR_INVALID_ARGUMENT, "workspace is not 4-byte aligned");
+    }
+    if (workspace_bytes < need && T > rom::kRouteSmallT)
+        return fail(ROM_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    routing->T = T;
+    routing->E = E;
+    routing->top_k = top_k;
+    routing->reserved = 0;
+    hipError_t err = rom::launch_route(X, x_dtype, T, d_model, W_router, bias, E, *routing, X_perm,
+                                       static_cast<int32_t *>(workspace), static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, "rom_route launch");
+    return ROM_OK;
+}
+
+rom_status rom_in_proj(const void *X, const rom_routing *routing, rom_dtype dtype, int32_t T, int32_t d_model,
+                       int32_t d_inner, const void *W_conv, const void *W_gate, void *x_out, void *z_out,
+                       void *stream) {
+    g_last_error[0] = '\0';
+    rom_status s;
+    if ((s = check_dtype(dtype)) != ROM_OK) return s;
+    if ((s = check_dims(T, d_model, "d_model")) != ROM_OK) return s;
+    if ((s = check_dims(T, d_inner, "d_inner")) != ROM_OK) return s;
+    if ((s = check_routing_for_proj(routing, T)) != ROM_OK) return s;
+    if (T == 0) return ROM_OK;
+    ROM_CHECK_PTR(X, 16);
+    ROM_CHECK_PTR(W_conv, 16);
+    ROM_CHECK_PTR(W_gate, 16);
+    ROM_CHECK_PTR(x_out, 16);
+    ROM_CHECK_PTR(z_out, 16);
+    const size_t es = elem_size(dtype);
+    const size_t xb = (size_t)T * d_model * es, ob = (size_t)T * d_inner * es;
+    if (overlap(x_out, ob, z_out, ob)) return fail(ROM_ERR_INVALID_ARGUMENT, "x_out and z_out overlap");
+    if (overlap(X, xb, x_out, ob) || overlap(X, xb, z_out, ob))
+        return fail(ROM_ERR_INVALID_ARGUMENT, "X overlaps an output");
+    hipError_t err = rom::launch_in_proj(X, *routing, dtype, T, d_model, d_inner, W_conv, W_gate, x_out, z_out,
+                                         static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, "rom_in_proj launch");
+    return ROM_OK;
+}
+
+rom_status rom_out_proj(const void *z, const void *h, const rom_routing *routing, rom_dtype dtype, int32_t T,
+                        int32_t d_model, int32_t d_inner, const void *W_out, void *out, void *stream) {
+    g_last_error[0] = '\0';
+    rom_status s;
+    if ((s = check_dtype(dtype)) != ROM_OK) return s;
+    if ((s = check_dims(T, d_model, "d_model")) != ROM_OK) return s;
+    if ((s = check_dims(T, d_inner, "d_inner")) != ROM_OK) return s;
+    if ((s = check_routing_for_proj(routing, T)) != ROM_OK) return s;
+    if (T == 0) return ROM_OK;
+    ROM_CHECK_PTR(z, 16);
+    ROM_CHECK_PTR(h, 16);
+    ROM_CHECK_PTR(W_out, 16);
+    ROM_CHECK_PTR(out, 16);
+    const size_t es = elem_size(dtype);
+    const size_t ib = (size_t)T * d_inner * es, ob = (size_t)T * d_model * es;
+    if (overlap(out, ob, z, ib) || overlap(out, ob, h, ib))
+        return fail(ROM_ERR_INVALID_ARGUMENT, "out overlaps z or h");
+    hipError_t err = rom::launch_out_proj(z, h, *routing, dtype, T, d_model, d_inner, W_out, out,
+                                          static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, "rom_out_proj launch");
+    return ROM_OK;
+}
+
+const char *rom_status_string(rom_status s) {
+    switch (s) {
+        case ROM_OK: return "ROM_OK";
+        case ROM_ERR_INVALID_ARGUMENT: return "ROM_ERR_INVALID_ARGUMENT";
+        case ROM_ERR_UNSUPPORTED: return "ROM_ERR_UNSUPPORTED";
+        case ROM_ERR_WORKSPACE_TOO_SMALL: return "ROM_ERR_WORKSPACE_TOO_SMALL";
+        case ROM_ERR_HIP: return "ROM_ERR_HIP";
+    }
+    return "unknown rom_status";
+}
+
+const char *rom_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// rom_device.h -- device helpers shared by the gfx950 kernels of librom (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rom {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// bf16 <-> fp32. Widening is exact (the bf16 bits are the high half of the fp32 word).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16, round to nearest even (gfx950 converts natively).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+// Two fp32 -> packed bf16 pair (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
+}
+
+// Eight consecutive elements widened to fp32 (p is 16-byte aligned for bf16, 32-byte for fp32).
+__device__ __forceinline__ void load8_f32(const uint16_t *p, float f[8]) {
+    uint4 v = *reinterpret_cast<const uint4 *>(p);
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+__device__ __forceinline__ void load8_f32(const float *p, float f[8]) {
+    float4 a = reinterpret_cast<const float4 *>(p)[0];
+    float4 b = reinterpret_cast<const float4 *>(p)[1];
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int l = lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// SiLU(v) = v / (1 + exp(-v)), the sigmoid-weighted linear unit.
+__device__ __forceinline__ float silu_precise(float v) { return v / (1.0f + expf(-v)); }
+__device__ __forceinline__ float silu_fast(float v) { return v * __frcp_rn(1.0f + __expf(-v)); }
+
+}  // namespace rom

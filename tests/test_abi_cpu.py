@@ -1,0 +1,135 @@
+"""The C ABI without a GPU: librom.so loads, exports what include/rom.h declares, and validates arguments
+before any HIP call (so these run on a machine with no GPU at all)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import state_space_lms_amd as rom
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rom.h")
+
+A = 0x10000  # fake, 16-byte-aligned "device" addresses: never dereferenced on these error paths
+OK, INVALID, UNSUPPORTED, WS_SMALL = rom.ROM_OK, rom.ROM_ERR_INVALID_ARGUMENT, rom.ROM_ERR_UNSUPPORTED, \
+    rom.ROM_ERR_WORKSPACE_TOO_SMALL
+BF16 = rom.ROM_DTYPE_BF16
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(rom.LIB_PATH):
+        from state_space_lms_amd import build
+        build.build()
+    return rom.lib()
+
+
+def declared_symbols():
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"ROM_API\s+[\w\s\*]*?\b(rom_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_symbols()
+    assert set(names) == set(rom.ABI_SYMBOLS), names
+    for n in names:
+        assert hasattr(L, n), f"{n} missing from librom.so"
+
+
+def test_version_and_status_strings(L):
+    assert L.rom_abi_version() == rom.ABI_VERSION
+    for code, name in enumerate(["ROM_OK", "ROM_ERR_INVALID_ARGUMENT", "ROM_ERR_UNSUPPORTED",
+                                 "ROM_ERR_WORKSPACE_TOO_SMALL", "ROM_ERR_HIP"]):
+        assert L.rom_status_string(code).decode() == name
+
+
+def test_workspace_bytes(L):
+    assert L.rom_route_workspace_bytes(0, 8) == 0
+    for T, E in [(1, 8), (257, 8), (16384, 8), (65536, 64)]:
+        b = L.rom_route_workspace_bytes(T, E)
+        assert b >= E * ((T + 255) // 256) * 4 and b % 256 == 0
+
+
+def _routing(T=512, E=8, **over):
+    f = dict(expert_id=A, prob=A, counts=A, offsets=A, perm=A, inv_perm=A)
+    f.update(over)
+    return rom.RoutingStruct(T, E, 1, 0, f["expert_id"], f["prob"], f["counts"], f["offsets"], f["perm"],
+                             f["inv_perm"])
+
+
+def _route(L, X=A, dt=BF16, T=512, dm=128, Wr=A, bias=None, E=8, k=1, r="default", Xp=None, ws=A, wsb=1 << 20):
+    rs = _routing(T, E) if r == "default" else r
+    ref = ctypes.byref(rs) if rs is not None else None
+    return L.rom_route(X, dt, T, dm, Wr, bias, E, k, ref, Xp, ws, wsb, None), rs
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), INVALID), (dict(E=0), INVALID), (dict(E=65), UNSUPPORTED), (dict(k=2), UNSUPPORTED),
+    (dict(k=0), INVALID), (dict(k=9), INVALID), (dict(dm=0), INVALID), (dict(dm=96), UNSUPPORTED),
+    (dict(dt=7), INVALID), (dict(X=None), INVALID), (dict(X=A + 8), INVALID), (dict(Wr=None), INVALID),
+    (dict(r=None), INVALID), (dict(bias=A + 2), INVALID), (dict(ws=None), WS_SMALL), (dict(wsb=16), WS_SMALL),
+    (dict(Xp=A + 4096), INVALID),  # overlaps X
+    (dict(T=(1 << 24) + 1), UNSUPPORTED),
+])
+def test_route_rejects(L, kw, code):
+    st, _ = _route(L, **kw)
+    assert st == code
+    assert L.rom_last_error().decode() != ""
+
+
+def test_route_rejects_null_routing_buffer(L):
+    for field in ("expert_id", "prob", "counts", "offsets", "perm", "inv_perm"):
+        st, _ = _route(L, r=_routing(512, 8, **{field: None}))
+        assert st == INVALID and field in L.rom_last_error().decode()
+
+
+def test_route_T0_is_noop_and_stamps(L):
+    rs = rom.RoutingStruct(99, 0, 0, 0, None, None, None, None, None, None)
+    st, _ = _route(L, X=None, Wr=None, T=0, r=rs, ws=None, wsb=0)
+    assert st == OK and (rs.T, rs.E, rs.top_k) == (0, 8, 1)
+
+
+def _in(L, X=A, T=512, dm=128, di=256, Wc=A, Wg=A, xo=A + (1 << 24), zo=A + (1 << 26), r=None, dt=BF16):
+    rs = r if r is not None else _routing(T, 8)
+    return L.rom_in_proj(X, ctypes.byref(rs), dt, T, dm, di, Wc, Wg, xo, zo, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), INVALID), (dict(di=100), UNSUPPORTED), (dict(dm=0), INVALID), (dict(X=None), INVALID),
+    (dict(Wc=A + 2), INVALID), (dict(zo=None), INVALID), (dict(zo=A + (1 << 24) + 64), INVALID),
+    (dict(xo=A + 256), INVALID), (dict(r=_routing(256, 8)), INVALID), (dict(r=_routing(512, 0)), INVALID),
+    (dict(r=_routing(512, 8, offsets=None)), INVALID), (dict(dt=3), INVALID),
+])
+def test_in_proj_rejects(L, kw, code):
+    assert _in(L, **kw) == code
+
+
+def test_in_proj_T0_noop(L):
+    assert _in(L, X=None, T=0, Wc=None, Wg=None, xo=None, zo=None, r=_routing(0, 8)) == OK
+
+
+def _out(L, z=A, h=A + (1 << 24), T=512, dm=128, di=256, Wo=A, o=A + (1 << 26), r=None):
+    rs = r if r is not None else _routing(T, 8)
+    return L.rom_out_proj(z, h, ctypes.byref(rs), BF16, T, dm, di, Wo, o, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-5), INVALID), (dict(dm=32), UNSUPPORTED), (dict(h=None), INVALID), (dict(o=A + 512), INVALID),
+    (dict(o=A + (1 << 24)), INVALID), (dict(r=_routing(512, 8, perm=None)), INVALID), (dict(Wo=A + 1), INVALID),
+])
+def test_out_proj_rejects(L, kw, code):
+    assert _out(L, **kw) == code
+
+
+def test_binding_has_no_cpu_path(L):
+    import torch
+    X = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        rom.route(X, torch.zeros(64, 8))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        rom.lib(os.path.join(tmp_path, "librom.so"))

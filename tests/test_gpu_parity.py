@@ -1,0 +1,186 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Small shapes compare every token; the full workload shapes compare sampled tokens (the first and last
+slots of every expert group, slots around M-tile boundaries, and a seeded random sample), with routing
+and grouping compared for every token.
+"""
+import numpy as np
+import pytest
+
+import parity
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rom():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm GPU visible")
+    import state_space_lms_amd as rom_mod
+    rom_mod.lib()  # raises if the HIP library is not built: there is no fallback
+    return rom_mod
+
+
+def _run_chain(rom, w, inp, permute=False, isolated=True):
+    import torch
+    d = lambda k: parity.to_device(inp[k], w.dtype) if k != "W_router" else parity.to_device(inp[k], "f32")
+    X, Wr, Wc, Wg, Wo, h = d("X"), d("W_router"), d("W_conv"), d("W_gate"), d("W_out"), d("h")
+    bias = parity.to_device(inp["bias"], "f32") if inp.get("bias") is not None else None
+    r = rom.route(X, Wr, bias, permute=permute)
+    x, z = rom.in_proj(X, r, Wc, Wg)
+    out = rom.out_proj(z, h, r, Wo)
+    out_iso = None
+    if isolated and inp.get("z") is not None:
+        out_iso = rom.out_proj(parity.to_device(inp["z"], w.dtype), h, r, Wo)
+    torch.cuda.synchronize()
+    return dict(r=r, X=X, x=x, z=z, out=out, out_iso=out_iso)
+
+
+def _route_host(r):
+    return {k: parity.to_host(getattr(r, k)) for k in ("expert_id", "prob", "counts", "offsets", "perm", "inv_perm")}
+
+
+def _rows(t, rows):
+    import torch
+    idx = torch.as_tensor(rows, dtype=torch.long, device=t.device)
+    return parity.to_host(t.index_select(0, idx))
+
+
+def check_workload(rom, orc, w, inp=None, rows=None, label=""):
+    """Full comparison of one workload; rows=None compares every token."""
+    inp = inp if inp is not None else workloads.make_inputs(w)
+    tol = parity.TOL[w.dtype]
+    print(f"[parity] {label or w.name}: T={w.T} d_model={w.d_model} d_inner={w.d_inner} E={w.E} {w.dtype}",
+          flush=True)
+    g = _run_chain(rom, w, inp)
+    gr = _route_host(g["r"])
+    o_route = orc.route(inp["X"], inp["W_router"], inp.get("bias"))
+    o_sort = orc.sort(o_route["ids"], w.E)
+    rep = parity.check_route(gr, o_route, o_sort, w.T, w.E, tol)
+    if rows is None:
+        rows = np.arange(w.T)
+    ids_o = o_route["ids"][:, 0]
+    agree = gr["expert_id"][rows] == ids_o[rows]
+    rows = rows[agree]
+    x_o, z_o = orc.in_proj(inp["X"][rows], o_route["ids"][rows], inp["W_conv"], inp["W_gate"])
+    ex = parity.norm_max_err(_rows(g["x"], rows), x_o)
+    ez = parity.norm_max_err(_rows(g["z"], rows), z_o)
+    out_o = orc.out_proj(z_o, inp["h"][rows], o_route["ids"][rows], o_route["prob"][rows], inp["W_out"])
+    eo = parity.norm_max_err(_rows(g["out"], rows), out_o)
+    ei = 0.0
+    if g["out_iso"] is not None:
+        out_i = orc.out_proj(inp["z"][rows].astype(np.float64), inp["h"][rows], o_route["ids"][rows],
+                             o_route["prob"][rows], inp["W_out"])
+        ei = parity.norm_max_err(_rows(g["out_iso"], rows), out_i)
+    print(f"[parity]   excluded(gap<1e-4)={rep.n_excluded} id-mismatch={rep.n_id_mismatch_excluded} "
+          f"prob={rep.prob_err:.2e} x={ex:.2e} z={ez:.2e} out={eo:.2e} out_isolated={ei:.2e} rows={len(rows)}",
+          flush=True)
+    for name, err in (("x", ex), ("z", ez), ("out", eo), ("out_isolated", ei)):
+        assert err <= tol, f"{name}: normalised max error {err:.3g} > {tol}"
+    return g, gr, o_route, o_sort
+
+
+# ------------------------------------------------------------------------------------------------
+# small shapes: every token
+
+SMALL = [
+    workloads.get_workload("tiny_f32"),
+    workloads.custom_workload("bf16_tiles", T=1000, d_model=256, d_inner=384, E=8, seed=101),
+    workloads.custom_workload("bf16_bn64_E3", T=777, d_model=192, d_inner=320, E=3, seed=102),
+    workloads.custom_workload("bf16_E1_dense", T=300, d_model=128, d_inner=256, E=1, seed=103),
+    workloads.custom_workload("bf16_T1", T=1, d_model=256, d_inner=256, E=8, seed=104),
+    workloads.custom_workload("bf16_T127", T=127, d_model=128, d_inner=128, E=8, seed=105),
+    workloads.custom_workload("bf16_T129", T=129, d_model=128, d_inner=128, E=8, seed=106),
+    workloads.custom_workload("bf16_T256_small_route", T=256, d_model=256, d_inner=128, E=8, seed=107),
+    workloads.custom_workload("bf16_T257_multi_wg_route", T=257, d_model=256, d_inner=128, E=8, seed=108),
+    workloads.custom_workload("bf16_E64", T=3000, d_model=128, d_inner=128, E=64, seed=109),
+    workloads.custom_workload("bf16_E16_T2000", T=2000, d_model=320, d_inner=192, E=16, seed=110),
+    workloads.custom_workload("f32_E5", T=333, d_model=128, d_inner=192, E=5, dtype="f32", seed=111),
+    workloads.custom_workload("f32_T1000_E8", T=1000, d_model=64, d_inner=128, E=8, dtype="f32", seed=112),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_small_shapes(rom, oracle, w):
+    check_workload(rom, oracle, w)
+
+
+def test_all_tokens_on_one_expert(rom, oracle):
+    w = workloads.custom_workload("one_expert", T=900, d_model=128, d_inner=256, E=8, seed=120)
+    bias = np.zeros(8, np.float32)
+    bias[5] = 1e3
+    inp = workloads.make_inputs(w, router_bias=bias)
+    _, gr, _, _ = check_workload(rom, oracle, w, inp, label="all tokens on expert 5")
+    assert gr["counts"][5] == w.T
+
+
+def test_empty_experts(rom, oracle):
+    w = workloads.custom_workload("empty_experts", T=700, d_model=128, d_inner=128, E=8, seed=121)
+    bias = np.zeros(8, np.float32)
+    bias[[0, 2, 7]] = -1e3
+    inp = workloads.make_inputs(w, router_bias=bias)
+    _, gr, _, _ = check_workload(rom, oracle, w, inp, label="experts 0, 2, 7 empty")
+    assert gr["counts"][0] == gr["counts"][2] == gr["counts"][7] == 0
+
+
+def test_tied_logits_lowest_index_and_exact_prob(rom, oracle):
+    """W_router = 0: every logit ties; both sides pick expert 0 and p = 1/E exactly."""
+    w = workloads.custom_workload("ties", T=500, d_model=128, d_inner=128, E=8, seed=122)
+    inp = workloads.make_inputs(w)
+    inp["W_router"] = np.zeros_like(inp["W_router"])
+    g = _run_chain(rom, w, inp, isolated=False)
+    gr = _route_host(g["r"])
+    assert np.all(gr["expert_id"] == 0) and np.all(gr["prob"] == np.float32(0.125))
+    np.testing.assert_array_equal(gr["perm"], np.arange(w.T))
+
+
+def test_deterministic_and_permute(rom, oracle):
+    """Two runs are bit-identical; the materialised permute is X[perm] exactly."""
+    w = workloads.custom_workload("determinism", T=3000, d_model=256, d_inner=256, E=8, seed=123)
+    inp = workloads.make_inputs(w)
+    a = _run_chain(rom, w, inp, permute=True, isolated=False)
+    b = _run_chain(rom, w, inp, permute=True, isolated=False)
+    for k in ("x", "z", "out"):
+        np.testing.assert_array_equal(parity.to_host(a[k]), parity.to_host(b[k]))
+    for k in ("expert_id", "prob", "perm", "inv_perm"):
+        np.testing.assert_array_equal(parity.to_host(getattr(a["r"], k)), parity.to_host(getattr(b["r"], k)))
+    perm = parity.to_host(a["r"].perm)
+    np.testing.assert_array_equal(parity.to_host(a["r"].x_perm), inp["X"][perm])
+    o_route = oracle.route(inp["X"], inp["W_router"])
+    o_sort = oracle.sort(o_route["ids"], w.E)
+    if np.array_equal(parity.to_host(a["r"].expert_id), o_route["ids"][:, 0]):
+        np.testing.assert_array_equal(parity.to_host(a["r"].x_perm), oracle.permute(inp["X"], o_sort["perm"]))
+
+
+def test_zero_tokens(rom):
+    import torch
+    X = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    Wr = torch.zeros((128, 8), dtype=torch.float32, device="cuda")
+    r = rom.route(X, Wr)
+    W = torch.zeros((8, 128, 128), dtype=torch.bfloat16, device="cuda")
+    x, z = rom.in_proj(X, r, W, W)
+    out = rom.out_proj(z, z.clone(), r, W)
+    torch.cuda.synchronize()
+    assert x.shape == (0, 128) and out.shape == (0, 128)
+
+
+# ------------------------------------------------------------------------------------------------
+# full workload shapes: routing for every token, projections on sampled tokens
+
+FULL = ["samba421m", "rom1p3b", "skewed", "decode_T1", "decode_T8", "decode_T64"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_workload(rom, oracle, name):
+    w = workloads.get_workload(name)
+    inp = workloads.make_inputs(w, which={"X", "W_router", "W_conv", "W_gate", "W_out", "h", "z"}
+                                if w.T <= 64 else {"X", "W_router", "W_conv", "W_gate", "W_out", "h"})
+    o_route = oracle.route(inp["X"], inp["W_router"], inp.get("bias"))
+    o_sort = oracle.sort(o_route["ids"], w.E)
+    rows = parity.sample_rows(o_sort, w.T) if w.T > 64 else None
+    _, gr, _, _ = check_workload(rom, oracle, w, inp, rows=rows)
+    if w.skew is not None:
+        frac = gr["counts"] / w.T
+        assert np.max(np.abs(frac - np.array(w.skew))) <= 0.0025, f"skewed loads {frac}"
