@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the Routing Mamba (RoM) routed-projection hot path on one MI355X.
+
+One step = the whole routed path over one batch of synthetic tokens, through the C ABI:
+    rom_route    fp32 router logits + softmax + top-1 + probability, histogram, scan, stable scatter
+    rom_in_proj  Conv/Gate expert grouped GEMM (bf16 MFMA), rows gathered through perm, un-permuted
+    rom_out_proj Out expert grouped GEMM on SiLU(z)*h, scaled by the router probability, un-permuted
+(Routing Mamba landing page on chapterpal.com, Knowl 1.) Inputs are resident in HBM before timing.
+
+Default workload: the Samba-421M-like block, T = 4 x 4096 tokens, d_model 1024, d_inner 2048, 8 experts,
+bf16 data. Prints ONE JSON line: whole-step tokens/s, the roofline of the dominant kernel (the
+in-projection grouped GEMM, timed live with HIP events on the stream it runs on), and the CPU oracle
+timed on a bounded sample of the same workload on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--cold]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed-projection tokens/sec + % bf16 MFMA peak (GEMM) / % HBM peak (decode)"
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA peaks
+PEAK_HBM_GBS = 8000.0                                # MI355X HBM3E
+KERNEL_SOURCES = ["state_space_lms_amd/csrc/rom_gemm.hip", "state_space_lms_amd/csrc/rom_device.h"]
+COUNTERS_FILE = "profiles/counters_in_proj_{workload}.txt"
+COPY_PROBE_BYTES = 256 << 20
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per in-projection launch from committed rocprofv3 counters, or None when the counters
+    are missing or were taken on another version of the kernel source."""
+    path = os.path.join(ROOT, COUNTERS_FILE.format(workload=workload))
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(rec["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, w, target_seconds: float):
+    """The CPU oracle as it stands, timed on a bounded prefix of the workload's tokens."""
+    import numpy as np
+    import oracle
+    orc = oracle.default()
+
+    def run(n):
+        t0 = time.perf_counter()
+        r = orc.route(inp["X"][:n], inp["W_router"], inp.get("bias"))
+        orc.sort(r["ids"], w.E)
+        x, z = orc.in_proj(inp["X"][:n], r["ids"], inp["W_conv"], inp["W_gate"])
+        orc.out_proj(z, inp["h"][:n], r["ids"], r["prob"], inp["W_out"])
+        return time.perf_counter() - t0
+
+    probe = min(w.T, 32)
+    tp = run(probe)
+    n = int(max(probe, min(w.T, probe * target_seconds / max(tp, 1e-6))))
+    dt = run(n) if n > probe else tp
+    return {"value": n / dt, "unit": "tokens/s", "cores": orc.threads(), "kind": "oracle",
+            "sample": f"first {n} of {w.T} tokens: route + histogram/sort + in_proj + out_proj in plain C "
+                      f"(fp32 router, fp64 projection sums, OpenMP over tokens), {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="samba421m")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cold", action="store_true", help="evict the 256 MB MALL before every step (decode)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the routed projections of a token need no data "
+              "from other GPUs, and no multi-GPU path is built); run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import state_space_lms_amd as rom
+    import workloads
+
+    w = workloads.get_workload(args.workload)
+    inp = workloads.make_inputs(w, which={"X", "W_router", "W_conv", "W_gate", "W_out", "h"})
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(a, dt):
+        if dt == "bf16":
+            return torch.from_numpy(workloads.bf16_bits(a).view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    X, h = up(inp["X"], w.dtype), up(inp["h"], w.dtype)
+    Wc, Wg, Wo = up(inp["W_conv"], w.dtype), up(inp["W_gate"], w.dtype), up(inp["W_out"], w.dtype)
+    Wr = up(inp["W_router"], "f32")
+    bias = up(inp["bias"], "f32") if inp.get("bias") is not None else None
+    routing = rom.Routing(w.T, w.E, dev)
+    x = torch.empty((w.T, w.d_inner), dtype=X.dtype, device=dev)
+    z = torch.empty_like(x)
+    out = torch.empty((w.T, w.d_model), dtype=X.dtype, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.cold else None
+
+    # plain copy of known size: the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters
+    cp_src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    torch.neg(cp_src, out=cp_dst)
+    del cp_src, cp_dst
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        rom.route(X, Wr, bias, routing=routing, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        rom.in_proj(X, routing, Wc, Wg, x, z, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        rom.out_proj(z, h, routing, Wo, out, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        if flush is not None:
+            flush.zero_()
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    if flush is None:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            step(events[k])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    else:
+        # cold cache: the eviction runs between steps and stays outside the timed sum
+        elapsed = 0.0
+        for k in range(args.steps):
+            flush.zero_()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            step(events[k])
+            torch.cuda.synchronize()
+            elapsed += time.perf_counter() - t0
+
+    t_route = np.array([e[0].elapsed_time(e[1]) for e in events]) * 1e-3
+    t_in = np.array([e[1].elapsed_time(e[2]) for e in events]) * 1e-3
+    t_out = np.array([e[2].elapsed_time(e[3]) for e in events]) * 1e-3
+    fl_in = 4.0 * w.T * w.d_model * w.d_inner
+    fl_out = 2.0 * w.T * w.d_model * w.d_inner
+    peak = PEAK_MFMA_TFLOPS[w.dtype]
+    counts = routing.counts.cpu().numpy()
+    es = 2 if w.dtype == "bf16" else 4
+    used = int(np.count_nonzero(counts))
+    # algorithmic bytes: every operand and result moved once, only the experts that received tokens
+    bytes_in = es * (w.T * w.d_model + used * 2 * w.d_inner * w.d_model + 2 * w.T * w.d_inner)
+    bytes_out = es * (2 * w.T * w.d_inner + used * w.d_model * w.d_inner + w.T * w.d_model) + 4 * w.T * 2
+    bytes_route = es * w.T * w.d_model + 4 * w.d_model * w.E + 4 * w.T * 4
+    ms_per_step = elapsed / args.steps * 1e3
+    mean_in, mean_out, mean_route = float(t_in.mean()), float(t_out.mean()), float(t_route.mean())
+
+    decode = w.T <= 64
+    if decode:
+        achieved = (bytes_in / mean_in) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = fl_in / mean_in / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+    roof["traffic"] = measured_traffic(w.name)
+    roof["kernel"] = "k_grouped_gemm_bf16 (rom_in_proj)" if w.dtype == "bf16" else "k_grouped_gemm_f32 (rom_in_proj)"
+    roof["algorithmic"] = ({"bytes_per_launch": bytes_in} if decode else {"flops_per_launch": fl_in})
+    roof["launch_us"] = round(mean_in * 1e6, 2)
+
+    result = {
+        "metric": METRIC,
+        "value": round(w.T * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded Gaussian tensors of the workload's shapes (no dataset)",
+        "config": {"workload": w.name, "T": w.T, "d_model": w.d_model, "d_inner": w.d_inner, "E": w.E,
+                   "top_k": 1, "router": "fp32", "cache": "cold" if args.cold else "warm",
+                   "expert_loads": counts.tolist()},
+        "roofline": roof,
+        "breakdown": {
+            "route_us": round(mean_route * 1e6, 2),
+            "in_proj_us": round(mean_in * 1e6, 2),
+            "out_proj_us": round(mean_out * 1e6, 2),
+            "in_proj_tflops": round(fl_in / mean_in / 1e12, 1),
+            "out_proj_tflops": round(fl_out / mean_out / 1e12, 1),
+            "gemm_mfma_frac": round((fl_in + fl_out) / (mean_in + mean_out) / 1e12 / peak, 4),
+            "route_gbs": round(bytes_route / mean_route / 1e9, 1),
+            "in_proj_gbs": round(bytes_in / mean_in / 1e9, 1),
+            "out_proj_gbs": round(bytes_out / mean_out / 1e9, 1),
+            "step_hbm_frac": round((bytes_route + bytes_in + bytes_out) / (mean_route + mean_in + mean_out)
+                                   / 1e9 / PEAK_HBM_GBS, 4),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define ROM_ABI_VERSION 1
+#define ROM_ABI_VERSION 2
 #ifndef ROM_API
 #define ROM_API __attribute__((visibility("default")))
 #endif
@@ -114,18 +114,24 @@ ROM_API rom_status rom_in_proj(const void *X, const rom_routing *routing, rom_dt
                        int32_t d_model, int32_t d_inner, const void *W_conv, const void *W_gate,
                        void *x_out, void *z_out, void *stream);
 
+/* Bytes of device workspace rom_out_proj needs (0 when it needs none: fp32 data, or T <= 64). */
+ROM_API size_t rom_out_proj_workspace_bytes(int32_t T, int32_t d_inner, rom_dtype dtype);
+
 /*
  * Out-projection experts (Knowl 1, O_t), with h standing in for the SSM-core output Y_t:
  *   a[t][n]   = SiLU(z[t][n]) * h[t][n],  SiLU(v) = v / (1 + exp(-v)), in fp32
  *   out[t][m] = prob[t] * sum_n a[t][n] * W_out[e][m][n],  e = expert_id[t]
  * The probability scale is r_t,e of Knowl 1 (stated only in that secondary summary: the authors'
  * own text does not write the formula). For bf16 data, a is rounded to bf16 once before the
- * MFMA product; accumulation is fp32; out is rounded once.
+ * MFMA product; accumulation is fp32; out is rounded once. For bf16 data with T > 64 the gated rows
+ * a are first written, in slot order, to the workspace, which the grouped GEMM then streams.
  *   z, h [T][d_inner]; W_out [E][d_model][d_inner]; out [T][d_model]; all dtype. out may not alias z or h.
+ *   workspace  device scratch of at least rom_out_proj_workspace_bytes(T, d_inner, dtype) bytes
+ *              (may be NULL when that is 0); contents on entry do not matter and are clobbered.
  */
 ROM_API rom_status rom_out_proj(const void *z, const void *h, const rom_routing *routing, rom_dtype dtype,
                         int32_t T, int32_t d_model, int32_t d_inner, const void *W_out, void *out,
-                        void *stream);
+                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static description of a status code. */
 ROM_API const char *rom_status_string(rom_status s);

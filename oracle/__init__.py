@@ -50,6 +50,7 @@ class Oracle:
         self.path = path
         lib = ctypes.CDLL(path)
         lib.orom_version.restype = ctypes.c_int
+        lib.orom_threads.restype = ctypes.c_int
         lib.orom_route.argtypes = [_f32p, _i64, _i64, _f32p, ctypes.c_void_p, _i32, _i32,
                                    _i32p, _f32p, _f32p, ctypes.c_void_p]
         lib.orom_route.restype = None
@@ -62,6 +63,10 @@ class Oracle:
         lib.orom_out_proj.argtypes = [_f64p, _f32p, _i64, _i64, _i64, _i32p, _f32p, _i32, _f32p, _i32, _f64p]
         lib.orom_out_proj.restype = None
         self.lib = lib
+
+    def threads(self) -> int:
+        """OpenMP threads the oracle's per-token loops run on."""
+        return int(self.lib.orom_threads())
 
     # -- router -------------------------------------------------------------------------------
     def route(self, X, W_router, bias=None, top_k: int = 1, want_logits: bool = False):

@@ -39,11 +39,24 @@
  * the independent per-token loops across threads; it reorders no sum.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 int orom_version(void) { return 1; }
+
+/* Threads the OpenMP loops below use (reporting only). */
+int orom_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
+}
 
 /* ---------------------------------------------------------------------------
  * Router (Knowl 1, first paragraph).

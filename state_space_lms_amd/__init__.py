@@ -23,15 +23,15 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["route", "in_proj", "out_proj", "Routing", "RomError", "lib", "LIB_PATH", "ABI_VERSION",
-           "route_workspace_bytes"]
+           "route_workspace_bytes", "out_proj_workspace_bytes"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "librom.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 ROM_OK, ROM_ERR_INVALID_ARGUMENT, ROM_ERR_UNSUPPORTED, ROM_ERR_WORKSPACE_TOO_SMALL, ROM_ERR_HIP = range(5)
 ROM_DTYPE_F32, ROM_DTYPE_BF16 = 0, 1
-ABI_SYMBOLS = ("rom_abi_version", "rom_route_workspace_bytes", "rom_route", "rom_in_proj", "rom_out_proj",
-               "rom_status_string", "rom_last_error")
+ABI_SYMBOLS = ("rom_abi_version", "rom_route_workspace_bytes", "rom_route", "rom_in_proj",
+               "rom_out_proj_workspace_bytes", "rom_out_proj", "rom_status_string", "rom_last_error")
 
 
 class RomError(RuntimeError):
@@ -68,7 +68,10 @@ def lib(path: str = LIB_PATH) -> ctypes.CDLL:
     L.rom_in_proj.argtypes = [_vp, ctypes.POINTER(RoutingStruct), ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                               _vp]
     L.rom_in_proj.restype = ctypes.c_int
-    L.rom_out_proj.argtypes = [_vp, _vp, ctypes.POINTER(RoutingStruct), ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp]
+    L.rom_out_proj_workspace_bytes.argtypes = [_i32, _i32, ctypes.c_int]
+    L.rom_out_proj_workspace_bytes.restype = _sz
+    L.rom_out_proj.argtypes = [_vp, _vp, ctypes.POINTER(RoutingStruct), ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp,
+                               _sz, _vp]
     L.rom_out_proj.restype = ctypes.c_int
     L.rom_status_string.argtypes = [ctypes.c_int]
     L.rom_status_string.restype = ctypes.c_char_p
@@ -130,6 +133,7 @@ class Routing:
         self.inv_perm = torch.empty(T, **i32)
         self.workspace = torch.empty(max(route_workspace_bytes(T, E), 256), dtype=torch.uint8, device=device)
         self.x_perm: Optional[torch.Tensor] = None
+        self.out_workspace: Optional[torch.Tensor] = None  # gated rows for rom_out_proj, sized on first use
         self.struct = RoutingStruct(0, E, top_k, 0, _ptr(self.expert_id), _ptr(self.prob), _ptr(self.counts),
                                     _ptr(self.offsets), _ptr(self.perm), _ptr(self.inv_perm))
 
@@ -180,8 +184,14 @@ def in_proj(X: torch.Tensor, routing: Routing, W_conv: torch.Tensor, W_gate: tor
     return x_out, z_out
 
 
+def out_proj_workspace_bytes(T: int, d_inner: int, dtype: torch.dtype) -> int:
+    code = ROM_DTYPE_BF16 if dtype == torch.bfloat16 else ROM_DTYPE_F32
+    return int(lib().rom_out_proj_workspace_bytes(T, d_inner, code))
+
+
 def out_proj(z: torch.Tensor, h: torch.Tensor, routing: Routing, W_out: torch.Tensor,
-             out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             stream=None) -> torch.Tensor:
     """rom_out_proj: out = p_t * W_out[e] (SiLU(z) * h) per token (token order)."""
     for t, n in ((z, "z"), (h, "h"), (W_out, "W_out")):
         _dev(t, n)
@@ -192,7 +202,13 @@ def out_proj(z: torch.Tensor, h: torch.Tensor, routing: Routing, W_out: torch.Te
     if E != routing.E:
         raise ValueError("expert count differs from the routing's")
     out = torch.empty((T, dm), dtype=z.dtype, device=z.device) if out is None else _dev(out, "out")
+    need = out_proj_workspace_bytes(T, di, z.dtype)
+    if workspace is None and need > 0:
+        if routing.out_workspace is None or routing.out_workspace.numel() < need:
+            routing.out_workspace = torch.empty(need, dtype=torch.uint8, device=z.device)
+        workspace = routing.out_workspace
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     status = lib().rom_out_proj(_ptr(z), _ptr(h), ctypes.byref(routing.struct), _dtype_code(z), T, dm, di,
-                                _ptr(W_out), _ptr(out), _stream(z.device, stream))
+                                _ptr(W_out), _ptr(out), _ptr(workspace), wsb, _stream(z.device, stream))
     _check(status, "rom_out_proj")
     return out

@@ -158,8 +158,14 @@ rom_status rom_in_proj(const void *X, const rom_routing *routing, rom_dtype dtyp
     return ROM_OK;
 }
 
+size_t rom_out_proj_workspace_bytes(int32_t T, int32_t d_inner, rom_dtype dtype) {
+    if (T <= 0 || d_inner <= 0 || (dtype != ROM_DTYPE_F32 && dtype != ROM_DTYPE_BF16)) return 0;
+    return rom::out_proj_workspace_bytes(T, d_inner, dtype);
+}
+
 rom_status rom_out_proj(const void *z, const void *h, const rom_routing *routing, rom_dtype dtype, int32_t T,
-                        int32_t d_model, int32_t d_inner, const void *W_out, void *out, void *stream) {
+                        int32_t d_model, int32_t d_inner, const void *W_out, void *out, void *workspace,
+                        size_t workspace_bytes, void *stream) {
     g_last_error[0] = '\0';
     rom_status s;
     if ((s = check_dtype(dtype)) != ROM_OK) return s;
@@ -175,7 +181,16 @@ rom_status rom_out_proj(const void *z, const void *h, const rom_routing *routing
     const size_t ib = (size_t)T * d_inner * es, ob = (size_t)T * d_model * es;
     if (overlap(out, ob, z, ib) || overlap(out, ob, h, ib))
         return fail(ROM_ERR_INVALID_ARGUMENT, "out overlaps z or h");
-    hipError_t err = rom::launch_out_proj(z, h, *routing, dtype, T, d_model, d_inner, W_out, out,
+    const size_t need = rom::out_proj_workspace_bytes(T, d_inner, dtype);
+    if (need > 0) {
+        if (workspace == nullptr || workspace_bytes < need)
+            return fail(ROM_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed",
+                        workspace == nullptr ? (size_t)0 : workspace_bytes, need);
+        if (!aligned(workspace, 16)) return fail(ROM_ERR_INVALID_ARGUMENT, "workspace is not 16-byte aligned");
+        if (overlap(workspace, need, z, ib) || overlap(workspace, need, h, ib) || overlap(workspace, need, out, ob))
+            return fail(ROM_ERR_INVALID_ARGUMENT, "workspace overlaps z, h or out");
+    }
+    hipError_t err = rom::launch_out_proj(z, h, *routing, dtype, T, d_model, d_inner, W_out, out, workspace,
                                           static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return hip_fail(err, "rom_out_proj launch");
     return ROM_OK;

@@ -43,6 +43,12 @@ __device__ __forceinline__ void load8_f32(const float *p, float f[8]) {
     f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane i of the wave writes
+// LDS bytes [lds + 16*i, lds + 16*i + 16). lds must be the same for every lane of the wave.
+__device__ __forceinline__ void dma16_to_lds(const void *src, void *lds) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {

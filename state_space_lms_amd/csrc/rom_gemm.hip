@@ -17,6 +17,8 @@
 // buffers: the next A/B tiles are fetched into registers while the current ones feed the MFMAs.
 // LDS rows are 128 bytes of 8 16-byte chunks, chunk c of row r stored at position c ^ (r & 7), so
 // the 16-byte MFMA operand reads of 8 consecutive rows hit 8 different bank groups.
+#include <stdlib.h>
+
 #include "rom_device.h"
 #include "rom_internal.h"
 
@@ -59,21 +61,61 @@ __device__ __forceinline__ bool locate_mtile(const int32_t *__restrict__ offsets
 }
 
 // ---------------------------------------------------------------------------------------------
-// bf16 MFMA grouped GEMM. OUT = false: in-projection; OUT = true: out-projection.
-template <int BM, int BN, bool OUT>
-__global__ __launch_bounds__(256) void k_grouped_gemm_bf16(GemmArgs p) {
-    constexpr int BK = 64;
-    constexpr int KCH = BK / 8;              // 16-byte chunks per LDS row
-    constexpr int RPP = 256 / KCH;           // rows one 16-byte load per thread covers
-    constexpr int A_LD = BM / RPP, B_LD = BN / RPP;
-    constexpr int WM = BM / 2, WN = BN / 2;  // wave block
+// bf16 MFMA grouped GEMM. OUT = false: in-projection, A rows are the tokens' X rows (gathered
+// through perm). OUT = true: out-projection, A rows are the gated rows a = bf16(SiLU(z) * h) that
+// k_gate_permute has already laid out in slot order, and results are scaled by p_t.
+//
+// Block tile BM x BN, K step BK (64 or 32), NSTAGE LDS stages, WGM x WGN waves, each wave owning a
+// (BM/WGM) x (BN/WGN) block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16, fp32 accumulators).
+//
+// Staging: A and B rows are copied global -> LDS directly (global_load_lds_dwordx4: lane i of a
+// wave writes 16 bytes at LDS base + 16*i), NSTAGE-1 K steps ahead of the MFMAs, with no register
+// round trip; before each step a wave waits only until its copies for that step have landed
+// (vmcnt counts the later steps' copies still in flight), then the workgroup meets at a barrier.
+// LDS rows hold BK bf16 values as BK/8 16-byte chunks; chunk c of row r sits at c ^ swz(r) so the
+// MFMA operand reads (8 lanes = 8 consecutive rows, one chunk each) spread over all bank groups.
+//
+// The MFMA computes the transposed tile C^T = W A^T (W operand first): a lane's 16 accumulators of
+// a 32x32 block belong to ONE token row (lane % 32) and hold 4 runs of 4 consecutive output columns,
+// so the epilogue scales them by that token's probability and writes 8-byte packed stores straight
+// to the token's output row (the un-permute).
+template <int KCH>
+__device__ __forceinline__ int lds_swz(int row) {
+    return KCH == 8 ? (row & 7) : ((row >> 1) & 3);
+}
+
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n and lgkmcnt == 0, expcnt untouched.
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4); }
+
+// Wait until at most `ahead` K steps of copies (PER_STEP instructions each) are still in flight.
+template <int PER_STEP, int MAXAHEAD>
+__device__ __forceinline__ void wait_copies(int ahead) {
+    static_assert(PER_STEP * MAXAHEAD < 64, "vmcnt range");
+    if (MAXAHEAD >= 3 && ahead >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(3 * PER_STEP));
+    else if (MAXAHEAD >= 2 && ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * PER_STEP));
+    else if (MAXAHEAD >= 1 && ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(PER_STEP));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+}
+
+template <int BM, int BN, int BK, int NSTAGE, int WGM, int WGN, bool OUT>
+__global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p) {
+    constexpr int NW = WGM * WGN;
+    constexpr int NT = 64 * NW;
+    constexpr int KCH = BK / 8;                     // 16-byte chunks per LDS row
+    constexpr int RG = 64 / KCH;                    // rows covered by one wave-wide 1 KiB copy
+    constexpr int A_DMA = BM / RG / NW;             // copy instructions per wave per K step
+    constexpr int B_DMA = BN / RG / NW;
+    constexpr int PER_STEP = A_DMA + B_DMA;
+    constexpr int STAGE = (BM + BN) * BK;           // bf16 elements per stage
+    constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int FM = WM / 32, FN = WN / 32;
-    static_assert(BM % RPP == 0 && BN % RPP == 0 && FM >= 1 && FN >= 1, "tile shape");
+    static_assert(BK == 64 || BK == 32, "BK");
+    static_assert((BM / RG) % NW == 0 && A_DMA >= 1 && (BN / RG) % NW == 0 && B_DMA >= 1, "copy split");
+    static_assert(NSTAGE >= 2 && NSTAGE <= 5 && FM >= 1 && FN >= 1, "shape");
 
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-    uint16_t *As = smem;                     // [2][BM*BK]
-    uint16_t *Bs = smem + 2 * BM * BK;       // [2][BN*BK]
     __shared__ int s_tok[BM];
+    __shared__ int s_arow[BM];
     __shared__ float s_prob[OUT ? BM : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -86,70 +128,44 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_bf16(GemmArgs p) {
     const uint16_t *Bsrc = static_cast<const uint16_t *>(which ? p.B1 : p.B0) + ((size_t)e * p.N0 + n0) * K;
     uint16_t *C = static_cast<uint16_t *>(which ? p.C1 : p.C0);
 
-    for (int i = tid; i < BM; i += 256) {
-        const int tok = i < rows ? p.perm[slot0 + i] : -1;
+    // rows past the group's end repeat its last row (in-bounds, finite data); they are never stored
+    for (int i = tid; i < BM; i += NT) {
+        const int slot = slot0 + min(i, rows - 1);
+        const int tok = p.perm[slot];
         s_tok[i] = tok;
-        if (OUT) s_prob[i] = tok >= 0 ? p.prob[tok] : 0.0f;
+        s_arow[i] = OUT ? slot : tok;
+        if (OUT) s_prob[i] = p.prob[tok];
     }
     __syncthreads();
 
-    // global -> register slots: thread loads 16 bytes of row (lr + i*RPP), chunk lc
-    const int lr = tid / KCH, lc = tid % KCH;
-    const uint16_t *a_src[A_LD];
-    const uint16_t *h_src[OUT ? A_LD : 1];
-    int a_dst[A_LD], b_dst[B_LD];
+    // ---- per-lane copy sources. Copy group g covers rows [g*RG, g*RG+RG); lane i fills row
+    // g*RG + i/KCH, physical chunk i%KCH, i.e. logical chunk (i%KCH) ^ swz(row).
+    const int dr = lane / KCH, dpc = lane % KCH;
+    const uint16_t *a_dma[A_DMA];
+    const uint16_t *b_dma[B_DMA];
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-        const int r = lr + i * RPP;
-        const int tok = s_tok[r];
-        a_src[i] = tok >= 0 ? static_cast<const uint16_t *>(p.A0) + (size_t)tok * K + lc * 8 : nullptr;
-        if (OUT) h_src[i] = tok >= 0 ? static_cast<const uint16_t *>(p.A1) + (size_t)tok * K + lc * 8 : nullptr;
-        a_dst[i] = (r * KCH + (lc ^ (r & 7))) * 8;
+    for (int j = 0; j < A_DMA; ++j) {
+        const int row = (wave * A_DMA + j) * RG + dr;
+        const int c = dpc ^ lds_swz<KCH>(row);
+        a_dma[j] = static_cast<const uint16_t *>(p.A0) + (size_t)s_arow[row] * K + c * 8;
     }
-    const uint16_t *b_src[B_LD];
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-        const int r = lr + i * RPP;
-        b_src[i] = Bsrc + (size_t)r * K + lc * 8;
-        b_dst[i] = (r * KCH + (lc ^ (r & 7))) * 8;
+    for (int j = 0; j < B_DMA; ++j) {
+        const int row = (wave * B_DMA + j) * RG + dr;
+        const int c = dpc ^ lds_swz<KCH>(row);
+        b_dma[j] = Bsrc + (size_t)row * K + c * 8;
     }
-
-    uint4 ra[A_LD], rh[OUT ? A_LD : 1], rb[B_LD];
-    auto load_tiles = [&](int k0) {
+    auto issue_copies = [&](int kt, int stage) {
+        uint16_t *as = smem + stage * STAGE;
+        uint16_t *bs = as + BM * BK;
+        const int k0 = kt * BK;
 #pragma unroll
-        for (int i = 0; i < A_LD; ++i) {
-            ra[i] = a_src[i] ? *reinterpret_cast<const uint4 *>(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
-            if (OUT) rh[i] = h_src[i] ? *reinterpret_cast<const uint4 *>(h_src[i] + k0) : make_uint4(0, 0, 0, 0);
-        }
+        for (int j = 0; j < A_DMA; ++j) dma16_to_lds(a_dma[j] + k0, as + (wave * A_DMA + j) * RG * BK);
 #pragma unroll
-        for (int i = 0; i < B_LD; ++i) rb[i] = *reinterpret_cast<const uint4 *>(b_src[i] + k0);
-    };
-    auto store_tiles = [&](int buf) {
-        uint16_t *as = As + buf * BM * BK;
-        uint16_t *bs = Bs + buf * BN * BK;
-#pragma unroll
-        for (int i = 0; i < A_LD; ++i) {
-            uint4 v = ra[i];
-            if (OUT) {
-                // a = bf16(SiLU(z) * h), fp32 arithmetic
-                const uint32_t zw[4] = {v.x, v.y, v.z, v.w};
-                const uint32_t hw[4] = {rh[i].x, rh[i].y, rh[i].z, rh[i].w};
-                uint32_t o[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float z0 = __uint_as_float(zw[q] << 16), z1 = __uint_as_float(zw[q] & 0xFFFF0000u);
-                    const float h0 = __uint_as_float(hw[q] << 16), h1 = __uint_as_float(hw[q] & 0xFFFF0000u);
-                    o[q] = pack_bf16x2(silu_fast(z0) * h0, silu_fast(z1) * h1);
-                }
-                v = make_uint4(o[0], o[1], o[2], o[3]);
-            }
-            *reinterpret_cast<uint4 *>(as + a_dst[i]) = v;
-        }
-#pragma unroll
-        for (int i = 0; i < B_LD; ++i) *reinterpret_cast<uint4 *>(bs + b_dst[i]) = rb[i];
+        for (int j = 0; j < B_DMA; ++j) dma16_to_lds(b_dma[j] + k0, bs + (wave * B_DMA + j) * RG * BK);
     };
 
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
     f32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -158,56 +174,246 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_bf16(GemmArgs p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int nk = K / BK;
-    load_tiles(0);
-    store_tiles(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) load_tiles((kt + 1) * BK);
-        const uint16_t *as = As + buf * BM * BK;
-        const uint16_t *bs = Bs + buf * BN * BK;
+    // fragment addresses (element offsets within a stage); rows of a fragment differ by multiples
+    // of 32, so they share one swizzle
+    int a_frag[FM], b_frag[FN];
+    const int half = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) a_frag[i] = (wm * WM + i * 32 + (lane & 31)) * BK;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b_frag[j] = BM * BK + (wn * WN + j * 32 + (lane & 31)) * BK;
+    const int swz = lds_swz<KCH>(lane & 31);
+
+    auto compute = [&](int stage) {
+        const uint16_t *st = smem + stage * STAGE;
+        bf16x8 af[2][FM], bfr[2][FN];
+        auto load_frags = [&](int kk, int set) {
+            const int co = ((kk * 2 + half) ^ swz) * 8;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) af[set][i] = *reinterpret_cast<const bf16x8 *>(st + a_frag[i] + co);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bfr[set][j] = *reinterpret_cast<const bf16x8 *>(st + b_frag[j] + co);
+        };
+        load_frags(0, 0);
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
-            const int chunk = kk * 2 + (lane >> 5);
-            bf16x8 af[FM], bfr[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int r = wm * WM + i * 32 + (lane & 31);
-                af[i] = *reinterpret_cast<const bf16x8 *>(as + (r * KCH + (chunk ^ (r & 7))) * 8);
-            }
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int r = wn * WN + j * 32 + (lane & 31);
-                bfr[j] = *reinterpret_cast<const bf16x8 *>(bs + (r * KCH + (chunk ^ (r & 7))) * 8);
-            }
+            if (kk + 1 < BK / 16) load_frags(kk + 1, (kk + 1) & 1);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk & 1][j], af[kk & 1][i], acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < nk) store_tiles(buf ^ 1);
-        __syncthreads();
+    };
+
+    const int nk = K / BK;
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; ++s)
+        if (s < nk) issue_copies(s, s);
+    int stage = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        // step kt's copies have landed once at most the later steps' copies are in flight; this
+        // wave's LDS reads of the previous step are done at lgkmcnt(0). Then a plain s_barrier: a
+        // full __syncthreads() fence would also wait for the copies of later steps.
+        wait_copies<PER_STEP, NSTAGE - 2>(min(NSTAGE - 2, nk - 1 - kt));
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (kt + NSTAGE - 1 < nk) issue_copies(kt + NSTAGE - 1, (stage + NSTAGE - 1) % NSTAGE);
+        compute(stage);
+        stage = (stage + 1) % NSTAGE;
     }
 
-    // epilogue: accumulator register r of a 32x32 block holds row 8*(r/4) + 4*(lane/32) + (r%4),
-    // column lane%32; rows go back to their tokens (un-permute), scaled by p_t for the out-projection
+    // epilogue: block (i, j) register r holds output column 8*(r/4) + 4*(lane/32) + (r%4) of token
+    // row lane%32 (C^T layout); rows go back to their tokens, scaled by p_t for the out-projection
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+        const int row = wm * WM + i * 32 + (lane & 31);
+        if (row < rows) {
+            const int tok = s_tok[row];
+            const float sc = OUT ? s_prob[row] : 1.0f;
+            uint16_t *crow = C + (size_t)tok * p.N0 + n0 + wn * WN + 4 * half;
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const int col = wn * WN + j * 32 + (lane & 31);
-                if (row < rows) {
-                    const int tok = s_tok[row];
-                    float v = acc[i][j][r];
-                    if (OUT) v *= s_prob[row];
-                    C[(size_t)tok * p.N0 + n0 + col] = f32_to_bf16(v);
+                for (int g = 0; g < 4; ++g) {
+                    uint2 pk;
+                    pk.x = pack_bf16x2(acc[i][j][4 * g] * sc, acc[i][j][4 * g + 1] * sc);
+                    pk.y = pack_bf16x2(acc[i][j][4 * g + 2] * sc, acc[i][j][4 * g + 3] * sc);
+                    *reinterpret_cast<uint2 *>(crow + j * 32 + 8 * g) = pk;
+                }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Gate and permute for the out-projection (bf16): a[pos][n] = bf16(SiLU(z[t][n]) * h[t][n]) with
+// t = perm[pos], fp32 arithmetic, rows written in slot order so the GEMM reads each expert's rows
+// contiguously. Memory-bound: 8 rows per workgroup, 32 lanes per row, 4 chunks of 8 elements in
+// flight per lane (chunk indices past the row end are clamped for the loads and not stored).
+__global__ __launch_bounds__(256) void k_gate_permute(const uint16_t *__restrict__ z, const uint16_t *__restrict__ h,
+                                                      const int32_t *__restrict__ perm, int T, int di,
+                                                      uint16_t *__restrict__ a) {
+    const int pos = blockIdx.x * 8 + (threadIdx.x >> 5);
+    if (pos >= T) return;
+    const int l = threadIdx.x & 31;
+    const int tok = perm[pos];
+    const int cpr = di >> 3;  // 16-byte chunks per row
+    const uint4 *zr = reinterpret_cast<const uint4 *>(z + (size_t)tok * di);
+    const uint4 *hr = reinterpret_cast<const uint4 *>(h + (size_t)tok * di);
+    uint4 *ar = reinterpret_cast<uint4 *>(a + (size_t)pos * di);
+    for (int c0 = l; c0 < cpr; c0 += 128) {
+        uint4 zv[4], hv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = min(c0 + 32 * u, cpr - 1);
+            zv[u] = zr[c];
+            hv[u] = hr[c];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t zw[4] = {zv[u].x, zv[u].y, zv[u].z, zv[u].w};
+            const uint32_t hw[4] = {hv[u].x, hv[u].y, hv[u].z, hv[u].w};
+            uint32_t o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float z0 = __uint_as_float(zw[q] << 16), z1 = __uint_as_float(zw[q] & 0xFFFF0000u);
+                const float h0 = __uint_as_float(hw[q] << 16), h1 = __uint_as_float(hw[q] & 0xFFFF0000u);
+                o[q] = pack_bf16x2(silu_fast(z0) * h0, silu_fast(z1) * h1);
+            }
+            if (c0 + 32 * u < cpr) ar[c0 + 32 * u] = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Decode path (T <= 64): the cost is streaming each active expert's weights from HBM once; the MFMA
+// work is tiny. A workgroup owns 16 weight rows of one expert and every token routed to it (at most
+// 64, i.e. NB blocks of 16), and its NW waves split K. The weight fragment of a 16x16x32 MFMA comes
+// straight from global memory (lane l: row l%16, 8 elements at k + 8*(l/16)), the token fragments
+// likewise through perm; each wave keeps U K-steps of loads in flight. Partial sums of the waves are
+// added in wave order through LDS (deterministic), then scaled (out-projection) and stored.
+// Grid: (weight rows / 16) x min(E, T): the second index is the rank among experts that received tokens;
+// each workgroup runs the variant sized for its expert's token-block count.
+template <int NW, int NB, int U, bool OUT>
+__device__ __forceinline__ void gemv_block(const GemmArgs &p, int e, int o0, int ne, int rb,
+                                           float (*s_red)[4][16][16]) {
+    constexpr int NT = 64 * NW;
+    __shared__ int s_tok[64];
+    __shared__ float s_prob[64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nglob = rb * 16;
+    const int which = nglob / p.N0, n0 = nglob % p.N0;
+    const int K = p.K;
+    const uint16_t *W = static_cast<const uint16_t *>(which ? p.B1 : p.B0) + ((size_t)e * p.N0 + n0) * K;
+    uint16_t *C = static_cast<uint16_t *>(which ? p.C1 : p.C0);
+    const int tok_first = p.perm[o0];
+    for (int i = tid; i < 64; i += NT) {
+        const int tok = i < ne ? p.perm[o0 + i] : tok_first;
+        s_tok[i] = tok;
+        s_prob[i] = OUT ? p.prob[tok] : 1.0f;
+    }
+    __syncthreads();
+
+    const int r = lane & 15, g = lane >> 4;
+    const uint16_t *wp = W + (size_t)r * K + g * 8;
+    const uint16_t *xp[NB], *hp[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const size_t off = (size_t)s_tok[b * 16 + r] * K + g * 8;
+        xp[b] = static_cast<const uint16_t *>(p.A0) + off;
+        hp[b] = OUT ? static_cast<const uint16_t *>(p.A1) + off : nullptr;
+    }
+    f32x4 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    const int nsteps = K / 32;
+    for (int s0 = wave; s0 < nsteps; s0 += NW * U) {
+        bf16x8 wf[U], xf[U][NB];
+        uint4 hf[OUT ? U : 1][NB];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k0 = min(s0 + u * NW, nsteps - 1) * 32;  // clamped: loads stay in bounds
+            wf[u] = *reinterpret_cast<const bf16x8 *>(wp + k0);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                xf[u][b] = *reinterpret_cast<const bf16x8 *>(xp[b] + k0);
+                if (OUT) hf[u][b] = *reinterpret_cast<const uint4 *>(hp[b] + k0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (s0 + u * NW < nsteps) {  // uniform
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    bf16x8 a = xf[u][b];
+                    if (OUT) {
+                        // a = bf16(SiLU(z) * h), fp32 arithmetic
+                        const uint4 zv = __builtin_bit_cast(uint4, xf[u][b]);
+                        const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w};
+                        const uint32_t hw[4] = {hf[u][b].x, hf[u][b].y, hf[u][b].z, hf[u][b].w};
+                        uint32_t o[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float z0 = __uint_as_float(zw[q] << 16), z1 = __uint_as_float(zw[q] & 0xFFFF0000u);
+                            const float h0 = __uint_as_float(hw[q] << 16), h1 = __uint_as_float(hw[q] & 0xFFFF0000u);
+                            o[q] = pack_bf16x2(silu_fast(z0) * h0, silu_fast(z1) * h1);
+                        }
+                        a = __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+                    }
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], a, acc[b], 0, 0, 0);
                 }
             }
+        }
+    }
+    // accumulator register i of lane l: weight row 4*(l/16) + i, token column l%16
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_red[wave][b][4 * g + i][r] = acc[b][i];
+    __syncthreads();
+    for (int idx = tid; idx < NB * 256; idx += NT) {
+        const int b = idx >> 8, n = (idx >> 4) & 15, m = idx & 15;
+        const int col = b * 16 + m;
+        if (col < ne) {
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) v += s_red[w][b][n][m];
+            C[(size_t)s_tok[col] * p.N0 + n0 + n] = f32_to_bf16(v * s_prob[col]);
+        }
+    }
+}
+
+template <int NW, bool OUT>
+__global__ __launch_bounds__(64 * NW) void k_grouped_gemv_bf16(GemmArgs p) {
+    __shared__ float s_red[NW][4][16][16];
+    const int rb = blockIdx.x % p.n_tiles, rank = blockIdx.x / p.n_tiles;
+    int e = -1, o0 = 0, ne = 0;
+    for (int i = 0, j = 0; i < p.E; ++i) {
+        const int c = p.offsets[i + 1] - p.offsets[i];
+        if (c > 0) {
+            if (j == rank) { e = i; o0 = p.offsets[i]; ne = c; break; }
+            ++j;
+        }
+    }
+    if (e < 0) return;
+    switch ((ne + 15) >> 4) {  // token blocks of this expert (1..4), uniform per workgroup
+        case 1: gemv_block<NW, 1, 8, OUT>(p, e, o0, ne, rb, s_red); break;
+        case 2: gemv_block<NW, 2, 4, OUT>(p, e, o0, ne, rb, s_red); break;
+        case 3: gemv_block<NW, 3, 4, OUT>(p, e, o0, ne, rb, s_red); break;
+        default: gemv_block<NW, 4, 4, OUT>(p, e, o0, ne, rb, s_red); break;
+    }
+}
+
+template <bool OUT>
+static hipError_t launch_gemv(const GemmArgs &a0, int nB, hipStream_t s) {
+    GemmArgs a = a0;
+    a.n_tiles = nB * a.N0 / 16;
+    a.n_tiles_per_b = a.N0 / 16;
+    const int active = a.T < a.E ? a.T : a.E;
+    hipLaunchKernelGGL((k_grouped_gemv_bf16<8, OUT>), dim3((unsigned)a.n_tiles * active), dim3(512), 0, s, a);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -281,23 +487,75 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs p) {
 
 // ---------------------------------------------------------------------------------------------
 
-template <int BM, int BN, bool OUT>
+template <int BM, int BN, int BK, int NSTAGE, int WGM, int WGN, bool OUT>
 static hipError_t launch_bf16(const GemmArgs &a0, int nB, hipStream_t s) {
     GemmArgs a = a0;
     a.n_tiles_per_b = a.N0 / BN;
     a.n_tiles = nB * a.n_tiles_per_b;
     const int max_mtiles = (a.T + a.E * (BM - 1)) / BM;
-    const size_t smem = (size_t)2 * (BM + BN) * 64 * sizeof(uint16_t);
+    const size_t smem = (size_t)NSTAGE * (BM + BN) * BK * sizeof(uint16_t);
     static bool attr_set = false;  // per process; the attribute is per function
     if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_grouped_gemm_bf16<BM, BN, OUT>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        hipError_t err = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&k_grouped_gemm_bf16<BM, BN, BK, NSTAGE, WGM, WGN, OUT>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (err != hipSuccess) return err;
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, OUT>), dim3((unsigned)max_mtiles * a.n_tiles), dim3(256), smem, s,
-                       a);
+    hipLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, BK, NSTAGE, WGM, WGN, OUT>), dim3((unsigned)max_mtiles * a.n_tiles),
+                       dim3(64 * WGM * WGN), smem, s, a);
     return hipGetLastError();
+}
+
+// Tile shapes available to the bf16 path.
+struct TileCfg { int bm, bn, bk, nstage, wgm, wgn; };
+constexpr TileCfg kTiles[] = {
+    {256, 256, 64, 2, 2, 4},  // 0: 8 waves (128x64 each), BK 64, 2 stages (128 KiB LDS)
+    {256, 256, 32, 4, 2, 4},  // 1: 8 waves, BK 32, 4 stages (128 KiB)
+    {256, 256, 32, 4, 2, 2},  // 2: 4 waves (128x128 each), BK 32, 4 stages
+    {256, 128, 64, 3, 2, 2},  // 3: 4 waves (128x64 each), BK 64, 3 stages (144 KiB)
+    {128, 128, 64, 4, 2, 2},  // 4: 4 waves (64x64 each), BK 64, 4 stages (128 KiB)
+    {128, 64, 64, 4, 2, 2},   // 5: 4 waves (64x32 each), BK 64, 4 stages (96 KiB)
+    {256, 256, 32, 3, 2, 4},  // 6: 8 waves, BK 32, 3 stages (96 KiB)
+    {128, 256, 64, 3, 2, 2},  // 7: 4 waves (64x128 each), BK 64, 3 stages (144 KiB)
+};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+
+// Optional override of the tile choice (tuning sweeps): ROM_TILE_IN / ROM_TILE_OUT = index above.
+static int tile_override(bool out) {
+    static int cached[2] = {-2, -2};
+    int &c = cached[out ? 1 : 0];
+    if (c == -2) {
+        const char *v = getenv(out ? "ROM_TILE_OUT" : "ROM_TILE_IN");
+        c = v ? atoi(v) : -1;
+        if (c < 0 || c >= kNumTiles) c = -1;
+    }
+    return c;
+}
+
+// Default tile shape by problem: 256x256 blocks when there are enough rows and columns, smaller
+// blocks for small T or narrow N.
+static int default_tile(const GemmArgs &a, bool out) {
+    (void)out;
+    if (a.T >= 4096 && a.N0 % 256 == 0) return 1;
+    if (a.N0 % 128 == 0) return 4;
+    return 5;
+}
+
+template <bool OUT>
+static hipError_t launch_bf16_auto(const GemmArgs &a, int nB, hipStream_t s) {
+    int t = tile_override(OUT);
+    if (t < 0 || a.N0 % kTiles[t].bn != 0) t = default_tile(a, OUT);
+    switch (t) {
+        case 0: return launch_bf16<256, 256, 64, 2, 2, 4, OUT>(a, nB, s);
+        case 1: return launch_bf16<256, 256, 32, 4, 2, 4, OUT>(a, nB, s);
+        case 2: return launch_bf16<256, 256, 32, 4, 2, 2, OUT>(a, nB, s);
+        case 3: return launch_bf16<256, 128, 64, 3, 2, 2, OUT>(a, nB, s);
+        case 4: return launch_bf16<128, 128, 64, 4, 2, 2, OUT>(a, nB, s);
+        case 6: return launch_bf16<256, 256, 32, 3, 2, 4, OUT>(a, nB, s);
+        case 7: return launch_bf16<128, 256, 64, 3, 2, 2, OUT>(a, nB, s);
+        default: return launch_bf16<128, 64, 64, 4, 2, 2, OUT>(a, nB, s);
+    }
 }
 
 template <bool OUT>
@@ -326,12 +584,12 @@ hipError_t launch_in_proj(const void *X, const rom_routing &r, rom_dtype dt, int
     a.N0 = di;
     a.E = r.E;
     if (dt == ROM_DTYPE_F32) return launch_f32<false>(a, 2, s);
-    if (di % 128 == 0) return launch_bf16<128, 128, false>(a, 2, s);
-    return launch_bf16<128, 64, false>(a, 2, s);
+    if (T <= kDecodeMaxT) return launch_gemv<false>(a, 2, s);
+    return launch_bf16_auto<false>(a, 2, s);
 }
 
 hipError_t launch_out_proj(const void *z, const void *h, const rom_routing &r, rom_dtype dt, int T, int dm, int di,
-                           const void *Wo, void *out, hipStream_t s) {
+                           const void *Wo, void *out, void *workspace, hipStream_t s) {
     GemmArgs a{};
     a.A0 = z;
     a.A1 = h;
@@ -345,8 +603,21 @@ hipError_t launch_out_proj(const void *z, const void *h, const rom_routing &r, r
     a.N0 = dm;
     a.E = r.E;
     if (dt == ROM_DTYPE_F32) return launch_f32<true>(a, 1, s);
-    if (dm % 128 == 0) return launch_bf16<128, 128, true>(a, 1, s);
-    return launch_bf16<128, 64, true>(a, 1, s);
+    if (T <= kDecodeMaxT) return launch_gemv<true>(a, 1, s);
+    // gated rows in slot order into the workspace, then the GEMM reads them contiguously
+    hipLaunchKernelGGL(k_gate_permute, dim3((unsigned)((T + 7) / 8)), dim3(256), 0, s,
+                       static_cast<const uint16_t *>(z), static_cast<const uint16_t *>(h), r.perm, T, di,
+                       static_cast<uint16_t *>(workspace));
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    a.A0 = workspace;
+    a.A1 = nullptr;
+    return launch_bf16_auto<true>(a, 1, s);
+}
+
+size_t out_proj_workspace_bytes(int T, int di, rom_dtype dt) {
+    if (dt != ROM_DTYPE_BF16 || T <= kDecodeMaxT) return 0;
+    return (size_t)T * di * sizeof(uint16_t);
 }
 
 }  // namespace rom

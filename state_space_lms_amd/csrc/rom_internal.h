@@ -9,12 +9,18 @@
 
 namespace rom {
 
-// Tokens handled by one router workgroup on the multi-workgroup path.
-constexpr int kRouteTokensPerWG = 256;
+// Fewest tokens per workgroup of the router-logits kernel (8; 32 when T is large), tokens per
+// workgroup of the scatter kernel.
+constexpr int kRouteMinTokensPerWG = 8;
+constexpr int kScatterTokensPerWG = 256;
 // Up to this many tokens the whole routing runs in one workgroup, in one launch.
-constexpr int kRouteSmallT = 256;
+constexpr int kRouteSmallT = 8;
 
-inline int route_workgroups(int T) { return (T + kRouteTokensPerWG - 1) / kRouteTokensPerWG; }
+// Up to this many tokens the bf16 projections take the weight-streaming (decode) kernels.
+constexpr int kDecodeMaxT = 64;
+
+// Upper bound of router-logits workgroups for T tokens (sizes the per-workgroup histogram workspace).
+inline int route_workgroups(int T) { return (T + kRouteMinTokensPerWG - 1) / kRouteMinTokensPerWG; }
 
 // Each returns hipSuccess or the launch error. Arguments are already validated.
 hipError_t launch_route(const void *X, rom_dtype dt, int T, int dm, const float *Wr, const float *bias, int E,
@@ -24,6 +30,9 @@ hipError_t launch_in_proj(const void *X, const rom_routing &r, rom_dtype dt, int
                           const void *Wc, const void *Wg, void *x_out, void *z_out, hipStream_t s);
 
 hipError_t launch_out_proj(const void *z, const void *h, const rom_routing &r, rom_dtype dt, int T, int dm, int di,
-                           const void *Wo, void *out, hipStream_t s);
+                           const void *Wo, void *out, void *workspace, hipStream_t s);
+
+// Workspace bytes the out-projection needs (the gated rows in slot order; 0 on the decode and fp32 paths).
+size_t out_proj_workspace_bytes(int T, int di, rom_dtype dt);
 
 }  // namespace rom

@@ -7,22 +7,83 @@
 //
 // Router arithmetic is fp32: logit_t,j = sum_k X[t][k] * W_r[k][j] (+ bias[j]); argmax keeps the
 // lowest index on ties (strict > in ascending j); prob = 1 / sum_j exp(logit_j - logit_max).
-// The router reads X once (HBM-bound: E flops per element); W_r (d_model * E * 4 bytes) stays in
-// L1/L2 and each lane reuses the W_r values it loads across 8 tokens.
+// The router reads X once (HBM-bound: E flops per element). A wave computes the logits of 8 tokens at
+// a time with all 64 lanes splitting d_model, so each W_r value a lane loads serves 8 tokens; W_r is
+// staged once per workgroup in LDS (when it fits) in a layout where the 64 lanes of a wave read 64
+// consecutive 16-byte words.
+//
+// Launches: T <= 8: one workgroup does everything. Otherwise (1) logits + top-1 + per-workgroup
+// histogram, 32 tokens per workgroup when that gives >= 512 workgroups (one wave per 8 tokens), else
+// 8 tokens per workgroup (the four waves split d_model); (2) per-expert totals and bases, stable
+// scatter (ballot ranks inside each 256-token workgroup), optional permute.
 #include "rom_device.h"
 #include "rom_internal.h"
 
 namespace rom {
 
-// ---------------------------------------------------------------------------------------------
+// Largest W_r staged in LDS (bytes).
+constexpr int kRouteLdsW = 64 * 1024;
+
+// W_r [d_model][E] -> LDS as float4 words: word (kk, x4, c) holds W_r[8c+kk][4*x4 .. 4*x4+4), stored at
+// ((kk * E/4 + x4) * nchunk + c), so lanes reading consecutive chunks c read consecutive words.
+// Requires E % 4 == 0. Reads global W_r coalesced; every thread of the workgroup takes part.
+__device__ __forceinline__ void stage_router_weight(const float *__restrict__ Wr, int dm, int E, float4 *wl) {
+    // W_r as dm*E/4 float4 words, at most kRouteLdsW/16 = 4096 of them: a 256-thread workgroup moves
+    // at most 16 words per thread. All loads are issued before any store (indices past the end are
+    // clamped and not stored). Requires E/4 to be a power of two.
+    const int e4 = E >> 2, nchunk = dm >> 3, n4 = dm * e4;
+    const int sh = __builtin_ctz(e4);
+    const float4 *src = reinterpret_cast<const float4 *>(Wr);
+    float4 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = src[min((int)threadIdx.x + j * 256, n4 - 1)];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int g = threadIdx.x + j * 256;
+        if (g < n4) {
+            const int k = g >> sh, x4 = g & (e4 - 1);
+            wl[((k & 7) * e4 + x4) * nchunk + (k >> 3)] = v[j];
+        }
+    }
+}
+
+// Raw 8-element chunk of an X row (kept packed until used, to hold two chunk sets in registers).
+template <typename TX> struct Chunk8;
+template <> struct Chunk8<uint16_t> {
+    uint4 v;
+    __device__ __forceinline__ void load(const uint16_t *p) { v = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void unpack(float f[8]) const {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    }
+};
+template <> struct Chunk8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float *p) {
+        a = reinterpret_cast<const float4 *>(p)[0];
+        b = reinterpret_cast<const float4 *>(p)[1];
+    }
+    __device__ __forceinline__ void unpack(float f[8]) const {
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    }
+};
+
 // Logits of a group of 8 tokens [tok0, tok0+8) for the experts [e0, e0+EG), computed by LPT lanes
-// (LPT = 8 or 64, consecutive lanes). Lane jl (0..LPT-1) sums the 8-element chunks c = jl, jl+LPT,
-// ... of d_model. Partial sums are then reduce-scattered over lane bits 0..2 (each lane keeps one
-// token) and, for LPT = 64, all-reduced over bits 3..5. On return lane jl holds the logits of token
-// tok0 + (jl & 7) in out[0..EG). Must be called by every lane of the wave (it shuffles).
+// (LPT = 64 * waves; lane jl = 0..LPT-1). Lane jl sums the 8-element chunks c = jl, jl+LPT, ... of
+// d_model; the next chunk's 8 token rows are fetched while the current one is multiplied (tokens past
+// T read row T-1 and are discarded). Partial sums are then reduce-scattered over lane bits 0..2 (each
+// lane keeps one token) and all-reduced over lane bits 3..5. On return every lane of the wave with
+// (lane & 7) == j holds this wave's partial logits of token tok0 + j in out[0..EG); with LPT > 64
+// the caller still sums the waves. Must be called by every lane of the wave (it shuffles).
+// wl != nullptr: W_r is read from the LDS copy made by stage_router_weight.
 template <typename TX, int LPT, int EG>
 __device__ __forceinline__ void logits_group8(const TX *__restrict__ X, int T, int dm, const float *__restrict__ Wr,
-                                              int E, int e0, int tok0, int jl, float out[EG]) {
+                                              const float4 *wl, int E, int e0, int tok0, int jl, float out[EG]) {
     float acc[8][EG];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
@@ -31,18 +92,44 @@ __device__ __forceinline__ void logits_group8(const TX *__restrict__ X, int T, i
 
     const int nchunk = dm >> 3;
     const bool vecw = (E % 4 == 0) && (EG % 4 == 0) && (e0 + EG <= E);
+    const int e4 = E >> 2;
+    const TX *xrow[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xrow[q] = X + (size_t)min(tok0 + q, T - 1) * dm;
+    // chunk indices are clamped to the last chunk so every load is in bounds and unconditional
+    Chunk8<TX> nxt[8];
+    {
+        const int c0 = min(jl, nchunk - 1);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) nxt[q].load(xrow[q] + c0 * 8);
+    }
     for (int c = jl; c < nchunk; c += LPT) {
+        Chunk8<TX> cur[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) cur[q] = nxt[q];
+        const int cn = min(c + LPT, nchunk - 1);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) nxt[q].load(xrow[q] + cn * 8);
         float w[8][EG];
-        const float *wrow = Wr + (size_t)(c * 8) * E + e0;
-        if (vecw) {
+        if (wl != nullptr && vecw) {
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
                 for (int x = 0; x < EG; x += 4) {
-                    float4 v = *reinterpret_cast<const float4 *>(wrow + (size_t)kk * E + x);
+                    const float4 v = wl[(kk * e4 + ((e0 + x) >> 2)) * nchunk + c];
+                    w[kk][x] = v.x; w[kk][x + 1] = v.y; w[kk][x + 2] = v.z; w[kk][x + 3] = v.w;
+                }
+        } else if (vecw) {
+            const float *wrow = Wr + (size_t)(c * 8) * E + e0;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                for (int x = 0; x < EG; x += 4) {
+                    const float4 v = *reinterpret_cast<const float4 *>(wrow + (size_t)kk * E + x);
                     w[kk][x] = v.x; w[kk][x + 1] = v.y; w[kk][x + 2] = v.z; w[kk][x + 3] = v.w;
                 }
         } else {
+            const float *wrow = Wr + (size_t)(c * 8) * E + e0;
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
@@ -50,15 +137,12 @@ __device__ __forceinline__ void logits_group8(const TX *__restrict__ X, int T, i
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            const int t = tok0 + q;
-            if (t < T) {
-                float xf[8];
-                load8_f32(X + (size_t)t * dm + c * 8, xf);
+            float xf[8];
+            cur[q].unpack(xf);
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk)
+            for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-                    for (int x = 0; x < EG; ++x) acc[q][x] = fmaf(xf[kk], w[kk][x], acc[q][x]);
-            }
+                for (int x = 0; x < EG; ++x) acc[q][x] = fmaf(xf[kk], w[kk][x], acc[q][x]);
         }
     }
     // reduce-scatter over lane bits 2, 1, 0: after the three steps lane j keeps token (j & 7)
@@ -85,23 +169,22 @@ __device__ __forceinline__ void logits_group8(const TX *__restrict__ X, int T, i
         const float send = (j & 1) ? acc[0][x] : acc[1][x];
         out[x] = keep + __shfl_xor(send, 1);
     }
-    if (LPT > 8) {
 #pragma unroll
-        for (int m = 8; m < LPT; m <<= 1)
+    for (int m = 8; m < 64; m <<= 1)
 #pragma unroll
-            for (int x = 0; x < EG; ++x) out[x] += __shfl_xor(out[x], m);
-    }
+        for (int x = 0; x < EG; ++x) out[x] += __shfl_xor(out[x], m);
 }
 
-// All E logits of token (tok0 + (jl & 7)) into lg[0..EMAX) (entries >= E are -inf).
+// All E logits (this wave's share when LPT > 64) of token (tok0 + (jl & 7)) into lg[0..EMAX)
+// (entries >= E are -inf).
 template <typename TX, int LPT, int EG, int EMAX>
-__device__ __forceinline__ void logits_token(const TX *X, int T, int dm, const float *Wr, int E, int tok0, int jl,
-                                             float lg[EMAX]) {
+__device__ __forceinline__ void logits_token(const TX *X, int T, int dm, const float *Wr, const float4 *wl, int E,
+                                             int tok0, int jl, float lg[EMAX]) {
 #pragma unroll
     for (int g = 0; g < EMAX / EG; ++g) {
         if (g * EG < E) {  // uniform
             float o[EG];
-            logits_group8<TX, LPT, EG>(X, T, dm, Wr, E, g * EG, tok0, jl, o);
+            logits_group8<TX, LPT, EG>(X, T, dm, Wr, wl, E, g * EG, tok0, jl, o);
 #pragma unroll
             for (int x = 0; x < EG; ++x) lg[g * EG + x] = (g * EG + x < E) ? o[x] : -INFINITY;
         } else {
@@ -109,6 +192,32 @@ __device__ __forceinline__ void logits_token(const TX *X, int T, int dm, const f
             for (int x = 0; x < EG; ++x) lg[g * EG + x] = -INFINITY;
         }
     }
+}
+
+// Logits of the workgroup's tokens. WPG = 1: wave w owns the 8 tokens [tok_base + 8w, +8).
+// WPG = 4: the four waves split d_model for the 8 tokens [tok_base, +8) and their partial sums are
+// added in wave order through LDS (s_red). On return, lanes 0..7 of every wave (WPG = 1) or of
+// wave 0 (WPG = 4) hold the full logits of token tok0 + lane, where tok0 is returned.
+template <typename TX, int EG, int EMAX, int WPG>
+__device__ __forceinline__ int wg_logits(const TX *X, int T, int dm, const float *Wr, const float4 *wl, int E,
+                                         int tok_base, float lg[EMAX], float (*s_red)[8][EMAX]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (WPG == 1) {
+        const int tok0 = tok_base + wave * 8;
+        logits_token<TX, 64, EG, EMAX>(X, T, dm, Wr, wl, E, tok0, lane, lg);
+        return tok0;
+    }
+    logits_token<TX, 256, EG, EMAX>(X, T, dm, Wr, wl, E, tok_base, wave * 64 + lane, lg);
+    if (lane < 8) {
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e) s_red[wave][lane][e] = lg[e];
+    }
+    __syncthreads();
+    if (lane < 8) {
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e) lg[e] = ((s_red[0][lane][e] + s_red[1][lane][e]) + s_red[2][lane][e]) + s_red[3][lane][e];
+    }
+    return tok_base;
 }
 
 // Bias, argmax (lowest index on ties), and the top-1 softmax probability.
@@ -163,22 +272,26 @@ __device__ __forceinline__ void permute_rows(const TX *X, TX *Xp, int dm, int to
 
 // ---------------------------------------------------------------------------------------------
 // Multi-workgroup path, kernel 1: logits, top-1, probability, and this workgroup's histogram.
-// 256 tokens per workgroup; lane groups of 8 lanes each own 8 tokens.
-template <typename TX, int EG, int EMAX>
+// WPG = 1: 32 tokens per workgroup (8 per wave); WPG = 4: 8 tokens per workgroup.
+template <typename TX, int EG, int EMAX, int WPG>
 __global__ __launch_bounds__(256) void k_route_logits(const TX *__restrict__ X, int T, int dm,
                                                       const float *__restrict__ Wr, const float *__restrict__ bias,
-                                                      int E, int32_t *__restrict__ ids, float *__restrict__ prob,
-                                                      int32_t *__restrict__ wg_counts, int nwg) {
+                                                      int E, int use_lds, int32_t *__restrict__ ids,
+                                                      float *__restrict__ prob, int32_t *__restrict__ wg_counts,
+                                                      int nwg) {
+    constexpr int TPW = 32 / WPG;  // tokens per workgroup
+    extern __shared__ float4 wl_dyn[];
     __shared__ int hist[ROM_MAX_EXPERTS];
+    __shared__ float s_red[WPG == 4 ? 4 : 1][8][EMAX];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int i = tid; i < E; i += 256) hist[i] = 0;
+    if (use_lds) stage_router_weight(Wr, dm, E, wl_dyn);
     __syncthreads();
-    const int jl = lane & 7;
-    const int tok0 = blockIdx.x * kRouteTokensPerWG + wave * 64 + (lane >> 3) * 8;
     float lg[EMAX];
-    logits_token<TX, 8, EG, EMAX>(X, T, dm, Wr, E, tok0, jl, lg);
-    const int t = tok0 + jl;
-    if (t < T) {
+    const int tok0 = wg_logits<TX, EG, EMAX, WPG>(X, T, dm, Wr, use_lds ? wl_dyn : nullptr, E, blockIdx.x * TPW, lg,
+                                                  s_red);
+    const int t = tok0 + lane;
+    if (lane < 8 && (WPG == 1 || wave == 0) && t < T) {
         int best;
         float p;
         select_top1<EMAX>(lg, bias, E, best, p);
@@ -190,24 +303,27 @@ __global__ __launch_bounds__(256) void k_route_logits(const TX *__restrict__ X, 
     for (int i = tid; i < E; i += 256) wg_counts[(size_t)i * nwg + blockIdx.x] = hist[i];
 }
 
-// Multi-workgroup path, kernel 2: per-expert totals and bases, then the stable scatter.
+// Multi-workgroup path, kernel 2: per-expert totals and bases, then the stable scatter of 256 tokens
+// per workgroup (= sub logits workgroups).
 template <typename TX>
 __global__ __launch_bounds__(256) void k_route_scatter(const int32_t *__restrict__ ids, int T, int E,
-                                                       const int32_t *__restrict__ wg_counts, int nwg,
+                                                       const int32_t *__restrict__ wg_counts, int nwg, int sub,
                                                        int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                                                        int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm,
                                                        const TX *__restrict__ X, TX *__restrict__ Xp, int dm) {
     __shared__ int s_before[ROM_MAX_EXPERTS], s_total[ROM_MAX_EXPERTS], s_base[ROM_MAX_EXPERTS];
     __shared__ int s_wcnt[4][ROM_MAX_EXPERTS];
-    __shared__ int s_pos[kRouteTokensPerWG];
+    __shared__ int s_pos[kScatterTokensPerWG];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wg = blockIdx.x;
+    const int first = wg * sub;  // logits workgroups before this one contribute to the base
     for (int e = wave; e < E; e += 4) {
         int before = 0, total = 0;
+#pragma unroll 8
         for (int w = lane; w < nwg; w += 64) {
             const int c = wg_counts[(size_t)e * nwg + w];
             total += c;
-            before += (w < wg) ? c : 0;
+            before += (w < first) ? c : 0;
         }
         for (int m = 32; m >= 1; m >>= 1) {
             before += __shfl_xor(before, m);
@@ -226,7 +342,7 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t *__restrict
         if (wg == 0) offsets[E] = run;
     }
     __syncthreads();
-    const int t = wg * kRouteTokensPerWG + tid;
+    const int t = wg * kScatterTokensPerWG + tid;
     const int e = t < T ? ids[t] : -1;
     const int rank = wg_stable_rank(e, E, s_wcnt);
     int pos = -1;
@@ -238,38 +354,39 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t *__restrict
     if (Xp) {
         s_pos[tid] = pos;
         __syncthreads();
-        permute_rows<TX>(X, Xp, dm, wg * kRouteTokensPerWG, min(kRouteTokensPerWG, T - wg * kRouteTokensPerWG), s_pos);
+        permute_rows<TX>(X, Xp, dm, wg * kScatterTokensPerWG, min(kScatterTokensPerWG, T - wg * kScatterTokensPerWG),
+                         s_pos);
     }
 }
 
 // ---------------------------------------------------------------------------------------------
-// Small-T path (T <= 256): the whole routing in one workgroup and one launch. Each wave takes
-// groups of 8 tokens and splits d_model over all 64 lanes.
+// Small-T path (T <= 8): the whole routing in one workgroup and one launch; the four waves split
+// d_model.
 template <typename TX, int EG, int EMAX>
 __global__ __launch_bounds__(256) void k_route_small(const TX *__restrict__ X, int T, int dm,
                                                      const float *__restrict__ Wr, const float *__restrict__ bias,
-                                                     int E, int32_t *__restrict__ ids, float *__restrict__ prob,
-                                                     int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-                                                     int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm,
-                                                     TX *__restrict__ Xp) {
+                                                     int E, int use_lds, int32_t *__restrict__ ids,
+                                                     float *__restrict__ prob, int32_t *__restrict__ counts,
+                                                     int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
+                                                     int32_t *__restrict__ inv_perm, TX *__restrict__ Xp) {
+    extern __shared__ float4 wl_dyn[];
     __shared__ int s_ids[kRouteSmallT];
     __shared__ int s_base[ROM_MAX_EXPERTS];
     __shared__ int s_wcnt[4][ROM_MAX_EXPERTS];
     __shared__ int s_pos[kRouteSmallT];
+    __shared__ float s_red[4][8][EMAX];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int ngroups = (T + 7) >> 3;
-    for (int g = wave; g < ngroups; g += 4) {
-        float lg[EMAX];
-        logits_token<TX, 64, EG, EMAX>(X, T, dm, Wr, E, g * 8, lane, lg);
-        const int t = g * 8 + lane;
-        if (lane < 8 && t < T) {
-            int best;
-            float p;
-            select_top1<EMAX>(lg, bias, E, best, p);
-            ids[t] = best;
-            prob[t] = p;
-            s_ids[t] = best;
-        }
+    if (use_lds) stage_router_weight(Wr, dm, E, wl_dyn);
+    __syncthreads();
+    float lg[EMAX];
+    wg_logits<TX, EG, EMAX, 4>(X, T, dm, Wr, use_lds ? wl_dyn : nullptr, E, 0, lg, s_red);
+    if (wave == 0 && lane < T) {
+        int best;
+        float p;
+        select_top1<EMAX>(lg, bias, E, best, p);
+        ids[lane] = best;
+        prob[lane] = p;
+        s_ids[lane] = best;
     }
     __syncthreads();
     if (tid < E) {
@@ -299,7 +416,7 @@ __global__ __launch_bounds__(256) void k_route_small(const TX *__restrict__ X, i
         inv_perm[tid] = pos;
     }
     if (Xp) {
-        s_pos[tid] = pos;
+        if (tid < kRouteSmallT) s_pos[tid] = pos;
         __syncthreads();
         permute_rows<TX>(X, Xp, dm, 0, T, s_pos);
     }
@@ -310,18 +427,41 @@ __global__ __launch_bounds__(256) void k_route_small(const TX *__restrict__ X, i
 template <typename TX, int EG, int EMAX>
 static hipError_t launch_route_t(const TX *X, int T, int dm, const float *Wr, const float *bias, int E,
                                  const rom_routing &r, TX *Xp, int32_t *wg_counts, hipStream_t s) {
+    const size_t wbytes = (size_t)dm * E * sizeof(float);
+    const int use_lds = (E % 4 == 0) && (((E >> 2) & ((E >> 2) - 1)) == 0) && wbytes <= (size_t)kRouteLdsW;
+    const size_t smem = use_lds ? wbytes : 0;
+    static bool attr_set = false;
+    if (!attr_set) {
+        const void *fns[3] = {reinterpret_cast<const void *>(&k_route_logits<TX, EG, EMAX, 1>),
+                              reinterpret_cast<const void *>(&k_route_logits<TX, EG, EMAX, 4>),
+                              reinterpret_cast<const void *>(&k_route_small<TX, EG, EMAX>)};
+        for (const void *f : fns) {
+            hipError_t err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kRouteLdsW);
+            if (err != hipSuccess) return err;
+        }
+        attr_set = true;
+    }
     if (T <= kRouteSmallT) {
-        hipLaunchKernelGGL((k_route_small<TX, EG, EMAX>), dim3(1), dim3(256), 0, s, X, T, dm, Wr, bias, E,
+        hipLaunchKernelGGL((k_route_small<TX, EG, EMAX>), dim3(1), dim3(256), smem, s, X, T, dm, Wr, bias, E, use_lds,
                            r.expert_id, r.prob, r.counts, r.offsets, r.perm, r.inv_perm, Xp);
         return hipGetLastError();
     }
-    const int nwg = route_workgroups(T);
-    hipLaunchKernelGGL((k_route_logits<TX, EG, EMAX>), dim3(nwg), dim3(256), 0, s, X, T, dm, Wr, bias, E,
-                       r.expert_id, r.prob, wg_counts, nwg);
+    // enough 32-token workgroups to fill the chip: one wave per 8 tokens; otherwise 8 tokens per
+    // workgroup with the waves splitting d_model
+    const bool wide = (T + 31) / 32 >= 512;
+    const int tpw = wide ? 32 : 8;
+    const int nwg = (T + tpw - 1) / tpw;
+    if (wide)
+        hipLaunchKernelGGL((k_route_logits<TX, EG, EMAX, 1>), dim3(nwg), dim3(256), smem, s, X, T, dm, Wr, bias, E,
+                           use_lds, r.expert_id, r.prob, wg_counts, nwg);
+    else
+        hipLaunchKernelGGL((k_route_logits<TX, EG, EMAX, 4>), dim3(nwg), dim3(256), smem, s, X, T, dm, Wr, bias, E,
+                           use_lds, r.expert_id, r.prob, wg_counts, nwg);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((k_route_scatter<TX>), dim3(nwg), dim3(256), 0, s, r.expert_id, T, E, wg_counts, nwg,
-                       r.counts, r.offsets, r.perm, r.inv_perm, X, Xp, dm);
+    const int nsc = (T + kScatterTokensPerWG - 1) / kScatterTokensPerWG;
+    hipLaunchKernelGGL((k_route_scatter<TX>), dim3(nsc), dim3(256), 0, s, r.expert_id, T, E, wg_counts, nwg,
+                       kScatterTokensPerWG / tpw, r.counts, r.offsets, r.perm, r.inv_perm, X, Xp, dm);
     return hipGetLastError();
 }
 

@@ -110,17 +110,29 @@ def test_in_proj_T0_noop(L):
     assert _in(L, X=None, T=0, Wc=None, Wg=None, xo=None, zo=None, r=_routing(0, 8)) == OK
 
 
-def _out(L, z=A, h=A + (1 << 24), T=512, dm=128, di=256, Wo=A, o=A + (1 << 26), r=None):
+WS = A + (1 << 28)
+
+
+def _out(L, z=A, h=A + (1 << 24), T=512, dm=128, di=256, Wo=A, o=A + (1 << 26), r=None, ws=WS, wsb=1 << 24):
     rs = r if r is not None else _routing(T, 8)
-    return L.rom_out_proj(z, h, ctypes.byref(rs), BF16, T, dm, di, Wo, o, None)
+    return L.rom_out_proj(z, h, ctypes.byref(rs), BF16, T, dm, di, Wo, o, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(T=-5), INVALID), (dict(dm=32), UNSUPPORTED), (dict(h=None), INVALID), (dict(o=A + 512), INVALID),
     (dict(o=A + (1 << 24)), INVALID), (dict(r=_routing(512, 8, perm=None)), INVALID), (dict(Wo=A + 1), INVALID),
+    (dict(ws=None), WS_SMALL), (dict(wsb=512 * 256 * 2 - 1), WS_SMALL), (dict(ws=WS + 8), INVALID),
+    (dict(ws=A + (1 << 24)), INVALID),  # overlaps h
 ])
 def test_out_proj_rejects(L, kw, code):
     assert _out(L, **kw) == code
+
+
+def test_out_proj_workspace_bytes(L):
+    assert L.rom_out_proj_workspace_bytes(0, 2048, BF16) == 0
+    assert L.rom_out_proj_workspace_bytes(64, 2048, BF16) == 0          # decode path needs none
+    assert L.rom_out_proj_workspace_bytes(1000, 2048, rom.ROM_DTYPE_F32) == 0
+    assert L.rom_out_proj_workspace_bytes(16384, 2048, BF16) == 16384 * 2048 * 2
 
 
 def test_binding_has_no_cpu_path(L):

@@ -97,6 +97,10 @@ SMALL = [
     workloads.custom_workload("bf16_T257_multi_wg_route", T=257, d_model=256, d_inner=128, E=8, seed=108),
     workloads.custom_workload("bf16_E64", T=3000, d_model=128, d_inner=128, E=64, seed=109),
     workloads.custom_workload("bf16_E16_T2000", T=2000, d_model=320, d_inner=192, E=16, seed=110),
+    workloads.custom_workload("bf16_T5_fused_route", T=5, d_model=512, d_inner=128, E=8, seed=113),
+    workloads.custom_workload("bf16_T9_split_route", T=9, d_model=512, d_inner=128, E=4, seed=114),
+    workloads.custom_workload("bf16_wide_route_E64", T=16400, d_model=128, d_inner=128, E=64, seed=115),
+    workloads.custom_workload("bf16_wide_route_E3", T=16421, d_model=192, d_inner=128, E=3, seed=116),
     workloads.custom_workload("f32_E5", T=333, d_model=128, d_inner=192, E=5, dtype="f32", seed=111),
     workloads.custom_workload("f32_T1000_E8", T=1000, d_model=64, d_inner=128, E=8, dtype="f32", seed=112),
 ]
@@ -114,6 +118,19 @@ def test_all_tokens_on_one_expert(rom, oracle):
     inp = workloads.make_inputs(w, router_bias=bias)
     _, gr, _, _ = check_workload(rom, oracle, w, inp, label="all tokens on expert 5")
     assert gr["counts"][5] == w.T
+
+
+@pytest.mark.parametrize("T,hot", [(40, 1), (64, 3), (64, None)])
+def test_decode_token_blocks(rom, oracle, T, hot):
+    """Decode kernels: an expert holding 33..64 tokens takes the 3- and 4-block variants."""
+    w = workloads.custom_workload(f"decode_blocks_T{T}", T=T, d_model=256, d_inner=320, E=4, seed=124 + T)
+    bias = np.zeros(4, np.float32)
+    if hot is not None:
+        bias[hot] = 1e3
+    inp = workloads.make_inputs(w, router_bias=bias)
+    _, gr, _, _ = check_workload(rom, oracle, w, inp, label=f"decode blocks T={T} hot={hot}")
+    if hot is not None:
+        assert gr["counts"][hot] == T
 
 
 def test_empty_experts(rom, oracle):
