@@ -198,7 +198,10 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4)}
     roof["traffic"] = measured_traffic(w.name)
-    roof["kernel"] = "k_grouped_gemm_bf16 (rom_in_proj)" if w.dtype == "bf16" else "k_grouped_gemm_f32 (rom_in_proj)"
+    if w.dtype != "bf16":
+        roof["kernel"] = "k_grouped_gemm_f32 (rom_in_proj)"
+    else:
+        roof["kernel"] = ("k_grouped_gemv_bf16" if decode else "k_grouped_gemm_bf16") + " (rom_in_proj)"
     roof["algorithmic"] = ({"bytes_per_launch": bytes_in} if decode else {"flops_per_launch": fl_in})
     roof["launch_us"] = round(mean_in * 1e6, 2)
 

@@ -37,7 +37,31 @@ struct GemmArgs {
     int T, K, N0, E;
     int n_tiles;          // N-tiles over the concatenated columns (nB * N0 / BN)
     int n_tiles_per_b;    // N0 / BN
+    int m_tiles;          // M-tiles launched (upper bound of the real ones)
+    int group_m;          // XCD-aware order: M-tiles per group (0: plain row-major order)
+    int per_xcd;          // XCD-aware order: tiles assigned to each of the 8 XCDs
 };
+
+// Tile (mt, nt) of workgroup blockIdx.x; false if the workgroup has no tile.
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on XCD b % 8), each with its
+// own L2. With group_m > 0, XCD x takes the contiguous range [x * per_xcd, (x + 1) * per_xcd) of a
+// grouped order in which group_m consecutive M-tiles share every N-tile: the workgroups resident on
+// one XCD at a time then need group_m A tiles and about 32 / group_m B tiles, so most operand reads
+// hit that XCD's L2.
+__device__ __forceinline__ bool tile_of_block(const GemmArgs &p, int &mt, int &nt) {
+    int L = blockIdx.x;
+    if (p.group_m > 0) {
+        L = (blockIdx.x & 7) * p.per_xcd + (blockIdx.x >> 3);
+        const int span = p.group_m * p.n_tiles;
+        const int g = L / span, in = L - g * span;
+        mt = g * p.group_m + in % p.group_m;
+        nt = in / p.group_m;
+    } else {
+        mt = L / p.n_tiles;
+        nt = L % p.n_tiles;
+    }
+    return mt < p.m_tiles;
+}
 
 // Expert and row range of M-tile mt: returns false if mt lies past the last real tile.
 template <int BM>
@@ -73,15 +97,20 @@ __device__ __forceinline__ bool locate_mtile(const int32_t *__restrict__ offsets
 // round trip; before each step a wave waits only until its copies for that step have landed
 // (vmcnt counts the later steps' copies still in flight), then the workgroup meets at a barrier.
 // LDS rows hold BK bf16 values as BK/8 16-byte chunks; chunk c of row r sits at c ^ swz(r) so the
-// MFMA operand reads (8 lanes = 8 consecutive rows, one chunk each) spread over all bank groups.
+// MFMA operand reads (16 lanes = 16 consecutive rows, one chunk each) spread over all banks.
 //
 // The MFMA computes the transposed tile C^T = W A^T (W operand first): a lane's 16 accumulators of
 // a 32x32 block belong to ONE token row (lane % 32) and hold 4 runs of 4 consecutive output columns,
 // so the epilogue scales them by that token's probability and writes 8-byte packed stores straight
 // to the token's output row (the un-permute).
+// gfx950 LDS serves a 16-byte-per-lane read 16 lanes at a time across 256 bytes of banks: 16 slots of
+// 16 bytes. An MFMA operand read has 16 consecutive lanes on 16 consecutive rows at one logical chunk,
+// so the swizzle must send those 16 rows to 16 different slots. With 128-byte rows (BK = 64) a row's
+// parity picks the half of the 256-byte window and (row >> 1) & 7 permutes the chunk within it; with
+// 64-byte rows (BK = 32) row & 3 picks the quarter and (row >> 2) & 3 permutes within it.
 template <int KCH>
 __device__ __forceinline__ int lds_swz(int row) {
-    return KCH == 8 ? (row & 7) : ((row >> 1) & 3);
+    return KCH == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
 }
 
 // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n and lgkmcnt == 0, expcnt untouched.
@@ -97,7 +126,7 @@ __device__ __forceinline__ void wait_copies(int ahead) {
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 }
 
-template <int BM, int BN, int BK, int NSTAGE, int WGM, int WGN, bool OUT>
+template <int BM, int BN, int BK, int NSTAGE, int WGM, int WGN, bool OUT, int SCHED>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p) {
     constexpr int NW = WGM * WGN;
     constexpr int NT = 64 * NW;
@@ -119,8 +148,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
     __shared__ float s_prob[OUT ? BM : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int mt = blockIdx.x / p.n_tiles, nt = blockIdx.x % p.n_tiles;
-    int e, slot0, rows;
+    int mt, nt, e, slot0, rows;
+    if (!tile_of_block(p, mt, nt)) return;
     if (!locate_mtile<BM>(p.offsets, p.E, mt, e, slot0, rows)) return;
     const int which = nt / p.n_tiles_per_b;
     const int n0 = (nt % p.n_tiles_per_b) * BN;
@@ -203,6 +232,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk & 1][j], af[kk & 1][i], acc[i][j], 0, 0, 0);
+        }
+        if (SCHED == 1) {
+            // issue order: the first sub-step's fragment reads, then for every sub-step but the last its
+            // MFMAs with the next sub-step's fragment reads slotted between them, then the last MFMAs
+            constexpr int NR = FM + FN, NM = FM * FN;
+            __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+            for (int kk = 0; kk + 1 < BK / 16; ++kk) {
+#pragma unroll
+                for (int q = 0; q < NR; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
         }
     };
 
@@ -487,37 +532,58 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs p) {
 
 // ---------------------------------------------------------------------------------------------
 
-template <int BM, int BN, int BK, int NSTAGE, int WGM, int WGN, bool OUT>
+// XCD-aware grouping of M-tiles (0 = off); ROM_GROUP_M overrides it for tuning sweeps.
+static int group_m_choice() {
+    static int cached = -2;
+    if (cached == -2) {
+        const char *v = getenv("ROM_GROUP_M");
+        cached = v ? atoi(v) : 0;
+        if (cached < 0 || cached > 64) cached = 0;
+    }
+    return cached;
+}
+
+template <int BM, int BN, int BK, int NSTAGE, int WGM, int WGN, bool OUT, int SCHED>
 static hipError_t launch_bf16(const GemmArgs &a0, int nB, hipStream_t s) {
     GemmArgs a = a0;
     a.n_tiles_per_b = a.N0 / BN;
     a.n_tiles = nB * a.n_tiles_per_b;
-    const int max_mtiles = (a.T + a.E * (BM - 1)) / BM;
+    a.m_tiles = (a.T + a.E * (BM - 1)) / BM;
+    a.group_m = group_m_choice();
+    unsigned grid;
+    if (a.group_m > 0) {
+        const int groups = (a.m_tiles + a.group_m - 1) / a.group_m;
+        const long total = (long)groups * a.group_m * a.n_tiles;
+        a.per_xcd = (int)((total + 7) / 8);
+        grid = (unsigned)a.per_xcd * 8;
+    } else {
+        grid = (unsigned)a.m_tiles * a.n_tiles;
+    }
     const size_t smem = (size_t)NSTAGE * (BM + BN) * BK * sizeof(uint16_t);
     static bool attr_set = false;  // per process; the attribute is per function
     if (!attr_set) {
         hipError_t err = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&k_grouped_gemm_bf16<BM, BN, BK, NSTAGE, WGM, WGN, OUT>),
+            reinterpret_cast<const void *>(&k_grouped_gemm_bf16<BM, BN, BK, NSTAGE, WGM, WGN, OUT, SCHED>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (err != hipSuccess) return err;
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, BK, NSTAGE, WGM, WGN, OUT>), dim3((unsigned)max_mtiles * a.n_tiles),
-                       dim3(64 * WGM * WGN), smem, s, a);
+    hipLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, BK, NSTAGE, WGM, WGN, OUT, SCHED>), dim3(grid), dim3(64 * WGM * WGN),
+                       smem, s, a);
     return hipGetLastError();
 }
 
 // Tile shapes available to the bf16 path.
-struct TileCfg { int bm, bn, bk, nstage, wgm, wgn; };
+struct TileCfg { int bm, bn, bk, nstage, wgm, wgn, sched; };
 constexpr TileCfg kTiles[] = {
-    {256, 256, 64, 2, 2, 4},  // 0: 8 waves (128x64 each), BK 64, 2 stages (128 KiB LDS)
-    {256, 256, 32, 4, 2, 4},  // 1: 8 waves, BK 32, 4 stages (128 KiB)
-    {256, 256, 32, 4, 2, 2},  // 2: 4 waves (128x128 each), BK 32, 4 stages
-    {256, 128, 64, 3, 2, 2},  // 3: 4 waves (128x64 each), BK 64, 3 stages (144 KiB)
-    {128, 128, 64, 4, 2, 2},  // 4: 4 waves (64x64 each), BK 64, 4 stages (128 KiB)
-    {128, 64, 64, 4, 2, 2},   // 5: 4 waves (64x32 each), BK 64, 4 stages (96 KiB)
-    {256, 256, 32, 3, 2, 4},  // 6: 8 waves, BK 32, 3 stages (96 KiB)
-    {128, 256, 64, 3, 2, 2},  // 7: 4 waves (64x128 each), BK 64, 3 stages (144 KiB)
+    {256, 256, 64, 2, 2, 4, 0},  // 0: 8 waves (128x64 each), BK 64, 2 stages (128 KiB LDS)
+    {256, 256, 32, 4, 2, 4, 0},  // 1: 8 waves, BK 32, 4 stages (128 KiB)
+    {256, 256, 64, 2, 2, 4, 1},  // 2: as 0, fragment reads interleaved with the MFMAs
+    {256, 128, 64, 3, 2, 2, 0},  // 3: 4 waves (128x64 each), BK 64, 3 stages (144 KiB)
+    {128, 128, 64, 4, 2, 2, 0},  // 4: 4 waves (64x64 each), BK 64, 4 stages (128 KiB)
+    {128, 64, 64, 4, 2, 2, 0},   // 5: 4 waves (64x32 each), BK 64, 4 stages (96 KiB)
+    {256, 256, 32, 4, 2, 4, 1},  // 6: as 1, interleaved
+    {256, 256, 64, 2, 2, 2, 1},  // 7: 4 waves (128x128 each), BK 64, 2 stages, interleaved
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -533,11 +599,12 @@ static int tile_override(bool out) {
     return c;
 }
 
-// Default tile shape by problem: 256x256 blocks when there are enough rows and columns, smaller
-// blocks for small T or narrow N.
+// Default tile shape by problem: 256x256 blocks of 8 waves with interleaved fragment reads when there
+// are enough rows and columns (measured best on MI355X at T = 16384), smaller blocks for small T or
+// narrow N.
 static int default_tile(const GemmArgs &a, bool out) {
     (void)out;
-    if (a.T >= 4096 && a.N0 % 256 == 0) return 1;
+    if (a.T >= 4096 && a.N0 % 256 == 0) return 2;
     if (a.N0 % 128 == 0) return 4;
     return 5;
 }
@@ -547,14 +614,14 @@ static hipError_t launch_bf16_auto(const GemmArgs &a, int nB, hipStream_t s) {
     int t = tile_override(OUT);
     if (t < 0 || a.N0 % kTiles[t].bn != 0) t = default_tile(a, OUT);
     switch (t) {
-        case 0: return launch_bf16<256, 256, 64, 2, 2, 4, OUT>(a, nB, s);
-        case 1: return launch_bf16<256, 256, 32, 4, 2, 4, OUT>(a, nB, s);
-        case 2: return launch_bf16<256, 256, 32, 4, 2, 2, OUT>(a, nB, s);
-        case 3: return launch_bf16<256, 128, 64, 3, 2, 2, OUT>(a, nB, s);
-        case 4: return launch_bf16<128, 128, 64, 4, 2, 2, OUT>(a, nB, s);
-        case 6: return launch_bf16<256, 256, 32, 3, 2, 4, OUT>(a, nB, s);
-        case 7: return launch_bf16<128, 256, 64, 3, 2, 2, OUT>(a, nB, s);
-        default: return launch_bf16<128, 64, 64, 4, 2, 2, OUT>(a, nB, s);
+        case 0: return launch_bf16<256, 256, 64, 2, 2, 4, OUT, 0>(a, nB, s);
+        case 1: return launch_bf16<256, 256, 32, 4, 2, 4, OUT, 0>(a, nB, s);
+        case 2: return launch_bf16<256, 256, 64, 2, 2, 4, OUT, 1>(a, nB, s);
+        case 3: return launch_bf16<256, 128, 64, 3, 2, 2, OUT, 0>(a, nB, s);
+        case 4: return launch_bf16<128, 128, 64, 4, 2, 2, OUT, 0>(a, nB, s);
+        case 6: return launch_bf16<256, 256, 32, 4, 2, 4, OUT, 1>(a, nB, s);
+        case 7: return launch_bf16<256, 256, 64, 2, 2, 2, OUT, 1>(a, nB, s);
+        default: return launch_bf16<128, 64, 64, 4, 2, 2, OUT, 0>(a, nB, s);
     }
 }
 
