@@ -12,11 +12,13 @@
 // last real tile exit at once. A rows are gathered through perm (token order -> slot order) while
 // they are staged into LDS; the epilogue scatters rows back to token order (the un-permute).
 //
-// bf16 path: 256 threads = 2 x 2 waves; each wave owns a (BM/2) x (BN/2) block of 32x32 MFMA tiles
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulators). K advances in BK = 64 steps through two LDS
-// buffers: the next A/B tiles are fetched into registers while the current ones feed the MFMAs.
-// LDS rows are 128 bytes of 8 16-byte chunks, chunk c of row r stored at position c ^ (r & 7), so
-// the 16-byte MFMA operand reads of 8 consecutive rows hit 8 different bank groups.
+// bf16 path (T > 64): workgroups of WGM x WGN waves (8 for the default 256 x 256 tile), each wave owning a
+// (BM/WGM) x (BN/WGN) block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16, fp32 accumulators). Operand
+// rows are copied global -> LDS directly (no register round trip), NSTAGE - 1 K steps ahead of the MFMAs;
+// LDS rows are XOR-swizzled so that MFMA operand reads are free of bank conflicts. The tile is written
+// back through LDS as whole 16-byte row chunks. Details at k_grouped_gemm_bf16.
+//
+// Decode path (T <= 64): weight-streaming kernels (k_grouped_gemv_bf16). fp32 data: k_grouped_gemm_f32.
 #include <stdlib.h>
 
 #include "rom_device.h"
@@ -124,6 +126,67 @@ __device__ __forceinline__ void wait_copies(int ahead) {
     else if (MAXAHEAD >= 2 && ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * PER_STEP));
     else if (MAXAHEAD >= 1 && ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(PER_STEP));
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+}
+
+// ---- staged epilogue. Scattering the C^T-layout accumulators straight to the token rows costs one
+// store instruction per 8 bytes and touches 32 rows (cache lines) per instruction. Instead each wave
+// writes its block, converted to bf16 and scaled per row, into an LDS tile of BM x BN, and the
+// workgroup then writes whole 16-byte chunks, consecutive lanes along a row, so one instruction covers
+// 2 (BN = 256) to 8 (BN = 64) full rows. The 16-byte chunk c of LDS row r sits at c ^ (r & (CPR - 1))
+// (CPR = chunks per row, at most 32): the 8-byte writes of 32 consecutive rows at one column and the
+// row-wise 16-byte reads both spread over the banks. The output is not read again by this kernel, so
+// the stores are non-temporal.
+template <int BN>
+__device__ __forceinline__ int ctile_swz(int row) {
+    constexpr int CPR = BN / 8;
+    return row & ((CPR < 32 ? CPR : 32) - 1);
+}
+
+// One wave's FM x FN blocks of 32 x 32 (C^T layout: register r of block (i, j) holds column
+// 8*(r/4) + 4*(lane/32) + r%4 of row lane%32) into LDS rows [row0 + 32 i ..], columns [col0 + 32 j ..],
+// scaled by sc[i].
+template <int FM, int FN, int BN>
+__device__ __forceinline__ void acc_to_ctile(const f32x16 (&acc)[FM][FN], uint16_t *ct, int row0, int col0,
+                                             int lane, const float (&sc)[FM]) {
+    const int half = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int row = row0 + i * 32 + (lane & 31);
+        uint16_t *crow = ct + row * BN;
+        const int swz = ctile_swz<BN>(row);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int col = col0 + j * 32 + 8 * g + 4 * half;
+                uint2 pk;
+                pk.x = pack_bf16x2(acc[i][j][4 * g] * sc[i], acc[i][j][4 * g + 1] * sc[i]);
+                pk.y = pack_bf16x2(acc[i][j][4 * g + 2] * sc[i], acc[i][j][4 * g + 3] * sc[i]);
+                *reinterpret_cast<uint2 *>(crow + (((col >> 3) ^ swz) << 3) + (col & 7)) = pk;
+            }
+    }
+}
+
+// LDS rows [0, nrows) of the tile to their token rows of C (row r goes to row tok[r]), columns
+// [n0, n0 + BN); rows at or past `valid` are not stored.
+template <int BN, int NT>
+__device__ __forceinline__ void ctile_to_global(const uint16_t *ct, int nrows, int valid, const int *tok, uint16_t *C,
+                                                int N0, int n0, int tid) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int CPR = BN / 8;
+#pragma unroll 4
+    for (int idx = tid; idx < nrows * CPR; idx += NT) {
+        const int r = idx / CPR, c = idx % CPR;
+        if (r < valid) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(ct + r * BN + ((c ^ ctile_swz<BN>(r)) << 3));
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(C + (size_t)tok[r] * N0 + n0 + c * 8));
+        }
+    }
+}
+
+// LDS of a bf16 tile configuration: the pipeline stages, or the C tile of the epilogue if larger.
+constexpr size_t gemm_lds_bytes(int BM, int BN, int BK, int NSTAGE) {
+    return (size_t)(NSTAGE * (BM + BN) * BK > BM * BN ? NSTAGE * (BM + BN) * BK : BM * BN) * 2;
 }
 
 template <int BM, int BN, int BK, int NSTAGE, int WGM, int WGN, bool OUT, int SCHED>
@@ -269,26 +332,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
         stage = (stage + 1) % NSTAGE;
     }
 
-    // epilogue: block (i, j) register r holds output column 8*(r/4) + 4*(lane/32) + (r%4) of token
-    // row lane%32 (C^T layout); rows go back to their tokens, scaled by p_t for the out-projection
+    // epilogue through LDS (no copies are in flight after the last step); rows go back to their tokens,
+    // scaled by p_t for the out-projection
+    __syncthreads();
+    float sc[FM];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int row = wm * WM + i * 32 + (lane & 31);
-        if (row < rows) {
-            const int tok = s_tok[row];
-            const float sc = OUT ? s_prob[row] : 1.0f;
-            uint16_t *crow = C + (size_t)tok * p.N0 + n0 + wn * WN + 4 * half;
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    uint2 pk;
-                    pk.x = pack_bf16x2(acc[i][j][4 * g] * sc, acc[i][j][4 * g + 1] * sc);
-                    pk.y = pack_bf16x2(acc[i][j][4 * g + 2] * sc, acc[i][j][4 * g + 3] * sc);
-                    *reinterpret_cast<uint2 *>(crow + j * 32 + 8 * g) = pk;
-                }
-        }
-    }
+    for (int i = 0; i < FM; ++i) sc[i] = OUT ? s_prob[wm * WM + i * 32 + (lane & 31)] : 1.0f;
+    acc_to_ctile<FM, FN, BN>(acc, smem, wm * WM, wn * WN, lane, sc);
+    __syncthreads();
+    ctile_to_global<BN, NT>(smem, BM, rows, s_tok, C, p.N0, n0, tid);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -559,7 +611,7 @@ static hipError_t launch_bf16(const GemmArgs &a0, int nB, hipStream_t s) {
     } else {
         grid = (unsigned)a.m_tiles * a.n_tiles;
     }
-    const size_t smem = (size_t)NSTAGE * (BM + BN) * BK * sizeof(uint16_t);
+    const size_t smem = gemm_lds_bytes(BM, BN, BK, NSTAGE);
     static bool attr_set = false;  // per process; the attribute is per function
     if (!attr_set) {
         hipError_t err = hipFuncSetAttribute(

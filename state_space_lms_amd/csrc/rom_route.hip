@@ -10,7 +10,8 @@
 // The router reads X once (HBM-bound: E flops per element). A wave computes the logits of 8 tokens at
 // a time with all 64 lanes splitting d_model, so each W_r value a lane loads serves 8 tokens; W_r is
 // staged once per workgroup in LDS (when it fits) in a layout where the 64 lanes of a wave read 64
-// consecutive 16-byte words.
+// consecutive 16-byte words. Each lane keeps two chunks of its 8 rows in flight, and the first two are
+// requested before W_r is staged.
 //
 // Launches: T <= 8: one workgroup does everything. Otherwise (1) logits + top-1 + per-workgroup
 // histogram, 32 tokens per workgroup when that gives >= 512 workgroups (one wave per 8 tokens), else
@@ -73,17 +74,41 @@ template <> struct Chunk8<float> {
     }
 };
 
-// Logits of a group of 8 tokens [tok0, tok0+8) for the experts [e0, e0+EG), computed by LPT lanes
-// (LPT = 64 * waves; lane jl = 0..LPT-1). Lane jl sums the 8-element chunks c = jl, jl+LPT, ... of
-// d_model; the next chunk's 8 token rows are fetched while the current one is multiplied (tokens past
-// T read row T-1 and are discarded). Partial sums are then reduce-scattered over lane bits 0..2 (each
-// lane keeps one token) and all-reduced over lane bits 3..5. On return every lane of the wave with
-// (lane & 7) == j holds this wave's partial logits of token tok0 + j in out[0..EG); with LPT > 64
-// the caller still sums the waves. Must be called by every lane of the wave (it shuffles).
-// wl != nullptr: W_r is read from the LDS copy made by stage_router_weight.
+// The 8 token rows of a group [tok0, tok0+8) and two 8-row chunk buffers: lane jl (of LPT lanes) reads
+// the 8-element chunks c = jl, jl+LPT, ... of d_model, chunk jl into `a` and jl+LPT into `b`, so two
+// chunks per row are in flight at a time. Tokens past T read row T-1 and are discarded; chunks past the
+// row end are not loaded.
+template <typename TX> struct XRows {
+    const TX *row[8];
+    Chunk8<TX> a[8], b[8];
+};
+
+// Issues the loads of chunks jl and jl+LPT. Called before the router weight is staged, so that the first
+// X fetches overlap the staging.
+template <typename TX, int LPT>
+__device__ __forceinline__ void xrows_issue(XRows<TX> &xr, const TX *__restrict__ X, int T, int dm, int tok0, int jl) {
+    const int nchunk = dm >> 3;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xr.row[q] = X + (size_t)min(tok0 + q, T - 1) * dm;
+    const int c0 = min(jl, nchunk - 1);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xr.a[q].load(xr.row[q] + c0 * 8);
+    if (jl + LPT < nchunk) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) xr.b[q].load(xr.row[q] + (jl + LPT) * 8);
+    }
+}
+
+// Logits of the 8 tokens of xr (whose first two chunks are in flight) for the experts [e0, e0+EG),
+// computed by LPT lanes (LPT = 64 * waves; lane jl = 0..LPT-1). Each lane's partial sums over its chunks
+// are then reduce-scattered over lane bits 0..2 (each lane keeps one token) and all-reduced over lane
+// bits 3..5. On return every lane of the wave with (lane & 7) == j holds this wave's partial logits of
+// token tok0 + j in out[0..EG); with LPT > 64 the caller still sums the waves. Must be called by every
+// lane of the wave (it shuffles). wl != nullptr: W_r is read from the LDS copy made by
+// stage_router_weight.
 template <typename TX, int LPT, int EG>
-__device__ __forceinline__ void logits_group8(const TX *__restrict__ X, int T, int dm, const float *__restrict__ Wr,
-                                              const float4 *wl, int E, int e0, int tok0, int jl, float out[EG]) {
+__device__ __forceinline__ void logits_group8(XRows<TX> &xr, int dm, const float *__restrict__ Wr, const float4 *wl,
+                                              int E, int e0, int jl, float out[EG]) {
     float acc[8][EG];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
@@ -93,23 +118,8 @@ __device__ __forceinline__ void logits_group8(const TX *__restrict__ X, int T, i
     const int nchunk = dm >> 3;
     const bool vecw = (E % 4 == 0) && (EG % 4 == 0) && (e0 + EG <= E);
     const int e4 = E >> 2;
-    const TX *xrow[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) xrow[q] = X + (size_t)min(tok0 + q, T - 1) * dm;
-    // chunk indices are clamped to the last chunk so every load is in bounds and unconditional
-    Chunk8<TX> nxt[8];
-    {
-        const int c0 = min(jl, nchunk - 1);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) nxt[q].load(xrow[q] + c0 * 8);
-    }
-    for (int c = jl; c < nchunk; c += LPT) {
-        Chunk8<TX> cur[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) cur[q] = nxt[q];
-        const int cn = min(c + LPT, nchunk - 1);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) nxt[q].load(xrow[q] + cn * 8);
+    // acc += the 8 rows' chunk c (held in buf) times W_r rows [8c, 8c+8)
+    auto mac = [&](const Chunk8<TX>(&buf)[8], int c) {
         float w[8][EG];
         if (wl != nullptr && vecw) {
 #pragma unroll
@@ -138,11 +148,26 @@ __device__ __forceinline__ void logits_group8(const TX *__restrict__ X, int T, i
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             float xf[8];
-            cur[q].unpack(xf);
+            buf[q].unpack(xf);
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
                 for (int x = 0; x < EG; ++x) acc[q][x] = fmaf(xf[kk], w[kk][x], acc[q][x]);
+        }
+    };
+    // chunks c (in a) and c + LPT (in b); each buffer is refilled two strides ahead as soon as it is used
+    for (int c = jl; c < nchunk; c += 2 * LPT) {
+        mac(xr.a, c);
+        if (c + 2 * LPT < nchunk) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) xr.a[q].load(xr.row[q] + (c + 2 * LPT) * 8);
+        }
+        if (c + LPT < nchunk) {
+            mac(xr.b, c + LPT);
+            if (c + 3 * LPT < nchunk) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) xr.b[q].load(xr.row[q] + (c + 3 * LPT) * 8);
+            }
         }
     }
     // reduce-scatter over lane bits 2, 1, 0: after the three steps lane j keeps token (j & 7)
@@ -176,15 +201,16 @@ __device__ __forceinline__ void logits_group8(const TX *__restrict__ X, int T, i
 }
 
 // All E logits (this wave's share when LPT > 64) of token (tok0 + (jl & 7)) into lg[0..EMAX)
-// (entries >= E are -inf).
+// (entries >= E are -inf). xr holds the issued first chunks; later expert groups re-read X.
 template <typename TX, int LPT, int EG, int EMAX>
-__device__ __forceinline__ void logits_token(const TX *X, int T, int dm, const float *Wr, const float4 *wl, int E,
-                                             int tok0, int jl, float lg[EMAX]) {
+__device__ __forceinline__ void logits_token(XRows<TX> &xr, const TX *X, int T, int dm, const float *Wr,
+                                             const float4 *wl, int E, int tok0, int jl, float lg[EMAX]) {
 #pragma unroll
     for (int g = 0; g < EMAX / EG; ++g) {
         if (g * EG < E) {  // uniform
+            if (g > 0) xrows_issue<TX, LPT>(xr, X, T, dm, tok0, jl);
             float o[EG];
-            logits_group8<TX, LPT, EG>(X, T, dm, Wr, wl, E, g * EG, tok0, jl, o);
+            logits_group8<TX, LPT, EG>(xr, dm, Wr, wl, E, g * EG, jl, o);
 #pragma unroll
             for (int x = 0; x < EG; ++x) lg[g * EG + x] = (g * EG + x < E) ? o[x] : -INFINITY;
         } else {
@@ -194,20 +220,31 @@ __device__ __forceinline__ void logits_token(const TX *X, int T, int dm, const f
     }
 }
 
-// Logits of the workgroup's tokens. WPG = 1: wave w owns the 8 tokens [tok_base + 8w, +8).
-// WPG = 4: the four waves split d_model for the 8 tokens [tok_base, +8) and their partial sums are
-// added in wave order through LDS (s_red). On return, lanes 0..7 of every wave (WPG = 1) or of
-// wave 0 (WPG = 4) hold the full logits of token tok0 + lane, where tok0 is returned.
-template <typename TX, int EG, int EMAX, int WPG>
-__device__ __forceinline__ int wg_logits(const TX *X, int T, int dm, const float *Wr, const float4 *wl, int E,
-                                         int tok_base, float lg[EMAX], float (*s_red)[8][EMAX]) {
+// The token group and lane index of this thread in wg_logits: WPG = 1: wave w owns the 8 tokens
+// [tok_base + 8w, +8) with lanes 0..63; WPG = 4: the four waves split d_model (lanes 0..255) for the 8
+// tokens [tok_base, +8).
+template <int WPG>
+__device__ __forceinline__ void wg_token_group(int tok_base, int &tok0, int &jl) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    tok0 = WPG == 1 ? tok_base + wave * 8 : tok_base;
+    jl = WPG == 1 ? lane : wave * 64 + lane;
+}
+
+// Logits of the workgroup's tokens (xr issued by xrows_issue for the group of wg_token_group). With
+// WPG = 4 the waves' partial sums are added in wave order through LDS (s_red). On return, lanes 0..7
+// of every wave (WPG = 1) or of wave 0 (WPG = 4) hold the full logits of token tok0 + lane, where tok0
+// is returned.
+template <typename TX, int EG, int EMAX, int WPG>
+__device__ __forceinline__ int wg_logits(XRows<TX> &xr, const TX *X, int T, int dm, const float *Wr, const float4 *wl,
+                                         int E, int tok_base, float lg[EMAX], float (*s_red)[8][EMAX]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int tok0, jl;
+    wg_token_group<WPG>(tok_base, tok0, jl);
     if (WPG == 1) {
-        const int tok0 = tok_base + wave * 8;
-        logits_token<TX, 64, EG, EMAX>(X, T, dm, Wr, wl, E, tok0, lane, lg);
+        logits_token<TX, 64, EG, EMAX>(xr, X, T, dm, Wr, wl, E, tok0, jl, lg);
         return tok0;
     }
-    logits_token<TX, 256, EG, EMAX>(X, T, dm, Wr, wl, E, tok_base, wave * 64 + lane, lg);
+    logits_token<TX, 256, EG, EMAX>(xr, X, T, dm, Wr, wl, E, tok0, jl, lg);
     if (lane < 8) {
 #pragma unroll
         for (int e = 0; e < EMAX; ++e) s_red[wave][lane][e] = lg[e];
@@ -285,11 +322,17 @@ __global__ __launch_bounds__(256) void k_route_logits(const TX *__restrict__ X, 
     __shared__ float s_red[WPG == 4 ? 4 : 1][8][EMAX];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int i = tid; i < E; i += 256) hist[i] = 0;
+    XRows<TX> xr;
+    {
+        int g0, jl;
+        wg_token_group<WPG>(blockIdx.x * TPW, g0, jl);
+        xrows_issue<TX, WPG * 64>(xr, X, T, dm, g0, jl);
+    }
     if (use_lds) stage_router_weight(Wr, dm, E, wl_dyn);
     __syncthreads();
     float lg[EMAX];
-    const int tok0 = wg_logits<TX, EG, EMAX, WPG>(X, T, dm, Wr, use_lds ? wl_dyn : nullptr, E, blockIdx.x * TPW, lg,
-                                                  s_red);
+    const int tok0 = wg_logits<TX, EG, EMAX, WPG>(xr, X, T, dm, Wr, use_lds ? wl_dyn : nullptr, E, blockIdx.x * TPW,
+                                                  lg, s_red);
     const int t = tok0 + lane;
     if (lane < 8 && (WPG == 1 || wave == 0) && t < T) {
         int best;
@@ -376,10 +419,16 @@ __global__ __launch_bounds__(256) void k_route_small(const TX *__restrict__ X, i
     __shared__ int s_pos[kRouteSmallT];
     __shared__ float s_red[4][8][EMAX];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    XRows<TX> xr;
+    {
+        int g0, jl;
+        wg_token_group<4>(0, g0, jl);
+        xrows_issue<TX, 256>(xr, X, T, dm, g0, jl);
+    }
     if (use_lds) stage_router_weight(Wr, dm, E, wl_dyn);
     __syncthreads();
     float lg[EMAX];
-    wg_logits<TX, EG, EMAX, 4>(X, T, dm, Wr, use_lds ? wl_dyn : nullptr, E, 0, lg, s_red);
+    wg_logits<TX, EG, EMAX, 4>(xr, X, T, dm, Wr, use_lds ? wl_dyn : nullptr, E, 0, lg, s_red);
     if (wave == 0 && lane < T) {
         int best;
         float p;
