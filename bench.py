@@ -120,7 +120,7 @@ def main() -> int:
     Wc, Wg, Wo = up(inp["W_conv"], w.dtype), up(inp["W_gate"], w.dtype), up(inp["W_out"], w.dtype)
     Wr = up(inp["W_router"], "f32")
     bias = up(inp["bias"], "f32") if inp.get("bias") is not None else None
-    routing = rom.Routing(w.T, w.E, dev)
+    routing = rom.Routing(w.T, w.E, dev, top_k=w.top_k)
     x = torch.empty((w.T, w.d_inner), dtype=X.dtype, device=dev)
     z = torch.empty_like(x)
     out = torch.empty((w.T, w.d_model), dtype=X.dtype, device=dev)
@@ -137,7 +137,7 @@ def main() -> int:
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        rom.route(X, Wr, bias, routing=routing, stream=stream)
+        rom.route(X, Wr, bias, top_k=w.top_k, routing=routing, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         rom.in_proj(X, routing, Wc, Wg, x, z, stream=stream)
@@ -175,12 +175,12 @@ def main() -> int:
     t_route = np.array([e[0].elapsed_time(e[1]) for e in events]) * 1e-3
     t_in = np.array([e[1].elapsed_time(e[2]) for e in events]) * 1e-3
     t_out = np.array([e[2].elapsed_time(e[3]) for e in events]) * 1e-3
-    fl_in = 4.0 * w.T * w.d_model * w.d_inner
-    fl_out = 2.0 * w.T * w.d_model * w.d_inner
+    fl_in = 4.0 * w.T * w.d_model * w.d_inner * w.top_k
+    fl_out = 2.0 * w.T * w.d_model * w.d_inner * w.top_k
     peak = PEAK_MFMA_TFLOPS[w.dtype]
-    counts = routing.counts.cpu().numpy()
+    counts = routing.counts.cpu().numpy()  # [top_k][E]
     es = 2 if w.dtype == "bf16" else 4
-    used = int(np.count_nonzero(counts))
+    used = int(np.count_nonzero(counts))  # expert stacks streamed, summed over the choices
     # algorithmic bytes: every operand and result moved once, only the experts that received tokens
     bytes_in = es * (w.T * w.d_model + used * 2 * w.d_inner * w.d_model + 2 * w.T * w.d_inner)
     bytes_out = es * (2 * w.T * w.d_inner + used * w.d_model * w.d_inner + w.T * w.d_model) + 4 * w.T * 2
@@ -219,8 +219,8 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic: seeded Gaussian tensors of the workload's shapes (no dataset)",
         "config": {"workload": w.name, "T": w.T, "d_model": w.d_model, "d_inner": w.d_inner, "E": w.E,
-                   "top_k": 1, "router": "fp32", "cache": "cold" if args.cold else "warm",
-                   "expert_loads": counts.tolist()},
+                   "top_k": w.top_k, "router": "fp32", "cache": "cold" if args.cold else "warm",
+                   "expert_loads": counts[0].tolist() if w.top_k == 1 else counts.tolist()},
         "roofline": roof,
         "breakdown": {
             "route_us": round(mean_route * 1e6, 2),

@@ -8,8 +8,9 @@
  *   H_t = sum_i 1[i in S_t] x_t W_in,i         G_t = SiLU(sum_i 1[i in S_t] x_t W_g,i);
  *   O_t = sum_i r_t,i (Y_t (.) G_t) W_out,i.
  * One router per block, shared by the Conv (input), Gate and Out projections (Knowl 1, and the
- * authors' rebuttal on the paperhub.cn page, reply to reviewer VBDT), one of eight experts per
- * token, dropless: no capacity factor and no token dropping (Knowl 12).
+ * authors' rebuttal on the paperhub.cn page, reply to reviewer VBDT), one (top-1) or two (top-2)
+ * of the experts per token, dropless: no capacity factor and no token dropping (Knowl 12). The page's
+ * scaling notes (Knowl 1) measure the 8top1, 16top1 and 8top2 settings.
  *
  * Conventions for every entry point
  *  - Pointers named in a signature are DEVICE pointers unless marked "host". The caller owns every
@@ -21,8 +22,8 @@
  *  - Arguments are validated before anything is enqueued; on a non-OK return nothing was enqueued,
  *    except for ROM_ERR_HIP, which reports a failed launch. rom_last_error() gives details.
  *  - T == 0 is a valid no-op (ROM_OK, nothing enqueued, no buffer touched).
- *  - Supported range: 1 <= E <= ROM_MAX_EXPERTS, top_k == 1, d_model and d_inner multiples of 64,
- *    T <= ROM_MAX_TOKENS. dtype is the storage type of X, the expert stacks, z, h and all outputs;
+ *  - Supported range: 1 <= E <= ROM_MAX_EXPERTS, 1 <= top_k <= min(E, ROM_MAX_TOP_K), d_model and
+ *    d_inner multiples of 64, T <= ROM_MAX_TOKENS. dtype is the storage type of X, the expert stacks, z, h and all outputs;
  *    the router weight and bias are always fp32. bf16 data is accumulated in fp32 on MFMA; fp32
  *    data is computed in fp32 throughout.
  *  - Expert matrices are stored transposed relative to the page's x_t W notation, as [out][in]
@@ -39,17 +40,18 @@
 extern "C" {
 #endif
 
-#define ROM_ABI_VERSION 2
+#define ROM_ABI_VERSION 3
 #ifndef ROM_API
 #define ROM_API __attribute__((visibility("default")))
 #endif
 #define ROM_MAX_EXPERTS 64
+#define ROM_MAX_TOP_K 2
 #define ROM_MAX_TOKENS (1 << 24)
 
 typedef enum {
     ROM_OK = 0,
     ROM_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative or inconsistent size, misalignment */
-    ROM_ERR_UNSUPPORTED = 2,        /* valid but outside the supported range (top_k != 1, E > 64, ...) */
+    ROM_ERR_UNSUPPORTED = 2,        /* valid but outside the supported range (top_k > 2, E > 64, ...) */
     ROM_ERR_WORKSPACE_TOO_SMALL = 3,
     ROM_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
 } rom_status;
@@ -57,41 +59,46 @@ typedef enum {
 typedef enum { ROM_DTYPE_F32 = 0, ROM_DTYPE_BF16 = 1 } rom_dtype;
 
 /*
- * The routing decision of one block for T tokens (Knowl 1: S_t and r_t,i; for top-1 these are
- * one expert id and one probability per token), plus the grouping that the grouped projections
- * use. A host struct of caller-owned DEVICE buffers: rom_route fills the buffers and stamps T, E
- * and top_k; rom_in_proj and rom_out_proj read them.
+ * The routing decision of one block for T tokens (Knowl 1: S_t and r_t,i), plus the grouping that the
+ * grouped projections use. A host struct of caller-owned DEVICE buffers: rom_route fills the buffers
+ * and stamps T, E and top_k; rom_in_proj and rom_out_proj read them.
+ *
+ * With top_k = K the buffers hold K stacked top-1 routings, choice k = 0 .. K-1 (k = 0 the largest
+ * logit, k = 1 the second largest): each array below is K times the size shown, slice k at offset
+ * k * (size shown). Slice k groups the tokens by their k-th choice on its own.
  */
 typedef struct rom_routing {
     int32_t T, E, top_k;     /* stamped by rom_route; checked by the projections */
     int32_t reserved;        /* zero */
-    int32_t *expert_id;      /* [T]   e*_t = argmax_j logit_t,j, lowest j on ties */
-    float *prob;             /* [T]   p_t,e*: the full softmax over E experts, not renormalised */
-    int32_t *counts;         /* [E]   tokens routed to each expert (sum = T) */
-    int32_t *offsets;        /* [E+1] exclusive prefix sum of counts; offsets[E] = T */
-    int32_t *perm;           /* [T]   slot -> token: expert-major, ascending token id within an expert */
-    int32_t *inv_perm;       /* [T]   token -> slot (perm[inv_perm[t]] == t) */
+    int32_t *expert_id;      /* [K][T]   choice k of token t; ties keep the lowest index */
+    float *prob;             /* [K][T]   p_t,e of that expert: the full softmax over E experts, not renormalised */
+    int32_t *counts;         /* [K][E]   tokens whose choice k is each expert (sum over e = T) */
+    int32_t *offsets;        /* [K][E+1] exclusive prefix sum of counts; offsets[k][E] = T */
+    int32_t *perm;           /* [K][T]   slot -> token: expert-major, ascending token id within an expert */
+    int32_t *inv_perm;       /* [K][T]   token -> slot (perm[k][inv_perm[k][t]] == t) */
 } rom_routing;
 
 /* ROM_ABI_VERSION of the loaded library. */
 ROM_API int rom_abi_version(void);
 
-/* Bytes of device workspace rom_route needs for T tokens and E experts (0 when T == 0). */
+/* Bytes of device workspace rom_route needs for T tokens and E experts, for any top_k (0 when T == 0). */
 ROM_API size_t rom_route_workspace_bytes(int32_t T, int32_t E);
 
 /*
  * Router, histogram, stable counting sort and (optionally) permute.
  * Knowl 1's router: logit_t,j = sum_k X[t][k] * W_router[k][j] (+ bias[j]) in fp32 (bf16 X is
- * widened exactly); e*_t = argmax_j logit_t,j with the lowest index on ties; prob_t =
- * 1 / sum_j exp(logit_t,j - logit_t,e*). The grouping (not on the page; a dropless grouped
- * computation needs it, Knowl 12): counts, offsets, and slot pos(t) = offsets[e*_t] +
- * #{t' < t : e*_t' = e*_t}, written as perm[pos(t)] = t and inv_perm[t] = pos(t).
+ * widened exactly); choice 0 = argmax_j logit_t,j with the lowest index on ties, choice 1 (top_k = 2)
+ * = the argmax over the other experts, again lowest index on ties; the probability of expert e is
+ * exp(logit_t,e - logit_t,max) / sum_j exp(logit_t,j - logit_t,max). The grouping of each choice k
+ * (not on the page; a dropless grouped computation needs it, Knowl 12): counts, offsets, and slot
+ * pos(t) = offsets[e_t] + #{t' < t : e_t' = e_t}, written as perm[pos(t)] = t, inv_perm[t] = pos(t).
  *
  *   X         [T][d_model], x_dtype
  *   W_router  [d_model][E] fp32;  bias [E] fp32 or NULL (a workload device; the page has none)
- *   top_k     must be 1
+ *   top_k     1 or 2 (at most E)
  *   routing   host pointer to a struct whose six device buffers are sized as documented above
- *   X_perm    NULL, or [T][d_model] x_dtype: receives X_perm[pos] = X[perm[pos]] (the permute)
+ *   X_perm    NULL, or [T][d_model] x_dtype: receives X_perm[pos] = X[perm[pos]] (the permute;
+ *             top_k = 1 only)
  *   workspace device scratch of at least rom_route_workspace_bytes(T, E) bytes; its contents on
  *             entry do not matter and are clobbered
  */
@@ -101,12 +108,12 @@ ROM_API rom_status rom_route(const void *X, rom_dtype x_dtype, int32_t T, int32_
                      void *stream);
 
 /*
- * In-projection experts (Knowl 1, H_t and the argument of SiLU in G_t): for every token t with
- * expert e = expert_id[t],
- *   x_out[t][n] = sum_k X[t][k] * W_conv[e][n][k],   z_out[t][n] = sum_k X[t][k] * W_gate[e][n][k]
- * with no probability scale (the indicator only). Computed as one ragged grouped GEMM over the
- * expert groups of `routing`; outputs are written in token order. z_out is the pre-activation
- * gate: SiLU is applied by rom_out_proj.
+ * In-projection experts (Knowl 1, H_t and the argument of SiLU in G_t): for every token t,
+ *   x_out[t][n] = sum_{e in S_t} sum_k X[t][k] * W_conv[e][n][k]   (z_out likewise with W_gate)
+ * with no probability scale (the indicator only). Computed as one ragged grouped GEMM per choice k
+ * over the expert groups of slice k of `routing`; the choices are added in the order k = 0, 1, the
+ * first rounded to dtype before the second is added. Outputs are in token order. z_out is the
+ * pre-activation gate: SiLU is applied by rom_out_proj.
  *   X [T][d_model]; W_conv, W_gate [E][d_inner][d_model]; x_out, z_out [T][d_inner]; all dtype.
  *   X may not alias an output; x_out and z_out may not overlap.
  */
@@ -120,11 +127,12 @@ ROM_API size_t rom_out_proj_workspace_bytes(int32_t T, int32_t d_inner, rom_dtyp
 /*
  * Out-projection experts (Knowl 1, O_t), with h standing in for the SSM-core output Y_t:
  *   a[t][n]   = SiLU(z[t][n]) * h[t][n],  SiLU(v) = v / (1 + exp(-v)), in fp32
- *   out[t][m] = prob[t] * sum_n a[t][n] * W_out[e][m][n],  e = expert_id[t]
+ *   out[t][m] = sum_{e in S_t} p_t,e * sum_n a[t][n] * W_out[e][m][n]
  * The probability scale is r_t,e of Knowl 1 (stated only in that secondary summary: the authors'
  * own text does not write the formula). For bf16 data, a is rounded to bf16 once before the
- * MFMA product; accumulation is fp32; out is rounded once. For bf16 data with T > 64 the gated rows
- * a are first written, in slot order, to the workspace, which the grouped GEMM then streams.
+ * MFMA product; accumulation is fp32; each choice's contribution is rounded once, added in the order
+ * k = 0, 1 as for the in-projection. For bf16 data with T > 64 the gated rows a are first written to
+ * the workspace (in slot order for top_k = 1, token order for top_k = 2), which the grouped GEMMs read.
  *   z, h [T][d_inner]; W_out [E][d_model][d_inner]; out [T][d_model]; all dtype. out may not alias z or h.
  *   workspace  device scratch of at least rom_out_proj_workspace_bytes(T, d_inner, dtype) bytes
  *              (may be NULL when that is 0); contents on entry do not matter and are clobbered.

@@ -26,7 +26,7 @@ __all__ = ["route", "in_proj", "out_proj", "Routing", "RomError", "lib", "LIB_PA
            "route_workspace_bytes", "out_proj_workspace_bytes"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "librom.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 ROM_OK, ROM_ERR_INVALID_ARGUMENT, ROM_ERR_UNSUPPORTED, ROM_ERR_WORKSPACE_TOO_SMALL, ROM_ERR_HIP = range(5)
 ROM_DTYPE_F32, ROM_DTYPE_BF16 = 0, 1
@@ -119,18 +119,21 @@ def route_workspace_bytes(T: int, E: int) -> int:
 
 
 class Routing:
-    """The device buffers of one routing decision (``rom_routing``), reusable across calls of the same T and E."""
+    """The device buffers of one routing decision (``rom_routing``), reusable across calls of the same T, E
+    and top_k. With top_k = K every array holds K stacked top-1 routings (choice k = row k): expert_id,
+    prob, perm, inv_perm are [K][T], counts [K][E], offsets [K][E+1]."""
 
     def __init__(self, T: int, E: int, device, top_k: int = 1):
         device = torch.device(device)
         i32 = dict(dtype=torch.int32, device=device)
         self.T, self.E, self.top_k, self.device = T, E, top_k, device
-        self.expert_id = torch.empty(T, **i32)
-        self.prob = torch.empty(T, dtype=torch.float32, device=device)
-        self.counts = torch.empty(E, **i32)
-        self.offsets = torch.empty(E + 1, **i32)
-        self.perm = torch.empty(T, **i32)
-        self.inv_perm = torch.empty(T, **i32)
+        K = top_k
+        self.expert_id = torch.empty((K, T), **i32)
+        self.prob = torch.empty((K, T), dtype=torch.float32, device=device)
+        self.counts = torch.empty((K, E), **i32)
+        self.offsets = torch.empty((K, E + 1), **i32)
+        self.perm = torch.empty((K, T), **i32)
+        self.inv_perm = torch.empty((K, T), **i32)
         self.workspace = torch.empty(max(route_workspace_bytes(T, E), 256), dtype=torch.uint8, device=device)
         self.x_perm: Optional[torch.Tensor] = None
         self.out_workspace: Optional[torch.Tensor] = None  # gated rows for rom_out_proj, sized on first use
@@ -140,7 +143,7 @@ class Routing:
 
 def route(X: torch.Tensor, W_router: torch.Tensor, bias: Optional[torch.Tensor] = None, top_k: int = 1,
           permute: bool = False, routing: Optional[Routing] = None, stream=None) -> Routing:
-    """rom_route: fp32 router, top-1, probability, histogram, stable counting sort (and the permute)."""
+    """rom_route: fp32 router, top-1 or top-2, probabilities, histogram, stable counting sort (and the permute)."""
     _dev(X, "X")
     _dev(W_router, "W_router")
     if W_router.dtype != torch.float32:
@@ -152,8 +155,8 @@ def route(X: torch.Tensor, W_router: torch.Tensor, bias: Optional[torch.Tensor] 
         if bias.dtype != torch.float32 or bias.shape != (E,):
             raise ValueError("bias must be fp32 of shape [E]")
     r = routing if routing is not None else Routing(T, E, X.device, top_k)
-    if (r.T, r.E) != (T, E):
-        raise ValueError("routing buffers were sized for another T or E")
+    if (r.T, r.E, r.top_k) != (T, E, top_k):
+        raise ValueError("routing buffers were sized for another T, E or top_k")
     if permute:
         if r.x_perm is None or r.x_perm.dtype != X.dtype or r.x_perm.shape != X.shape:
             r.x_perm = torch.empty_like(X)
@@ -167,7 +170,8 @@ def route(X: torch.Tensor, W_router: torch.Tensor, bias: Optional[torch.Tensor] 
 def in_proj(X: torch.Tensor, routing: Routing, W_conv: torch.Tensor, W_gate: torch.Tensor,
             x_out: Optional[torch.Tensor] = None, z_out: Optional[torch.Tensor] = None,
             stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """rom_in_proj: x = W_conv[e] X, z = W_gate[e] X per token (token order, no probability scale)."""
+    """rom_in_proj: x = sum over the token's experts of W_conv[e] X, z likewise with W_gate (token order, no
+    probability scale)."""
     for t, n in ((X, "X"), (W_conv, "W_conv"), (W_gate, "W_gate")):
         _dev(t, n)
     T, dm = X.shape
@@ -192,7 +196,7 @@ def out_proj_workspace_bytes(T: int, d_inner: int, dtype: torch.dtype) -> int:
 def out_proj(z: torch.Tensor, h: torch.Tensor, routing: Routing, W_out: torch.Tensor,
              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
              stream=None) -> torch.Tensor:
-    """rom_out_proj: out = p_t * W_out[e] (SiLU(z) * h) per token (token order)."""
+    """rom_out_proj: out = sum over the token's experts of p_t,e * W_out[e] (SiLU(z) * h) (token order)."""
     for t, n in ((z, "z"), (h, "h"), (W_out, "W_out")):
         _dev(t, n)
     T, di = z.shape

@@ -56,7 +56,8 @@ rom_status check_experts(int32_t E, int32_t top_k) {
     if (E < 1) return fail(ROM_ERR_INVALID_ARGUMENT, "E = %d must be at least 1", E);
     if (E > ROM_MAX_EXPERTS) return fail(ROM_ERR_UNSUPPORTED, "E = %d exceeds ROM_MAX_EXPERTS (%d)", E, ROM_MAX_EXPERTS);
     if (top_k < 1 || top_k > E) return fail(ROM_ERR_INVALID_ARGUMENT, "top_k = %d outside [1, E]", top_k);
-    if (top_k != 1) return fail(ROM_ERR_UNSUPPORTED, "top_k = %d: only top-1 routing is implemented", top_k);
+    if (top_k > ROM_MAX_TOP_K)
+        return fail(ROM_ERR_UNSUPPORTED, "top_k = %d exceeds ROM_MAX_TOP_K (%d)", top_k, ROM_MAX_TOP_K);
     return ROM_OK;
 }
 
@@ -82,7 +83,7 @@ int rom_abi_version(void) { return ROM_ABI_VERSION; }
 
 size_t rom_route_workspace_bytes(int32_t T, int32_t E) {
     if (T <= 0 || E <= 0) return 0;
-    const size_t b = (size_t)E * (size_t)rom::route_workgroups(T) * sizeof(int32_t);
+    const size_t b = (size_t)ROM_MAX_TOP_K * E * (size_t)rom::route_workgroups(T) * sizeof(int32_t);
     return (b + 255) & ~(size_t)255;
 }
 
@@ -111,6 +112,7 @@ rom_status rom_route(const void *X, rom_dtype x_dtype, int32_t T, int32_t d_mode
     ROM_CHECK_PTR(routing->perm, 4);
     ROM_CHECK_PTR(routing->inv_perm, 4);
     if (X_perm != nullptr) {
+        if (top_k != 1) return fail(ROM_ERR_UNSUPPORTED, "X_perm (the materialised permute) needs top_k == 1");
         if (!aligned(X_perm, 16)) return fail(ROM_ERR_INVALID_ARGUMENT, "X_perm is not 16-byte aligned");
         const size_t xb = (size_t)T * d_model * elem_size(x_dtype);
         if (overlap(X, xb, X_perm, xb)) return fail(ROM_ERR_INVALID_ARGUMENT, "X_perm overlaps X");

@@ -42,6 +42,8 @@ struct GemmArgs {
     int m_tiles;          // M-tiles launched (upper bound of the real ones)
     int group_m;          // XCD-aware order: M-tiles per group (0: plain row-major order)
     int per_xcd;          // XCD-aware order: tiles assigned to each of the 8 XCDs
+    int accumulate;       // 1: add to the values already in C (the second choice of a top-2 routing)
+    int a_by_token;       // out-projection: A rows are in token order (gathered through perm), not slot order
 };
 
 // Tile (mt, nt) of workgroup blockIdx.x; false if the workgroup has no tile.
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
         const int slot = slot0 + min(i, rows - 1);
         const int tok = p.perm[slot];
         s_tok[i] = tok;
-        s_arow[i] = OUT ? slot : tok;
+        s_arow[i] = (OUT && !p.a_by_token) ? slot : tok;
         if (OUT) s_prob[i] = p.prob[tok];
     }
     __syncthreads();
@@ -332,8 +334,34 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
         stage = (stage + 1) % NSTAGE;
     }
 
-    // epilogue through LDS (no copies are in flight after the last step); rows go back to their tokens,
-    // scaled by p_t for the out-projection
+    // epilogue; rows go back to their tokens, scaled by p_t for the out-projection
+    if (p.accumulate) {
+        // C += result, straight from the C^T-layout registers (one rounding of the sum): register r of
+        // block (i, j) holds column 8*(r/4) + 4*half + r%4 of token row lane%32
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = wm * WM + i * 32 + (lane & 31);
+            if (row < rows) {
+                const float sc = OUT ? s_prob[row] : 1.0f;
+                uint16_t *crow = C + (size_t)s_tok[row] * p.N0 + n0 + wn * WN + 4 * half;
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        uint2 *dst = reinterpret_cast<uint2 *>(crow + j * 32 + 8 * g);
+                        const uint2 old = *dst;
+                        uint2 pk;
+                        pk.x = pack_bf16x2(fmaf(acc[i][j][4 * g], sc, __uint_as_float(old.x << 16)),
+                                           fmaf(acc[i][j][4 * g + 1], sc, __uint_as_float(old.x & 0xFFFF0000u)));
+                        pk.y = pack_bf16x2(fmaf(acc[i][j][4 * g + 2], sc, __uint_as_float(old.y << 16)),
+                                           fmaf(acc[i][j][4 * g + 3], sc, __uint_as_float(old.y & 0xFFFF0000u)));
+                        *dst = pk;
+                    }
+            }
+        }
+        return;
+    }
+    // through LDS (no copies are in flight after the last step)
     __syncthreads();
     float sc[FM];
 #pragma unroll
@@ -346,7 +374,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
 // ---------------------------------------------------------------------------------------------
 // Gate and permute for the out-projection (bf16): a[pos][n] = bf16(SiLU(z[t][n]) * h[t][n]) with
 // t = perm[pos], fp32 arithmetic, rows written in slot order so the GEMM reads each expert's rows
-// contiguously. Memory-bound: 8 rows per workgroup, 32 lanes per row, 4 chunks of 8 elements in
+// contiguously; with perm == NULL, t = pos (token order, shared by the two choices of a top-2 routing). Memory-bound: 8 rows per workgroup, 32 lanes per row, 4 chunks of 8 elements in
 // flight per lane (chunk indices past the row end are clamped for the loads and not stored).
 __global__ __launch_bounds__(256) void k_gate_permute(const uint16_t *__restrict__ z, const uint16_t *__restrict__ h,
                                                       const int32_t *__restrict__ perm, int T, int di,
@@ -354,7 +382,7 @@ __global__ __launch_bounds__(256) void k_gate_permute(const uint16_t *__restrict
     const int pos = blockIdx.x * 8 + (threadIdx.x >> 5);
     if (pos >= T) return;
     const int l = threadIdx.x & 31;
-    const int tok = perm[pos];
+    const int tok = perm != nullptr ? perm[pos] : pos;
     const int cpr = di >> 3;  // 16-byte chunks per row
     const uint4 *zr = reinterpret_cast<const uint4 *>(z + (size_t)tok * di);
     const uint4 *hr = reinterpret_cast<const uint4 *>(h + (size_t)tok * di);
@@ -477,7 +505,8 @@ __device__ __forceinline__ void gemv_block(const GemmArgs &p, int e, int o0, int
             float v = 0.0f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) v += s_red[w][b][n][m];
-            C[(size_t)s_tok[col] * p.N0 + n0 + n] = f32_to_bf16(v * s_prob[col]);
+            uint16_t *dst = C + (size_t)s_tok[col] * p.N0 + n0 + n;
+            *dst = f32_to_bf16(p.accumulate ? fmaf(v, s_prob[col], bf16_to_f32(*dst)) : v * s_prob[col]);
         }
     }
 }
@@ -577,7 +606,12 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs p) {
             const int t = s_tok[row];
             const float sc = OUT ? s_prob[row] : 1.0f;
             float4 v = make_float4(acc[i][0] * sc, acc[i][1] * sc, acc[i][2] * sc, acc[i][3] * sc);
-            *reinterpret_cast<float4 *>(C + (size_t)t * p.N0 + n0 + tx * 4) = v;
+            float4 *dst = reinterpret_cast<float4 *>(C + (size_t)t * p.N0 + n0 + tx * 4);
+            if (p.accumulate) {
+                const float4 o = *dst;
+                v = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+            }
+            *dst = v;
         }
     }
 }
@@ -687,6 +721,15 @@ static hipError_t launch_f32(const GemmArgs &a0, int nB, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Choice k of a stacked top-K routing as the arguments of one top-1 grouped product: the second choice
+// adds to what the first wrote.
+static void set_choice(GemmArgs &a, const rom_routing &r, int T, int k) {
+    a.offsets = r.offsets + k * (r.E + 1);
+    a.perm = r.perm + (size_t)k * T;
+    a.prob = r.prob + (size_t)k * T;
+    a.accumulate = k > 0;
+}
+
 hipError_t launch_in_proj(const void *X, const rom_routing &r, rom_dtype dt, int T, int dm, int di, const void *Wc,
                           const void *Wg, void *x_out, void *z_out, hipStream_t s) {
     GemmArgs a{};
@@ -695,16 +738,19 @@ hipError_t launch_in_proj(const void *X, const rom_routing &r, rom_dtype dt, int
     a.B1 = Wg;
     a.C0 = x_out;
     a.C1 = z_out;
-    a.offsets = r.offsets;
-    a.perm = r.perm;
-    a.prob = r.prob;
     a.T = T;
     a.K = dm;
     a.N0 = di;
     a.E = r.E;
-    if (dt == ROM_DTYPE_F32) return launch_f32<false>(a, 2, s);
-    if (T <= kDecodeMaxT) return launch_gemv<false>(a, 2, s);
-    return launch_bf16_auto<false>(a, 2, s);
+    for (int k = 0; k < r.top_k; ++k) {
+        set_choice(a, r, T, k);
+        hipError_t err;
+        if (dt == ROM_DTYPE_F32) err = launch_f32<false>(a, 2, s);
+        else if (T <= kDecodeMaxT) err = launch_gemv<false>(a, 2, s);
+        else err = launch_bf16_auto<false>(a, 2, s);
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_out_proj(const void *z, const void *h, const rom_routing &r, rom_dtype dt, int T, int dm, int di,
@@ -714,24 +760,32 @@ hipError_t launch_out_proj(const void *z, const void *h, const rom_routing &r, r
     a.A1 = h;
     a.B0 = Wo;
     a.C0 = out;
-    a.offsets = r.offsets;
-    a.perm = r.perm;
-    a.prob = r.prob;
     a.T = T;
     a.K = di;
     a.N0 = dm;
     a.E = r.E;
-    if (dt == ROM_DTYPE_F32) return launch_f32<true>(a, 1, s);
-    if (T <= kDecodeMaxT) return launch_gemv<true>(a, 1, s);
-    // gated rows in slot order into the workspace, then the GEMM reads them contiguously
-    hipLaunchKernelGGL(k_gate_permute, dim3((unsigned)((T + 7) / 8)), dim3(256), 0, s,
-                       static_cast<const uint16_t *>(z), static_cast<const uint16_t *>(h), r.perm, T, di,
-                       static_cast<uint16_t *>(workspace));
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    a.A0 = workspace;
-    a.A1 = nullptr;
-    return launch_bf16_auto<true>(a, 1, s);
+    const bool staged = dt == ROM_DTYPE_BF16 && T > kDecodeMaxT;
+    if (staged) {
+        // gated rows into the workspace: in slot order for top-1 (the GEMM then reads them contiguously),
+        // in token order for top-2 (both choices gather from the same rows)
+        hipLaunchKernelGGL(k_gate_permute, dim3((unsigned)((T + 7) / 8)), dim3(256), 0, s,
+                           static_cast<const uint16_t *>(z), static_cast<const uint16_t *>(h),
+                           r.top_k == 1 ? r.perm : nullptr, T, di, static_cast<uint16_t *>(workspace));
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        a.A0 = workspace;
+        a.A1 = nullptr;
+        a.a_by_token = r.top_k > 1;
+    }
+    for (int k = 0; k < r.top_k; ++k) {
+        set_choice(a, r, T, k);
+        hipError_t err;
+        if (dt == ROM_DTYPE_F32) err = launch_f32<true>(a, 1, s);
+        else if (!staged) err = launch_gemv<true>(a, 1, s);
+        else err = launch_bf16_auto<true>(a, 1, s);
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
 }
 
 size_t out_proj_workspace_bytes(int T, int di, rom_dtype dt) {

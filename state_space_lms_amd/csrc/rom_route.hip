@@ -2,8 +2,10 @@
 // by expert (histogram, scan, stable counting-sort scatter, optional permute).
 //
 // Method: Routing Mamba landing page (chapterpal.com), Knowl 1: p_t = Softmax(x_t W_r) over the
-// experts, S_t = the top-1 expert, r_t = p_t,e* (not renormalised). The grouping is not on the page;
-// a dropless grouped GEMM (Knowl 12: no capacity factor, no token dropping) needs it.
+// experts, S_t = the K largest (K = 1 or 2; the page's 8top1, 16top1 and 8top2 settings), r_t,i =
+// p_t,i (not renormalised). The grouping is not on the page; a dropless grouped GEMM (Knowl 12: no
+// capacity factor, no token dropping) needs it. With K = 2 the routing is kept as two stacked top-1
+// routings (choice k of every token, grouped on its own), which the projections run one after the other.
 //
 // Router arithmetic is fp32: logit_t,j = sum_k X[t][k] * W_r[k][j] (+ bias[j]); argmax keeps the
 // lowest index on ties (strict > in ascending j); prob = 1 / sum_j exp(logit_j - logit_max).
@@ -257,24 +259,36 @@ __device__ __forceinline__ int wg_logits(XRows<TX> &xr, const TX *X, int T, int 
     return tok_base;
 }
 
-// Bias, argmax (lowest index on ties), and the top-1 softmax probability.
+// Bias, the K (1 or 2) largest logits (each choice keeps the lowest index on ties), and their softmax
+// probabilities over all E experts (not renormalised over the choice).
 template <int EMAX>
-__device__ __forceinline__ void select_top1(float lg[EMAX], const float *bias, int E, int &best, float &p) {
+__device__ __forceinline__ void select_topk(float lg[EMAX], const float *bias, int E, int K, int (&best)[2],
+                                            float (&p)[2]) {
     if (bias) {
 #pragma unroll
         for (int e = 0; e < EMAX; ++e)
             if (e < E) lg[e] = lg[e] + bias[e];
     }
-    best = 0;
-    float lmax = lg[0];
+    int b0 = 0;
+    float l0 = lg[0];
 #pragma unroll
     for (int e = 1; e < EMAX; ++e)
-        if (e < E && lg[e] > lmax) { lmax = lg[e]; best = e; }
+        if (e < E && lg[e] > l0) { l0 = lg[e]; b0 = e; }
+    int b1 = -1;
+    float l1 = -INFINITY;
+    if (K > 1) {
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e)
+            if (e < E && e != b0 && (b1 < 0 || lg[e] > l1)) { l1 = lg[e]; b1 = e; }
+    }
     float denom = 0.0f;
 #pragma unroll
     for (int e = 0; e < EMAX; ++e)
-        if (e < E) denom += expf(lg[e] - lmax);
-    p = 1.0f / denom;
+        if (e < E) denom += expf(lg[e] - l0);
+    best[0] = b0;
+    best[1] = b1;
+    p[0] = 1.0f / denom;
+    p[1] = K > 1 ? expf(l1 - l0) / denom : 0.0f;
 }
 
 // Stable ranks of one token per thread within the workgroup (256 threads, 4 waves):
@@ -313,15 +327,15 @@ __device__ __forceinline__ void permute_rows(const TX *X, TX *Xp, int dm, int to
 template <typename TX, int EG, int EMAX, int WPG>
 __global__ __launch_bounds__(256) void k_route_logits(const TX *__restrict__ X, int T, int dm,
                                                       const float *__restrict__ Wr, const float *__restrict__ bias,
-                                                      int E, int use_lds, int32_t *__restrict__ ids,
+                                                      int E, int K, int use_lds, int32_t *__restrict__ ids,
                                                       float *__restrict__ prob, int32_t *__restrict__ wg_counts,
                                                       int nwg) {
     constexpr int TPW = 32 / WPG;  // tokens per workgroup
     extern __shared__ float4 wl_dyn[];
-    __shared__ int hist[ROM_MAX_EXPERTS];
+    __shared__ int hist[ROM_MAX_TOP_K * ROM_MAX_EXPERTS];
     __shared__ float s_red[WPG == 4 ? 4 : 1][8][EMAX];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int i = tid; i < E; i += 256) hist[i] = 0;
+    for (int i = tid; i < K * E; i += 256) hist[i] = 0;
     XRows<TX> xr;
     {
         int g0, jl;
@@ -335,15 +349,20 @@ __global__ __launch_bounds__(256) void k_route_logits(const TX *__restrict__ X, 
                                                   lg, s_red);
     const int t = tok0 + lane;
     if (lane < 8 && (WPG == 1 || wave == 0) && t < T) {
-        int best;
-        float p;
-        select_top1<EMAX>(lg, bias, E, best, p);
-        ids[t] = best;
-        prob[t] = p;
-        atomicAdd(&hist[best], 1);
+        int best[2];
+        float p[2];
+        select_topk<EMAX>(lg, bias, E, K, best, p);
+#pragma unroll
+        for (int k = 0; k < ROM_MAX_TOP_K; ++k) {
+            if (k < K) {
+                ids[(size_t)k * T + t] = best[k];
+                prob[(size_t)k * T + t] = p[k];
+                atomicAdd(&hist[k * E + best[k]], 1);
+            }
+        }
     }
     __syncthreads();
-    for (int i = tid; i < E; i += 256) wg_counts[(size_t)i * nwg + blockIdx.x] = hist[i];
+    for (int i = tid; i < K * E; i += 256) wg_counts[(size_t)i * nwg + blockIdx.x] = hist[i];
 }
 
 // Multi-workgroup path, kernel 2: per-expert totals and bases, then the stable scatter of 256 tokens
@@ -359,6 +378,13 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t *__restrict
     __shared__ int s_pos[kScatterTokensPerWG];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wg = blockIdx.x;
+    // choice k = blockIdx.y: the k-th stacked top-1 routing
+    ids += (size_t)blockIdx.y * T;
+    wg_counts += (size_t)blockIdx.y * E * nwg;
+    counts += blockIdx.y * E;
+    offsets += blockIdx.y * (E + 1);
+    perm += (size_t)blockIdx.y * T;
+    inv_perm += (size_t)blockIdx.y * T;
     const int first = wg * sub;  // logits workgroups before this one contribute to the base
     for (int e = wave; e < E; e += 4) {
         int before = 0, total = 0;
@@ -408,12 +434,12 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t *__restrict
 template <typename TX, int EG, int EMAX>
 __global__ __launch_bounds__(256) void k_route_small(const TX *__restrict__ X, int T, int dm,
                                                      const float *__restrict__ Wr, const float *__restrict__ bias,
-                                                     int E, int use_lds, int32_t *__restrict__ ids,
+                                                     int E, int K, int use_lds, int32_t *__restrict__ ids,
                                                      float *__restrict__ prob, int32_t *__restrict__ counts,
                                                      int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
                                                      int32_t *__restrict__ inv_perm, TX *__restrict__ Xp) {
     extern __shared__ float4 wl_dyn[];
-    __shared__ int s_ids[kRouteSmallT];
+    __shared__ int s_ids[ROM_MAX_TOP_K * kRouteSmallT];
     __shared__ int s_base[ROM_MAX_EXPERTS];
     __shared__ int s_wcnt[4][ROM_MAX_EXPERTS];
     __shared__ int s_pos[kRouteSmallT];
@@ -430,44 +456,52 @@ __global__ __launch_bounds__(256) void k_route_small(const TX *__restrict__ X, i
     float lg[EMAX];
     wg_logits<TX, EG, EMAX, 4>(xr, X, T, dm, Wr, use_lds ? wl_dyn : nullptr, E, 0, lg, s_red);
     if (wave == 0 && lane < T) {
-        int best;
-        float p;
-        select_top1<EMAX>(lg, bias, E, best, p);
-        ids[lane] = best;
-        prob[lane] = p;
-        s_ids[lane] = best;
-    }
-    __syncthreads();
-    if (tid < E) {
-        int c = 0;
-        for (int t = 0; t < T; ++t) c += (s_ids[t] == tid);
-        s_wcnt[0][tid] = c;  // borrowed as the histogram until the scan below
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int e = 0; e < E; ++e) {
-            const int c = s_wcnt[0][e];
-            s_base[e] = run;
-            counts[e] = c;
-            offsets[e] = run;
-            run += c;
+        int best[2];
+        float p[2];
+        select_topk<EMAX>(lg, bias, E, K, best, p);
+#pragma unroll
+        for (int k = 0; k < ROM_MAX_TOP_K; ++k) {
+            if (k < K) {
+                ids[k * T + lane] = best[k];
+                prob[k * T + lane] = p[k];
+                s_ids[k * kRouteSmallT + lane] = best[k];
+            }
         }
-        offsets[E] = run;
     }
     __syncthreads();
-    const int e = tid < T ? s_ids[tid] : -1;
-    const int rank = wg_stable_rank(e, E, s_wcnt);
-    int pos = -1;
-    if (e >= 0) {
-        pos = s_base[e] + rank;
-        perm[pos] = tid;
-        inv_perm[tid] = pos;
-    }
-    if (Xp) {
-        if (tid < kRouteSmallT) s_pos[tid] = pos;
+    for (int k = 0; k < K; ++k) {  // the K stacked top-1 routings, one after the other
+        if (tid < E) {
+            int c = 0;
+            for (int t = 0; t < T; ++t) c += (s_ids[k * kRouteSmallT + t] == tid);
+            s_wcnt[0][tid] = c;  // borrowed as the histogram until the scan below
+        }
         __syncthreads();
-        permute_rows<TX>(X, Xp, dm, 0, T, s_pos);
+        if (tid == 0) {
+            int run = 0;
+            for (int e = 0; e < E; ++e) {
+                const int c = s_wcnt[0][e];
+                s_base[e] = run;
+                counts[k * E + e] = c;
+                offsets[k * (E + 1) + e] = run;
+                run += c;
+            }
+            offsets[k * (E + 1) + E] = run;
+        }
+        __syncthreads();
+        const int e = tid < T ? s_ids[k * kRouteSmallT + tid] : -1;
+        const int rank = wg_stable_rank(e, E, s_wcnt);
+        int pos = -1;
+        if (e >= 0) {
+            pos = s_base[e] + rank;
+            perm[k * T + pos] = tid;
+            inv_perm[k * T + tid] = pos;
+        }
+        if (Xp) {  // top-1 only
+            if (tid < kRouteSmallT) s_pos[tid] = pos;
+            __syncthreads();
+            permute_rows<TX>(X, Xp, dm, 0, T, s_pos);
+        }
+        __syncthreads();
     }
 }
 
@@ -491,8 +525,8 @@ static hipError_t launch_route_t(const TX *X, int T, int dm, const float *Wr, co
         attr_set = true;
     }
     if (T <= kRouteSmallT) {
-        hipLaunchKernelGGL((k_route_small<TX, EG, EMAX>), dim3(1), dim3(256), smem, s, X, T, dm, Wr, bias, E, use_lds,
-                           r.expert_id, r.prob, r.counts, r.offsets, r.perm, r.inv_perm, Xp);
+        hipLaunchKernelGGL((k_route_small<TX, EG, EMAX>), dim3(1), dim3(256), smem, s, X, T, dm, Wr, bias, E, r.top_k,
+                           use_lds, r.expert_id, r.prob, r.counts, r.offsets, r.perm, r.inv_perm, Xp);
         return hipGetLastError();
     }
     // enough 32-token workgroups to fill the chip: one wave per 8 tokens; otherwise 8 tokens per
@@ -502,14 +536,14 @@ static hipError_t launch_route_t(const TX *X, int T, int dm, const float *Wr, co
     const int nwg = (T + tpw - 1) / tpw;
     if (wide)
         hipLaunchKernelGGL((k_route_logits<TX, EG, EMAX, 1>), dim3(nwg), dim3(256), smem, s, X, T, dm, Wr, bias, E,
-                           use_lds, r.expert_id, r.prob, wg_counts, nwg);
+                           r.top_k, use_lds, r.expert_id, r.prob, wg_counts, nwg);
     else
         hipLaunchKernelGGL((k_route_logits<TX, EG, EMAX, 4>), dim3(nwg), dim3(256), smem, s, X, T, dm, Wr, bias, E,
-                           use_lds, r.expert_id, r.prob, wg_counts, nwg);
+                           r.top_k, use_lds, r.expert_id, r.prob, wg_counts, nwg);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int nsc = (T + kScatterTokensPerWG - 1) / kScatterTokensPerWG;
-    hipLaunchKernelGGL((k_route_scatter<TX>), dim3(nsc), dim3(256), 0, s, r.expert_id, T, E, wg_counts, nwg,
+    hipLaunchKernelGGL((k_route_scatter<TX>), dim3(nsc, r.top_k), dim3(256), 0, s, r.expert_id, T, E, wg_counts, nwg,
                        kScatterTokensPerWG / tpw, r.counts, r.offsets, r.perm, r.inv_perm, X, Xp, dm);
     return hipGetLastError();
 }

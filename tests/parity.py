@@ -90,6 +90,49 @@ def check_route(gpu, orc_route, orc_sort, T, E, tol) -> RouteReport:
     return RouteReport(int(excl.sum()), int((~agree).sum()), bool(np.all(agree)), perr)
 
 
+def check_route_topk(gpu, orc_route, T, E, K, tol):
+    """Top-K routing (K stacked top-1 routings on the GPU side, arrays [K][T]) against the oracle's
+    ids/prob [T][K]. Returns the boolean mask of tokens whose expert set agrees with the oracle's.
+
+    Sets must agree on every token whose oracle margin between the K-th and (K+1)-th logit is at least
+    GAP_EXCLUDE; the order of the choices must agree where the oracle's margin between consecutive
+    chosen logits is at least GAP_EXCLUDE too (computed from the oracle's own logits). Probabilities are
+    compared expert by expert. Each choice's grouping must be the valid stable grouping of the GPU's own
+    choice-k ids (numpy bincount / stable argsort)."""
+    ids_g, prob_g = gpu["expert_id"], gpu["prob"]
+    assert ids_g.shape == (K, T) and prob_g.shape == (K, T)
+    assert np.all((ids_g >= 0) & (ids_g < E)), "expert id out of range"
+    ids_o, prob_o = orc_route["ids"], orc_route["prob"]
+    if K > 1:
+        assert np.all(ids_g[0] != ids_g[1]), "a token chose the same expert twice"
+    decided = orc_route["gap"] >= GAP_EXCLUDE
+    same_set = np.all(np.sort(ids_g.T, axis=1) == np.sort(ids_o, axis=1), axis=1)
+    bad = ~same_set & decided
+    assert not np.any(bad), f"{int(bad.sum())} expert sets differ on decided tokens, first at {np.flatnonzero(bad)[:5]}"
+    lg = orc_route["logits"]
+    if lg is not None:
+        chosen = np.take_along_axis(lg, ids_o.astype(np.int64), axis=1)  # [T][K], descending
+        ordered = np.all(np.diff(-chosen, axis=1) >= GAP_EXCLUDE, axis=1) if K > 1 else np.ones(T, bool)
+        mis = same_set & ordered & np.any(ids_g.T != ids_o, axis=1)
+        assert not np.any(mis), f"{int(mis.sum())} tokens have their choices in another order"
+    # probabilities paired by expert on the agreeing tokens
+    rows = np.flatnonzero(same_set)
+    if rows.size:
+        order_g = np.argsort(ids_g.T[rows], axis=1)
+        order_o = np.argsort(ids_o[rows], axis=1)
+        pg = np.take_along_axis(prob_g.T[rows], order_g, axis=1)
+        po = np.take_along_axis(prob_o[rows], order_o, axis=1)
+        perr = norm_max_err(pg, po)
+        assert perr <= tol, f"router probability error {perr:.3g} > {tol}"
+    for k in range(K):
+        cnt = np.bincount(ids_g[k], minlength=E)
+        np.testing.assert_array_equal(gpu["counts"][k], cnt, err_msg=f"counts of choice {k}")
+        np.testing.assert_array_equal(gpu["offsets"][k], np.concatenate([[0], np.cumsum(cnt)]))
+        np.testing.assert_array_equal(gpu["perm"][k], np.argsort(ids_g[k], kind="stable"))
+        np.testing.assert_array_equal(gpu["inv_perm"][k][gpu["perm"][k]], np.arange(T))
+    return same_set
+
+
 def sample_rows(orc_sort, T, n_random=192, bm=(64, 128, 256), seed=0) -> np.ndarray:
     """Tokens to check at full size: the first and last slots of every expert group, slots around
     M-tile boundaries inside each group, and a seeded random sample."""

@@ -49,13 +49,14 @@ def test_workspace_bytes(L):
     assert L.rom_route_workspace_bytes(0, 8) == 0
     for T, E in [(1, 8), (257, 8), (16384, 8), (65536, 64)]:
         b = L.rom_route_workspace_bytes(T, E)
-        assert b >= E * ((T + 255) // 256) * 4 and b % 256 == 0
+        # a [top_k][E][workgroups] histogram for up to two choices, 8 tokens per workgroup at the least
+        assert b >= 2 * E * ((T + 7) // 8) * 4 and b % 256 == 0
 
 
-def _routing(T=512, E=8, **over):
+def _routing(T=512, E=8, top_k=1, **over):
     f = dict(expert_id=A, prob=A, counts=A, offsets=A, perm=A, inv_perm=A)
     f.update(over)
-    return rom.RoutingStruct(T, E, 1, 0, f["expert_id"], f["prob"], f["counts"], f["offsets"], f["perm"],
+    return rom.RoutingStruct(T, E, top_k, 0, f["expert_id"], f["prob"], f["counts"], f["offsets"], f["perm"],
                              f["inv_perm"])
 
 
@@ -66,7 +67,8 @@ def _route(L, X=A, dt=BF16, T=512, dm=128, Wr=A, bias=None, E=8, k=1, r="default
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(T=-1), INVALID), (dict(E=0), INVALID), (dict(E=65), UNSUPPORTED), (dict(k=2), UNSUPPORTED),
+    (dict(T=-1), INVALID), (dict(E=0), INVALID), (dict(E=65), UNSUPPORTED), (dict(k=3), UNSUPPORTED),
+    (dict(k=2, E=1), INVALID), (dict(k=2, Xp=A + (1 << 24)), UNSUPPORTED),  # the permute is top-1 only
     (dict(k=0), INVALID), (dict(k=9), INVALID), (dict(dm=0), INVALID), (dict(dm=96), UNSUPPORTED),
     (dict(dt=7), INVALID), (dict(X=None), INVALID), (dict(X=A + 8), INVALID), (dict(Wr=None), INVALID),
     (dict(r=None), INVALID), (dict(bias=A + 2), INVALID), (dict(ws=None), WS_SMALL), (dict(wsb=16), WS_SMALL),
@@ -101,6 +103,7 @@ def _in(L, X=A, T=512, dm=128, di=256, Wc=A, Wg=A, xo=A + (1 << 24), zo=A + (1 <
     (dict(Wc=A + 2), INVALID), (dict(zo=None), INVALID), (dict(zo=A + (1 << 24) + 64), INVALID),
     (dict(xo=A + 256), INVALID), (dict(r=_routing(256, 8)), INVALID), (dict(r=_routing(512, 0)), INVALID),
     (dict(r=_routing(512, 8, offsets=None)), INVALID), (dict(dt=3), INVALID),
+    (dict(r=_routing(512, 8, top_k=3)), UNSUPPORTED), (dict(r=_routing(512, 2, top_k=3)), INVALID),
 ])
 def test_in_proj_rejects(L, kw, code):
     assert _in(L, **kw) == code

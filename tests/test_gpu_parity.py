@@ -23,12 +23,12 @@ def rom():
     return rom_mod
 
 
-def _run_chain(rom, w, inp, permute=False, isolated=True):
+def _run_chain(rom, w, inp, permute=False, isolated=True, top_k=1):
     import torch
     d = lambda k: parity.to_device(inp[k], w.dtype) if k != "W_router" else parity.to_device(inp[k], "f32")
     X, Wr, Wc, Wg, Wo, h = d("X"), d("W_router"), d("W_conv"), d("W_gate"), d("W_out"), d("h")
     bias = parity.to_device(inp["bias"], "f32") if inp.get("bias") is not None else None
-    r = rom.route(X, Wr, bias, permute=permute)
+    r = rom.route(X, Wr, bias, top_k=top_k, permute=permute)
     x, z = rom.in_proj(X, r, Wc, Wg)
     out = rom.out_proj(z, h, r, Wo)
     out_iso = None
@@ -38,8 +38,12 @@ def _run_chain(rom, w, inp, permute=False, isolated=True):
     return dict(r=r, X=X, x=x, z=z, out=out, out_iso=out_iso)
 
 
-def _route_host(r):
-    return {k: parity.to_host(getattr(r, k)) for k in ("expert_id", "prob", "counts", "offsets", "perm", "inv_perm")}
+def _route_host(r, squeeze=True):
+    """Routing buffers on the host; for top-1 (squeeze) the [1][...] arrays become flat."""
+    out = {k: parity.to_host(getattr(r, k)) for k in ("expert_id", "prob", "counts", "offsets", "perm", "inv_perm")}
+    if squeeze and r.top_k == 1:
+        out = {k: v[0] for k, v in out.items()}
+    return out
 
 
 def _rows(t, rows):
@@ -151,6 +155,10 @@ def test_tied_logits_lowest_index_and_exact_prob(rom, oracle):
     gr = _route_host(g["r"])
     assert np.all(gr["expert_id"] == 0) and np.all(gr["prob"] == np.float32(0.125))
     np.testing.assert_array_equal(gr["perm"], np.arange(w.T))
+    g2 = _run_chain(rom, w, inp, isolated=False, top_k=2)
+    gr2 = _route_host(g2["r"])
+    assert np.all(gr2["expert_id"][0] == 0) and np.all(gr2["expert_id"][1] == 1)
+    assert np.all(gr2["prob"] == np.float32(0.125))
 
 
 def test_deterministic_and_permute(rom, oracle):
@@ -163,11 +171,15 @@ def test_deterministic_and_permute(rom, oracle):
         np.testing.assert_array_equal(parity.to_host(a[k]), parity.to_host(b[k]))
     for k in ("expert_id", "prob", "perm", "inv_perm"):
         np.testing.assert_array_equal(parity.to_host(getattr(a["r"], k)), parity.to_host(getattr(b["r"], k)))
-    perm = parity.to_host(a["r"].perm)
+    a2 = _run_chain(rom, w, inp, isolated=False, top_k=2)
+    b2 = _run_chain(rom, w, inp, isolated=False, top_k=2)
+    for k in ("x", "z", "out"):
+        np.testing.assert_array_equal(parity.to_host(a2[k]), parity.to_host(b2[k]))
+    perm = parity.to_host(a["r"].perm)[0]
     np.testing.assert_array_equal(parity.to_host(a["r"].x_perm), inp["X"][perm])
     o_route = oracle.route(inp["X"], inp["W_router"])
     o_sort = oracle.sort(o_route["ids"], w.E)
-    if np.array_equal(parity.to_host(a["r"].expert_id), o_route["ids"][:, 0]):
+    if np.array_equal(parity.to_host(a["r"].expert_id)[0], o_route["ids"][:, 0]):
         np.testing.assert_array_equal(parity.to_host(a["r"].x_perm), oracle.permute(inp["X"], o_sort["perm"]))
 
 
@@ -201,3 +213,69 @@ def test_full_workload(rom, oracle, name):
     if w.skew is not None:
         frac = gr["counts"] / w.T
         assert np.max(np.abs(frac - np.array(w.skew))) <= 0.0025, f"skewed loads {frac}"
+
+
+# ------------------------------------------------------------------------------------------------
+# top-2 routing (the page's 8top2 setting): two stacked top-1 routings, choices added in order
+
+def check_workload_top2(rom, orc, w, inp=None, rows=None, label=""):
+    K = 2
+    inp = inp if inp is not None else workloads.make_inputs(w)
+    tol = parity.TOL[w.dtype]
+    print(f"[parity top2] {label or w.name}: T={w.T} d_model={w.d_model} d_inner={w.d_inner} E={w.E} {w.dtype}",
+          flush=True)
+    g = _run_chain(rom, w, inp, top_k=K)
+    gr = _route_host(g["r"], squeeze=False)
+    o_route = orc.route(inp["X"], inp["W_router"], inp.get("bias"), top_k=K, want_logits=True)
+    agree = parity.check_route_topk(gr, o_route, w.T, w.E, K, tol)
+    rows = np.arange(w.T) if rows is None else rows
+    rows = rows[agree[rows]]
+    ids_o, prob_o = o_route["ids"][rows], o_route["prob"][rows]
+    x_o, z_o = orc.in_proj(inp["X"][rows], ids_o, inp["W_conv"], inp["W_gate"])
+    ex = parity.norm_max_err(_rows(g["x"], rows), x_o)
+    ez = parity.norm_max_err(_rows(g["z"], rows), z_o)
+    out_o = orc.out_proj(z_o, inp["h"][rows], ids_o, prob_o, inp["W_out"])
+    eo = parity.norm_max_err(_rows(g["out"], rows), out_o)
+    ei = 0.0
+    if g["out_iso"] is not None:
+        out_i = orc.out_proj(inp["z"][rows].astype(np.float64), inp["h"][rows], ids_o, prob_o, inp["W_out"])
+        ei = parity.norm_max_err(_rows(g["out_iso"], rows), out_i)
+    print(f"[parity top2]   set-mismatch={int((~agree).sum())} x={ex:.2e} z={ez:.2e} out={eo:.2e} "
+          f"out_isolated={ei:.2e} rows={len(rows)}", flush=True)
+    for name, err in (("x", ex), ("z", ez), ("out", eo), ("out_isolated", ei)):
+        assert err <= tol, f"{name}: normalised max error {err:.3g} > {tol}"
+    return g, gr, o_route
+
+
+TOP2 = [
+    workloads.custom_workload("top2_f32", T=300, d_model=64, d_inner=128, E=8, dtype="f32", seed=201),
+    workloads.custom_workload("top2_bf16_tiles", T=1000, d_model=256, d_inner=384, E=8, seed=202),
+    workloads.custom_workload("top2_bf16_E2", T=513, d_model=128, d_inner=256, E=2, seed=203),
+    workloads.custom_workload("top2_bf16_E16", T=2000, d_model=320, d_inner=192, E=16, seed=204),
+    workloads.custom_workload("top2_T5_fused_route", T=5, d_model=512, d_inner=128, E=8, seed=205),
+    workloads.custom_workload("top2_T40_decode", T=40, d_model=256, d_inner=320, E=4, seed=206),
+    workloads.custom_workload("top2_T64_decode", T=64, d_model=512, d_inner=256, E=8, seed=207),
+    workloads.custom_workload("top2_wide_route", T=16400, d_model=128, d_inner=128, E=8, seed=208),
+]
+
+
+@pytest.mark.parametrize("w", TOP2, ids=[w.name for w in TOP2])
+def test_top2_small_shapes(rom, oracle, w):
+    check_workload_top2(rom, oracle, w)
+
+
+def test_top2_hot_expert(rom, oracle):
+    """A dominant bias: every token's first choice is expert 3, the second spreads over the others."""
+    w = workloads.custom_workload("top2_hot", T=700, d_model=128, d_inner=128, E=8, seed=209)
+    bias = np.zeros(8, np.float32)
+    bias[3] = 1e3
+    _, gr, _ = check_workload_top2(rom, oracle, w, workloads.make_inputs(w, router_bias=bias), label="hot expert 3")
+    assert np.all(gr["expert_id"][0] == 3) and np.all(gr["expert_id"][1] != 3)
+
+
+def test_top2_full_samba_shape(rom, oracle):
+    w = workloads.get_workload("samba421m")
+    inp = workloads.make_inputs(w, which={"X", "W_router", "W_conv", "W_gate", "W_out", "h"})
+    o_route = oracle.route(inp["X"], inp["W_router"], top_k=2)
+    rows = parity.sample_rows(oracle.sort(o_route["ids"][:, :1].copy(), w.E), w.T)
+    check_workload_top2(rom, oracle, w, inp, rows=rows, label="samba421m top-2")

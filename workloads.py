@@ -73,6 +73,9 @@ WORKLOADS = {
     # 1.3B-active-scale block on one 16K-token sequence
     "rom1p3b": Workload("rom1p3b", T=16384, d_model=2048, d_inner=4096, E=8, dtype="bf16", seed=3,
                         x_std=1.0, wr_std=0.02, w_std=0.02, h_std=1.0, z_std=1.0),
+    # the same block with top-2 routing (the page's 8top2 setting); same seed, hence the same tensors
+    "samba421m_top2": Workload("samba421m_top2", T=16384, d_model=1024, d_inner=2048, E=8, dtype="bf16", seed=2,
+                               x_std=1.0, wr_std=None, w_std=0.02, h_std=1.0, z_std=1.0, top_k=2),
     # skewed routing without a balance loss: a router bias gives loads 60/10/10/5/5/5/3/2 %
     "skewed": Workload("skewed", T=65536, d_model=2048, d_inner=4096, E=8, dtype="bf16", seed=4,
                        x_std=1.0, wr_std=0.02, w_std=0.02, h_std=1.0, z_std=1.0,
