@@ -121,7 +121,7 @@ ROM_API rom_status rom_in_proj(const void *X, const rom_routing *routing, rom_dt
                        int32_t d_model, int32_t d_inner, const void *W_conv, const void *W_gate,
                        void *x_out, void *z_out, void *stream);
 
-/* Bytes of device workspace rom_out_proj needs (0 when it needs none: fp32 data, or T <= 64). */
+/* Bytes of device workspace rom_out_proj needs (T * d_inner bf16 values for bf16 data; 0 for fp32 data). */
 ROM_API size_t rom_out_proj_workspace_bytes(int32_t T, int32_t d_inner, rom_dtype dtype);
 
 /*
@@ -131,8 +131,8 @@ ROM_API size_t rom_out_proj_workspace_bytes(int32_t T, int32_t d_inner, rom_dtyp
  * The probability scale is r_t,e of Knowl 1 (stated only in that secondary summary: the authors'
  * own text does not write the formula). For bf16 data, a is rounded to bf16 once before the
  * MFMA product; accumulation is fp32; each choice's contribution is rounded once, added in the order
- * k = 0, 1 as for the in-projection. For bf16 data with T > 64 the gated rows a are first written to
- * the workspace (in slot order for top_k = 1, token order for top_k = 2), which the grouped GEMMs read.
+ * k = 0, 1 as for the in-projection. For bf16 data the gated rows a are first written to the workspace
+ * (in slot order for top_k = 1 and T > 64, otherwise in token order), which the grouped products read.
  *   z, h [T][d_inner]; W_out [E][d_model][d_inner]; out [T][d_model]; all dtype. out may not alias z or h.
  *   workspace  device scratch of at least rom_out_proj_workspace_bytes(T, d_inner, dtype) bytes
  *              (may be NULL when that is 0); contents on entry do not matter and are clobbered.

@@ -374,31 +374,33 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
 // ---------------------------------------------------------------------------------------------
 // Gate and permute for the out-projection (bf16): a[pos][n] = bf16(SiLU(z[t][n]) * h[t][n]) with
 // t = perm[pos], fp32 arithmetic, rows written in slot order so the GEMM reads each expert's rows
-// contiguously; with perm == NULL, t = pos (token order, shared by the two choices of a top-2 routing). Memory-bound: 8 rows per workgroup, 32 lanes per row, 4 chunks of 8 elements in
-// flight per lane (chunk indices past the row end are clamped for the loads and not stored).
+// contiguously; with perm == NULL, t = pos (token order, shared by the two choices of a top-2 routing
+// and by the decode kernels). Memory-bound: a workgroup owns gate_rows_per_wg(d_inner) consecutive
+// output rows (about 1024 16-byte chunks) and its 256 threads stride over their chunks, 4 chunks of z
+// and h in flight per thread, so even a single row is spread over the whole workgroup.
+inline int gate_rows_per_wg(int di) { return di / 8 >= 1024 ? 1 : 1024 / (di / 8); }
+
 __global__ __launch_bounds__(256) void k_gate_permute(const uint16_t *__restrict__ z, const uint16_t *__restrict__ h,
-                                                      const int32_t *__restrict__ perm, int T, int di,
+                                                      const int32_t *__restrict__ perm, int T, int di, int rows_per_wg,
                                                       uint16_t *__restrict__ a) {
-    const int pos = blockIdx.x * 8 + (threadIdx.x >> 5);
-    if (pos >= T) return;
-    const int l = threadIdx.x & 31;
-    const int tok = perm != nullptr ? perm[pos] : pos;
     const int cpr = di >> 3;  // 16-byte chunks per row
-    const uint4 *zr = reinterpret_cast<const uint4 *>(z + (size_t)tok * di);
-    const uint4 *hr = reinterpret_cast<const uint4 *>(h + (size_t)tok * di);
-    uint4 *ar = reinterpret_cast<uint4 *>(a + (size_t)pos * di);
-    for (int c0 = l; c0 < cpr; c0 += 128) {
+    const int r0 = blockIdx.x * rows_per_wg;
+    const int n = min(rows_per_wg, T - r0) * cpr;  // chunk units of this workgroup
+    for (int ub = threadIdx.x; ub < n; ub += 4 * 256) {
         uint4 zv[4], hv[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int c = min(c0 + 32 * u, cpr - 1);
-            zv[u] = zr[c];
-            hv[u] = hr[c];
+        for (int j = 0; j < 4; ++j) {
+            const int u = min(ub + j * 256, n - 1);  // clamped: every load is in bounds
+            const int rr = u / cpr, c = u - rr * cpr;
+            const int pos = r0 + rr;
+            const int tok = perm != nullptr ? perm[pos] : pos;
+            zv[j] = reinterpret_cast<const uint4 *>(z + (size_t)tok * di)[c];
+            hv[j] = reinterpret_cast<const uint4 *>(h + (size_t)tok * di)[c];
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t zw[4] = {zv[u].x, zv[u].y, zv[u].z, zv[u].w};
-            const uint32_t hw[4] = {hv[u].x, hv[u].y, hv[u].z, hv[u].w};
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t zw[4] = {zv[j].x, zv[j].y, zv[j].z, zv[j].w};
+            const uint32_t hw[4] = {hv[j].x, hv[j].y, hv[j].z, hv[j].w};
             uint32_t o[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -406,7 +408,11 @@ __global__ __launch_bounds__(256) void k_gate_permute(const uint16_t *__restrict
                 const float h0 = __uint_as_float(hw[q] << 16), h1 = __uint_as_float(hw[q] & 0xFFFF0000u);
                 o[q] = pack_bf16x2(silu_fast(z0) * h0, silu_fast(z1) * h1);
             }
-            if (c0 + 32 * u < cpr) ar[c0 + 32 * u] = make_uint4(o[0], o[1], o[2], o[3]);
+            if (ub + j * 256 < n) {
+                const int u = ub + j * 256;
+                const int rr = u / cpr, c = u - rr * cpr;
+                reinterpret_cast<uint4 *>(a + (size_t)(r0 + rr) * di)[c] = make_uint4(o[0], o[1], o[2], o[3]);
+            }
         }
     }
 }
@@ -416,8 +422,10 @@ __global__ __launch_bounds__(256) void k_gate_permute(const uint16_t *__restrict
 // work is tiny. A workgroup owns 16 weight rows of one expert and every token routed to it (at most
 // 64, i.e. NB blocks of 16), and its NW waves split K. The weight fragment of a 16x16x32 MFMA comes
 // straight from global memory (lane l: row l%16, 8 elements at k + 8*(l/16)), the token fragments
-// likewise through perm; each wave keeps U K-steps of loads in flight. Partial sums of the waves are
-// added in wave order through LDS (deterministic), then scaled (out-projection) and stored.
+// likewise through perm (for the out-projection, from the gated rows k_gate_permute wrote in token
+// order: the gate is evaluated once per token, not once per workgroup and padding column); each wave
+// keeps U K-steps of loads in flight. Partial sums of the waves are added in wave order through LDS
+// (deterministic), then scaled (out-projection) and stored.
 // Grid: (weight rows / 16) x min(E, T): the second index is the rank among experts that received tokens;
 // each workgroup runs the variant sized for its expert's token-block count.
 template <int NW, int NB, int U, bool OUT>
@@ -442,53 +450,30 @@ __device__ __forceinline__ void gemv_block(const GemmArgs &p, int e, int o0, int
 
     const int r = lane & 15, g = lane >> 4;
     const uint16_t *wp = W + (size_t)r * K + g * 8;
-    const uint16_t *xp[NB], *hp[NB];
+    const uint16_t *xp[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        const size_t off = (size_t)s_tok[b * 16 + r] * K + g * 8;
-        xp[b] = static_cast<const uint16_t *>(p.A0) + off;
-        hp[b] = OUT ? static_cast<const uint16_t *>(p.A1) + off : nullptr;
-    }
+    for (int b = 0; b < NB; ++b) xp[b] = static_cast<const uint16_t *>(p.A0) + (size_t)s_tok[b * 16 + r] * K + g * 8;
     f32x4 acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
+    // U K-steps of loads in flight per wave (indices clamped, so every load is in bounds), then their MFMAs
     const int nsteps = K / 32;
     for (int s0 = wave; s0 < nsteps; s0 += NW * U) {
         bf16x8 wf[U], xf[U][NB];
-        uint4 hf[OUT ? U : 1][NB];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int k0 = min(s0 + u * NW, nsteps - 1) * 32;  // clamped: loads stay in bounds
+            const int k0 = min(s0 + u * NW, nsteps - 1) * 32;
             wf[u] = *reinterpret_cast<const bf16x8 *>(wp + k0);
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                xf[u][b] = *reinterpret_cast<const bf16x8 *>(xp[b] + k0);
-                if (OUT) hf[u][b] = *reinterpret_cast<const uint4 *>(hp[b] + k0);
-            }
+            for (int b = 0; b < NB; ++b) xf[u][b] = *reinterpret_cast<const bf16x8 *>(xp[b] + k0);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (s0 + u * NW < nsteps) {  // uniform
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    bf16x8 a = xf[u][b];
-                    if (OUT) {
-                        // a = bf16(SiLU(z) * h), fp32 arithmetic
-                        const uint4 zv = __builtin_bit_cast(uint4, xf[u][b]);
-                        const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w};
-                        const uint32_t hw[4] = {hf[u][b].x, hf[u][b].y, hf[u][b].z, hf[u][b].w};
-                        uint32_t o[4];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float z0 = __uint_as_float(zw[q] << 16), z1 = __uint_as_float(zw[q] & 0xFFFF0000u);
-                            const float h0 = __uint_as_float(hw[q] << 16), h1 = __uint_as_float(hw[q] & 0xFFFF0000u);
-                            o[q] = pack_bf16x2(silu_fast(z0) * h0, silu_fast(z1) * h1);
-                        }
-                        a = __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
-                    }
-                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], a, acc[b], 0, 0, 0);
-                }
+                for (int b = 0; b < NB; ++b)
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], xf[u][b], acc[b], 0, 0, 0);
             }
         }
     }
@@ -764,24 +749,26 @@ hipError_t launch_out_proj(const void *z, const void *h, const rom_routing &r, r
     a.K = di;
     a.N0 = dm;
     a.E = r.E;
-    const bool staged = dt == ROM_DTYPE_BF16 && T > kDecodeMaxT;
-    if (staged) {
-        // gated rows into the workspace: in slot order for top-1 (the GEMM then reads them contiguously),
-        // in token order for top-2 (both choices gather from the same rows)
-        hipLaunchKernelGGL(k_gate_permute, dim3((unsigned)((T + 7) / 8)), dim3(256), 0, s,
+    if (dt == ROM_DTYPE_BF16) {
+        // gated rows a = bf16(SiLU(z) * h) into the workspace, once per token: in slot order for top-1 at
+        // T > 64 (the GEMM then reads each expert's rows contiguously), otherwise in token order (both
+        // choices of a top-2 routing, and the decode kernels, gather rows from it)
+        const bool slot_order = r.top_k == 1 && T > kDecodeMaxT;
+        const int rpw = gate_rows_per_wg(di);
+        hipLaunchKernelGGL(k_gate_permute, dim3((unsigned)((T + rpw - 1) / rpw)), dim3(256), 0, s,
                            static_cast<const uint16_t *>(z), static_cast<const uint16_t *>(h),
-                           r.top_k == 1 ? r.perm : nullptr, T, di, static_cast<uint16_t *>(workspace));
+                           slot_order ? r.perm : nullptr, T, di, rpw, static_cast<uint16_t *>(workspace));
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
         a.A0 = workspace;
         a.A1 = nullptr;
-        a.a_by_token = r.top_k > 1;
+        a.a_by_token = !slot_order;
     }
     for (int k = 0; k < r.top_k; ++k) {
         set_choice(a, r, T, k);
         hipError_t err;
         if (dt == ROM_DTYPE_F32) err = launch_f32<true>(a, 1, s);
-        else if (!staged) err = launch_gemv<true>(a, 1, s);
+        else if (T <= kDecodeMaxT) err = launch_gemv<true>(a, 1, s);
         else err = launch_bf16_auto<true>(a, 1, s);
         if (err != hipSuccess) return err;
     }
@@ -789,7 +776,7 @@ hipError_t launch_out_proj(const void *z, const void *h, const rom_routing &r, r
 }
 
 size_t out_proj_workspace_bytes(int T, int di, rom_dtype dt) {
-    if (dt != ROM_DTYPE_BF16 || T <= kDecodeMaxT) return 0;
+    if (dt != ROM_DTYPE_BF16) return 0;
     return (size_t)T * di * sizeof(uint16_t);
 }
 

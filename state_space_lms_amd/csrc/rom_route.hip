@@ -511,7 +511,11 @@ template <typename TX, int EG, int EMAX>
 static hipError_t launch_route_t(const TX *X, int T, int dm, const float *Wr, const float *bias, int E,
                                  const rom_routing &r, TX *Xp, int32_t *wg_counts, hipStream_t s) {
     const size_t wbytes = (size_t)dm * E * sizeof(float);
-    const int use_lds = (E % 4 == 0) && (((E >> 2) & ((E >> 2) - 1)) == 0) && wbytes <= (size_t)kRouteLdsW;
+    // enough 32-token workgroups to fill the chip: one wave per 8 tokens; otherwise 8 tokens per
+    // workgroup with the waves splitting d_model. W_r is staged in LDS only on the wide path: with 8
+    // tokens per workgroup each W_r value serves too few tokens to repay the staging round trip.
+    const bool wide = (T + 31) / 32 >= 512;
+    const int use_lds = wide && (E % 4 == 0) && (((E >> 2) & ((E >> 2) - 1)) == 0) && wbytes <= (size_t)kRouteLdsW;
     const size_t smem = use_lds ? wbytes : 0;
     static bool attr_set = false;
     if (!attr_set) {
@@ -529,9 +533,6 @@ static hipError_t launch_route_t(const TX *X, int T, int dm, const float *Wr, co
                            use_lds, r.expert_id, r.prob, r.counts, r.offsets, r.perm, r.inv_perm, Xp);
         return hipGetLastError();
     }
-    // enough 32-token workgroups to fill the chip: one wave per 8 tokens; otherwise 8 tokens per
-    // workgroup with the waves splitting d_model
-    const bool wide = (T + 31) / 32 >= 512;
     const int tpw = wide ? 32 : 8;
     const int nwg = (T + tpw - 1) / tpw;
     if (wide)

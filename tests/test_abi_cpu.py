@@ -133,7 +133,7 @@ def test_out_proj_rejects(L, kw, code):
 
 def test_out_proj_workspace_bytes(L):
     assert L.rom_out_proj_workspace_bytes(0, 2048, BF16) == 0
-    assert L.rom_out_proj_workspace_bytes(64, 2048, BF16) == 0          # decode path needs none
+    assert L.rom_out_proj_workspace_bytes(64, 2048, BF16) == 64 * 2048 * 2  # gated rows, decode too
     assert L.rom_out_proj_workspace_bytes(1000, 2048, rom.ROM_DTYPE_F32) == 0
     assert L.rom_out_proj_workspace_bytes(16384, 2048, BF16) == 16384 * 2048 * 2
 
