@@ -21,6 +21,8 @@
 // Decode path (T <= 64): weight-streaming kernels (k_grouped_gemv_bf16). fp32 data: k_grouped_gemm_f32.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "rom_device.h"
 #include "rom_internal.h"
 
@@ -377,12 +379,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
 // contiguously; with perm == NULL, t = pos (token order, shared by the two choices of a top-2 routing
 // and by the decode kernels). Memory-bound: a workgroup owns gate_rows_per_wg(d_inner) consecutive
 // output rows (about 1024 16-byte chunks) and its 256 threads stride over their chunks, 4 chunks of z
-// and h in flight per thread, so even a single row is spread over the whole workgroup.
+// and h in flight per thread, so even a single row is spread over the whole workgroup. The row of
+// chunk unit u is u / cpr, computed as umulhi(u, cpr_magic) with cpr_magic = floor(2^32 / cpr) + 1,
+// exact for every u below rows_per_wg * cpr and cpr < 2^16 (an integer division would cost more than
+// the memory traffic).
 inline int gate_rows_per_wg(int di) { return di / 8 >= 1024 ? 1 : 1024 / (di / 8); }
+inline uint32_t gate_cpr_magic(int di) { return (uint32_t)((1ull << 32) / (uint64_t)(di / 8) + 1); }
 
 __global__ __launch_bounds__(256) void k_gate_permute(const uint16_t *__restrict__ z, const uint16_t *__restrict__ h,
                                                       const int32_t *__restrict__ perm, int T, int di, int rows_per_wg,
-                                                      uint16_t *__restrict__ a) {
+                                                      uint32_t cpr_magic, uint16_t *__restrict__ a) {
     const int cpr = di >> 3;  // 16-byte chunks per row
     const int r0 = blockIdx.x * rows_per_wg;
     const int n = min(rows_per_wg, T - r0) * cpr;  // chunk units of this workgroup
@@ -391,7 +397,7 @@ __global__ __launch_bounds__(256) void k_gate_permute(const uint16_t *__restrict
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int u = min(ub + j * 256, n - 1);  // clamped: every load is in bounds
-            const int rr = u / cpr, c = u - rr * cpr;
+            const int rr = (int)__umulhi((uint32_t)u, cpr_magic), c = u - rr * cpr;
             const int pos = r0 + rr;
             const int tok = perm != nullptr ? perm[pos] : pos;
             zv[j] = reinterpret_cast<const uint4 *>(z + (size_t)tok * di)[c];
@@ -410,7 +416,7 @@ __global__ __launch_bounds__(256) void k_gate_permute(const uint16_t *__restrict
             }
             if (ub + j * 256 < n) {
                 const int u = ub + j * 256;
-                const int rr = u / cpr, c = u - rr * cpr;
+                const int rr = (int)__umulhi((uint32_t)u, cpr_magic), c = u - rr * cpr;
                 reinterpret_cast<uint4 *>(a + (size_t)(r0 + rr) * di)[c] = make_uint4(o[0], o[1], o[2], o[3]);
             }
         }
@@ -757,7 +763,8 @@ hipError_t launch_out_proj(const void *z, const void *h, const rom_routing &r, r
         const int rpw = gate_rows_per_wg(di);
         hipLaunchKernelGGL(k_gate_permute, dim3((unsigned)((T + rpw - 1) / rpw)), dim3(256), 0, s,
                            static_cast<const uint16_t *>(z), static_cast<const uint16_t *>(h),
-                           slot_order ? r.perm : nullptr, T, di, rpw, static_cast<uint16_t *>(workspace));
+                           slot_order ? r.perm : nullptr, T, di, rpw, gate_cpr_magic(di),
+                           static_cast<uint16_t *>(workspace));
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
         a.A0 = workspace;
