@@ -21,8 +21,6 @@
 // Decode path (T <= 64): weight-streaming kernels (k_grouped_gemv_bf16). fp32 data: k_grouped_gemm_f32.
 #include <stdlib.h>
 
-#include <type_traits>
-
 #include "rom_device.h"
 #include "rom_internal.h"
 
