@@ -62,6 +62,8 @@ class Oracle:
         lib.orom_in_proj.restype = None
         lib.orom_out_proj.argtypes = [_f64p, _f32p, _i64, _i64, _i64, _i32p, _f32p, _i32, _f32p, _i32, _f64p]
         lib.orom_out_proj.restype = None
+        lib.orom_in_proj_weighted.argtypes = [_f32p, _i64, _i64, _i64, _i32p, _f32p, _i32, _f32p, _i32, _f64p]
+        lib.orom_in_proj_weighted.restype = None
         self.lib = lib
 
     def threads(self) -> int:
@@ -139,6 +141,21 @@ class Oracle:
         out = np.empty((n, dm), np.float64)
         self.lib.orom_out_proj(z, h, n, di, dm, ids, prob, ids.shape[1], Wo, E, out)
         return out
+
+    def in_proj_weighted(self, X, ids, prob, W_in):
+        """Swimba's routing-weighted in-projection: y [n][d_out] in float64,
+        y[t] = sum_s prob[t][s] * W_in[ids[t][s]] X[t]."""
+        X = np.ascontiguousarray(X, dtype=np.float32)
+        n, dm = X.shape
+        ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(n, -1)
+        prob = np.ascontiguousarray(prob, dtype=np.float32).reshape(n, -1)
+        W = np.ascontiguousarray(W_in, dtype=np.float32)
+        E, dout, dm2 = W.shape
+        assert dm2 == dm and prob.shape == ids.shape
+        assert ids.size == 0 or (ids.min() >= 0 and ids.max() < E)
+        y = np.empty((n, dout), np.float64)
+        self.lib.orom_in_proj_weighted(X, n, dm, dout, ids, prob, ids.shape[1], W, E, y)
+        return y
 
     # -- the whole routed path for a subset of tokens --------------------------------------------
     def forward_rows(self, inp: dict, rows: Optional[np.ndarray] = None, top_k: int = 1, routed=None):

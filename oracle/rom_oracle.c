@@ -227,3 +227,37 @@ void orom_out_proj(const double *z, const float *h, int64_t n, int64_t di, int64
         free(a);
     }
 }
+
+/* ---------------------------------------------------------------------------
+ * Routing-weighted in-projection of Switch Mamba (Swimba project page,
+ * extended abstract): the in-projection is a set of expert projections behind a
+ * token-level softmax router, and the experts' streams, each weighted by its
+ * routing weight, are summed into the one input of the SSM kernel. The routing
+ * weight is read as Knowl 1's r_t,i of the RoM page, i.e. the softmax
+ * probability of a selected expert, not renormalised over the selection.
+ *
+ * X [n][dm]; ids, prob [n][K]; W [E][dout][dm] (row c of expert i is column c
+ * of that expert's in-projection). Output y [n][dout] in double:
+ *   y[t][c] = sum_{s<K} prob[t][s] * sum_k X[t][k] * W[ids[t][s]][c][k]
+ */
+void orom_in_proj_weighted(const float *X, int64_t n, int64_t dm, int64_t dout, const int32_t *ids,
+                           const float *prob, int32_t K, const float *W, int32_t E, double *y)
+{
+    (void)E;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        const float *x = X + t * dm;
+        for (int64_t c = 0; c < dout; ++c) {
+            double yc = 0.0;
+            for (int32_t s = 0; s < K; ++s) {
+                const int64_t i = ids[t * K + s];
+                const float *w = W + (i * dout + c) * dm;
+                double stream = 0.0;
+                for (int64_t k = 0; k < dm; ++k)
+                    stream += (double)x[k] * (double)w[k];
+                yc += (double)prob[t * K + s] * stream;
+            }
+            y[t * dout + c] = yc;
+        }
+    }
+}

@@ -249,6 +249,46 @@ def pin_out_proj(orc):
     assert np.all(s_pos[z > 0] > 0) and np.all(s_pos[z < 0] < 0)
 
 
+def pin_in_proj_weighted(orc):
+    """Swimba's routing-weighted in-projection (Swimba project page, extended abstract)."""
+    rng = np.random.default_rng(16)
+    for (T, dm, do, E, K) in [(30, 24, 40, 4, 1), (20, 40, 24, 8, 1), (16, 8, 12, 5, 2)]:
+        X, W, _, _, _, ids, prob = _proj_case(rng, T, dm, do, E, K)
+        y = orc.in_proj_weighted(X, ids, prob, W)
+        # per-token float64 brute force: the selected experts' streams, each times its weight
+        yb = np.zeros((T, do))
+        for t in range(T):
+            for s in range(K):
+                yb[t] += float(prob[t, s]) * (W[ids[t, s]].astype(np.float64) @ X[t].astype(np.float64))
+        np.testing.assert_allclose(y, yb, rtol=1e-12, atol=1e-12)
+    # E = 1 with p = 1: a dense projection X @ W^T (BLAS)
+    X, W, _, _, _, _, _ = _proj_case(rng, 33, 20, 28, 1, 1)
+    y = orc.in_proj_weighted(X, np.zeros((33, 1), np.int32), np.ones((33, 1), np.float32), W)
+    np.testing.assert_allclose(y, X.astype(np.float64) @ W[0].astype(np.float64).T, rtol=1e-12, atol=1e-12)
+    # linear in the weight: halving p halves the output exactly
+    X, W, _, _, _, ids, prob = _proj_case(rng, 15, 10, 14, 4, 1)
+    y1 = orc.in_proj_weighted(X, ids, prob, W)
+    y2 = orc.in_proj_weighted(X, ids, (prob * np.float32(0.5)).astype(np.float32), W)
+    np.testing.assert_array_equal(y2, 0.5 * y1)
+    # the page's two-expert construction (Swimba Theorem 5): with the router choosing both of two experts
+    # and expert 0 projecting to zero, the output is the logistic sigmoid of the logit margin times
+    # expert 1's projection
+    T, dm, do = 40, 12, 10
+    X = _rand(rng, (T, dm))
+    Wr = _rand(rng, (dm, 2), 0.5)
+    W = _rand(rng, (2, do, dm), 0.4)
+    W[0] = 0.0
+    r = orc.route(X, Wr, top_k=2)
+    y = orc.in_proj_weighted(X, r["ids"], r["prob"], W)
+    l64 = X.astype(np.float64) @ Wr.astype(np.float64)
+    ref = expit(l64[:, 1] - l64[:, 0])[:, None] * (X.astype(np.float64) @ W[1].astype(np.float64).T)
+    np.testing.assert_allclose(y, ref, rtol=2e-6, atol=1e-9)
+    # identical experts, both chosen: the weights sum to 1, so the output is the single projection
+    W[0] = W[1]
+    y = orc.in_proj_weighted(X, r["ids"], r["prob"], W)
+    np.testing.assert_allclose(y, X.astype(np.float64) @ W[0].astype(np.float64).T, rtol=2e-6, atol=1e-9)
+
+
 # ------------------------------------------------------------------------------------------------
 # hand-worked example
 
@@ -316,4 +356,5 @@ def pin_handworked(orc):
     np.testing.assert_allclose(out[0], ev(np.array(e2["out_t0"])), rtol=1e-6, atol=1e-12)
 
 
-ALL_PINS = [pin_router_bruteforce, pin_router_special, pin_sort, pin_in_proj, pin_out_proj, pin_handworked]
+ALL_PINS = [pin_router_bruteforce, pin_router_special, pin_sort, pin_in_proj, pin_out_proj, pin_in_proj_weighted,
+            pin_handworked]

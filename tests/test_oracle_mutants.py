@@ -42,6 +42,13 @@ MUTANTS = [
     ("out_proj_unscaled", [("o += (double)prob[t * K + s] * acc;", "o += acc;")]),
     ("out_proj_transposed_weight", [("const float *wo = Wo + (i * dm + m) * di;", "const float *wo = Wo + i * dm * di + m;"),
                                     ("acc += a[c] * (double)wo[c];", "acc += a[c] * (double)wo[c * dm];")]),
+    ("weighted_in_proj_unscaled", [("yc += (double)prob[t * K + s] * stream;", "yc += stream;")]),
+    ("weighted_in_proj_only_first_expert",
+     [("for (int32_t s = 0; s < K; ++s) {\n                const int64_t i = ids[t * K + s];\n                const float *w ",
+       "for (int32_t s = 0; s < 1; ++s) {\n                const int64_t i = ids[t * K + s];\n                const float *w ")]),
+    ("weighted_in_proj_transposed_weight", [("const float *w = W + (i * dout + c) * dm;", "const float *w = W + i * dout * dm + c;"),
+                                            ("stream += (double)x[k] * (double)w[k];",
+                                             "stream += (double)x[k] * (double)w[k * dout];")]),
 ]
 
 
