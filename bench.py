@@ -6,6 +6,9 @@ One step = the whole routed path over one batch of synthetic tokens, through the
     rom_in_proj  Conv/Gate expert grouped GEMM (bf16 MFMA), rows gathered through perm, un-permuted
     rom_out_proj Out expert grouped GEMM on SiLU(z)*h, scaled by the router probability, un-permuted
 (Routing Mamba landing page on chapterpal.com, Knowl 1.) Inputs are resident in HBM before timing.
+For the Swimba workloads (swimba_decode_T*) one step is rom_route + rom_in_proj_weighted, the routed part of a
+Switch Mamba layer (Swimba project page, extended abstract): expert in-projections whose outputs are weighted
+by the router probability.
 
 Default workload: the Samba-421M-like block, T = 4 x 4096 tokens, d_model 1024, d_inner 2048, 8 experts,
 bf16 data. Prints ONE JSON line: whole-step tokens/s, the roofline of the dominant kernel (the
@@ -70,18 +73,22 @@ def cpu_baseline(inp, w, target_seconds: float):
 
     def run(n):
         t0 = time.perf_counter()
-        r = orc.route(inp["X"][:n], inp["W_router"], inp.get("bias"))
+        r = orc.route(inp["X"][:n], inp["W_router"], inp.get("bias"), top_k=w.top_k)
         orc.sort(r["ids"], w.E)
-        x, z = orc.in_proj(inp["X"][:n], r["ids"], inp["W_conv"], inp["W_gate"])
-        orc.out_proj(z, inp["h"][:n], r["ids"], r["prob"], inp["W_out"])
+        if w.method == "swimba":
+            orc.in_proj_weighted(inp["X"][:n], r["ids"], r["prob"], inp["W_in"])
+        else:
+            x, z = orc.in_proj(inp["X"][:n], r["ids"], inp["W_conv"], inp["W_gate"])
+            orc.out_proj(z, inp["h"][:n], r["ids"], r["prob"], inp["W_out"])
         return time.perf_counter() - t0
 
     probe = min(w.T, 32)
     tp = run(probe)
     n = int(max(probe, min(w.T, probe * target_seconds / max(tp, 1e-6))))
     dt = run(n) if n > probe else tp
+    path = "in_proj_weighted" if w.method == "swimba" else "in_proj + out_proj"
     return {"value": n / dt, "unit": "tokens/s", "cores": orc.threads(), "kind": "oracle",
-            "sample": f"first {n} of {w.T} tokens: route + histogram/sort + in_proj + out_proj in plain C "
+            "sample": f"first {n} of {w.T} tokens: route + histogram/sort + {path} in plain C "
                       f"(fp32 router, fp64 projection sums, OpenMP over tokens), {dt:.1f} s"}
 
 
@@ -109,7 +116,9 @@ def main() -> int:
     import workloads
 
     w = workloads.get_workload(args.workload)
-    inp = workloads.make_inputs(w, which={"X", "W_router", "W_conv", "W_gate", "W_out", "h"})
+    swimba = w.method == "swimba"
+    inp = workloads.make_inputs(w, which={"X", "W_router", "W_in"} if swimba else
+                                {"X", "W_router", "W_conv", "W_gate", "W_out", "h"})
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -118,14 +127,19 @@ def main() -> int:
             return torch.from_numpy(workloads.bf16_bits(a).view(np.int16).copy()).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    X, h = up(inp["X"], w.dtype), up(inp["h"], w.dtype)
-    Wc, Wg, Wo = up(inp["W_conv"], w.dtype), up(inp["W_gate"], w.dtype), up(inp["W_out"], w.dtype)
+    X = up(inp["X"], w.dtype)
     Wr = up(inp["W_router"], "f32")
     bias = up(inp["bias"], "f32") if inp.get("bias") is not None else None
     routing = rom.Routing(w.T, w.E, dev, top_k=w.top_k)
-    x = torch.empty((w.T, w.d_inner), dtype=X.dtype, device=dev)
-    z = torch.empty_like(x)
-    out = torch.empty((w.T, w.d_model), dtype=X.dtype, device=dev)
+    if swimba:
+        W_in = up(inp["W_in"], w.dtype)
+        y = torch.empty((w.T, w.dout), dtype=X.dtype, device=dev)
+    else:
+        h = up(inp["h"], w.dtype)
+        Wc, Wg, Wo = up(inp["W_conv"], w.dtype), up(inp["W_gate"], w.dtype), up(inp["W_out"], w.dtype)
+        x = torch.empty((w.T, w.d_inner), dtype=X.dtype, device=dev)
+        z = torch.empty_like(x)
+        out = torch.empty((w.T, w.d_model), dtype=X.dtype, device=dev)
     # cold runs stream this buffer through the caches before each step; reading (not writing) it leaves no
     # dirty lines whose write-back would be charged to the step
     flush = torch.zeros((1 << 30) // 4, dtype=torch.int32, device=dev) if args.cold else None
@@ -144,10 +158,14 @@ def main() -> int:
         rom.route(X, Wr, bias, top_k=w.top_k, routing=routing, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        rom.in_proj(X, routing, Wc, Wg, x, z, stream=stream)
+        if swimba:
+            rom.in_proj_weighted(X, routing, W_in, y, stream=stream)
+        else:
+            rom.in_proj(X, routing, Wc, Wg, x, z, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        rom.out_proj(z, h, routing, Wo, out, stream=stream)
+        if not swimba:
+            rom.out_proj(z, h, routing, Wo, out, stream=stream)
         if ev is not None:
             ev[3].record(stream)
 
@@ -177,15 +195,17 @@ def main() -> int:
     t_route = np.array([e[0].elapsed_time(e[1]) for e in events]) * 1e-3
     t_in = np.array([e[1].elapsed_time(e[2]) for e in events]) * 1e-3
     t_out = np.array([e[2].elapsed_time(e[3]) for e in events]) * 1e-3
-    fl_in = 4.0 * w.T * w.d_model * w.d_inner * w.top_k
-    fl_out = 2.0 * w.T * w.d_model * w.d_inner * w.top_k
+    # the in-projection's output width: Conv + Gate (2 * d_inner) for RoM, d_out for Swimba
+    n_in = w.dout if swimba else 2 * w.d_inner
+    fl_in = 2.0 * w.T * w.d_model * n_in * w.top_k
+    fl_out = 0.0 if swimba else 2.0 * w.T * w.d_model * w.d_inner * w.top_k
     peak = PEAK_MFMA_TFLOPS[w.dtype]
     counts = routing.counts.cpu().numpy()  # [top_k][E]
     es = 2 if w.dtype == "bf16" else 4
     used = int(np.count_nonzero(counts))  # expert stacks streamed, summed over the choices
     # algorithmic bytes: every operand and result moved once, only the experts that received tokens
-    bytes_in = es * (w.T * w.d_model + used * 2 * w.d_inner * w.d_model + 2 * w.T * w.d_inner)
-    bytes_out = es * (2 * w.T * w.d_inner + used * w.d_model * w.d_inner + w.T * w.d_model) + 4 * w.T * 2
+    bytes_in = es * (w.T * w.d_model + used * n_in * w.d_model + w.T * n_in)
+    bytes_out = 0 if swimba else es * (2 * w.T * w.d_inner + used * w.d_model * w.d_inner + w.T * w.d_model) + 4 * w.T * 2
     bytes_route = es * w.T * w.d_model + 4 * w.d_model * w.E + 4 * w.T * 4
     ms_per_step = elapsed / args.steps * 1e3
     mean_in, mean_out, mean_route = float(t_in.mean()), float(t_out.mean()), float(t_route.mean())
@@ -200,13 +220,19 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4)}
     roof["traffic"] = measured_traffic(w.name)
+    entry = "rom_in_proj_weighted" if swimba else "rom_in_proj"
     if w.dtype != "bf16":
-        roof["kernel"] = "k_grouped_gemm_f32 (rom_in_proj)"
+        roof["kernel"] = f"k_grouped_gemm_f32 ({entry})"
     else:
-        roof["kernel"] = ("k_grouped_gemv_bf16" if decode else "k_grouped_gemm_bf16") + " (rom_in_proj)"
+        roof["kernel"] = ("k_grouped_gemv_bf16" if decode else "k_grouped_gemm_bf16") + f" ({entry})"
     roof["algorithmic"] = ({"bytes_per_launch": bytes_in} if decode else {"flops_per_launch": fl_in})
     roof["launch_us"] = round(mean_in * 1e6, 2)
 
+    config = {"workload": w.name, "T": w.T, "d_model": w.d_model, "d_inner": w.d_inner, "E": w.E,
+              "top_k": w.top_k, "router": "fp32", "cache": "cold" if args.cold else "warm",
+              "expert_loads": counts[0].tolist() if w.top_k == 1 else counts.tolist()}
+    if swimba:
+        config["d_out"] = w.dout
     result = {
         "metric": METRIC,
         "value": round(w.T * args.steps / elapsed, 1),
@@ -220,20 +246,18 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic: seeded Gaussian tensors of the workload's shapes (no dataset)",
-        "config": {"workload": w.name, "T": w.T, "d_model": w.d_model, "d_inner": w.d_inner, "E": w.E,
-                   "top_k": w.top_k, "router": "fp32", "cache": "cold" if args.cold else "warm",
-                   "expert_loads": counts[0].tolist() if w.top_k == 1 else counts.tolist()},
+        "config": config,
         "roofline": roof,
         "breakdown": {
             "route_us": round(mean_route * 1e6, 2),
             "in_proj_us": round(mean_in * 1e6, 2),
             "out_proj_us": round(mean_out * 1e6, 2),
             "in_proj_tflops": round(fl_in / mean_in / 1e12, 1),
-            "out_proj_tflops": round(fl_out / mean_out / 1e12, 1),
+            "out_proj_tflops": round(fl_out / mean_out / 1e12, 1) if mean_out > 0 else 0.0,
             "gemm_mfma_frac": round((fl_in + fl_out) / (mean_in + mean_out) / 1e12 / peak, 4),
             "route_gbs": round(bytes_route / mean_route / 1e9, 1),
             "in_proj_gbs": round(bytes_in / mean_in / 1e9, 1),
-            "out_proj_gbs": round(bytes_out / mean_out / 1e9, 1),
+            "out_proj_gbs": round(bytes_out / mean_out / 1e9, 1) if mean_out > 0 else 0.0,
             "step_hbm_frac": round((bytes_route + bytes_in + bytes_out) / (mean_route + mean_in + mean_out)
                                    / 1e9 / PEAK_HBM_GBS, 4),
         },

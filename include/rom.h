@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define ROM_ABI_VERSION 3
+#define ROM_ABI_VERSION 4
 #ifndef ROM_API
 #define ROM_API __attribute__((visibility("default")))
 #endif
@@ -120,6 +120,21 @@ ROM_API rom_status rom_route(const void *X, rom_dtype x_dtype, int32_t T, int32_
 ROM_API rom_status rom_in_proj(const void *X, const rom_routing *routing, rom_dtype dtype, int32_t T,
                        int32_t d_model, int32_t d_inner, const void *W_conv, const void *W_gate,
                        void *x_out, void *z_out, void *stream);
+
+/*
+ * Routing-weighted in-projection of Switch Mamba (Swimba project page, extended abstract): expert
+ * in-projections behind a token-level softmax router, whose output streams are each weighted by the
+ * routing weight and summed into the single input of the (unchanged) SSM kernel. The routing weight is
+ * the router probability p_t,e of a selected expert, as in r_t,i above (not renormalised):
+ *   y_out[t][n] = sum_{e in S_t} p_t,e * sum_k X[t][k] * W_in[e][n][k]
+ * The same grouped products as rom_out_proj, applied to X with no gate; accumulation is fp32 (MFMA for
+ * bf16 data), each choice's contribution is rounded once, and the choices are added in the order
+ * k = 0, 1 as for rom_in_proj. Output in token order. Swimba routes 4 experts, top-1 per token.
+ *   X [T][d_model]; W_in [E][d_out][d_model]; y_out [T][d_out]; all dtype; d_out a multiple of 64.
+ *   X may not alias y_out.
+ */
+ROM_API rom_status rom_in_proj_weighted(const void *X, const rom_routing *routing, rom_dtype dtype, int32_t T,
+                                int32_t d_model, int32_t d_out, const void *W_in, void *y_out, void *stream);
 
 /* Bytes of device workspace rom_out_proj needs (T * d_inner bf16 values for bf16 data; 0 for fp32 data). */
 ROM_API size_t rom_out_proj_workspace_bytes(int32_t T, int32_t d_inner, rom_dtype dtype);

@@ -22,15 +22,15 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["route", "in_proj", "out_proj", "Routing", "RomError", "lib", "LIB_PATH", "ABI_VERSION",
+__all__ = ["route", "in_proj", "in_proj_weighted", "out_proj", "Routing", "RomError", "lib", "LIB_PATH", "ABI_VERSION",
            "route_workspace_bytes", "out_proj_workspace_bytes"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "librom.so")
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 ROM_OK, ROM_ERR_INVALID_ARGUMENT, ROM_ERR_UNSUPPORTED, ROM_ERR_WORKSPACE_TOO_SMALL, ROM_ERR_HIP = range(5)
 ROM_DTYPE_F32, ROM_DTYPE_BF16 = 0, 1
-ABI_SYMBOLS = ("rom_abi_version", "rom_route_workspace_bytes", "rom_route", "rom_in_proj",
+ABI_SYMBOLS = ("rom_abi_version", "rom_route_workspace_bytes", "rom_route", "rom_in_proj", "rom_in_proj_weighted",
                "rom_out_proj_workspace_bytes", "rom_out_proj", "rom_status_string", "rom_last_error")
 
 
@@ -68,6 +68,9 @@ def lib(path: str = LIB_PATH) -> ctypes.CDLL:
     L.rom_in_proj.argtypes = [_vp, ctypes.POINTER(RoutingStruct), ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                               _vp]
     L.rom_in_proj.restype = ctypes.c_int
+    L.rom_in_proj_weighted.argtypes = [_vp, ctypes.POINTER(RoutingStruct), ctypes.c_int, _i32, _i32, _i32, _vp, _vp,
+                                       _vp]
+    L.rom_in_proj_weighted.restype = ctypes.c_int
     L.rom_out_proj_workspace_bytes.argtypes = [_i32, _i32, ctypes.c_int]
     L.rom_out_proj_workspace_bytes.restype = _sz
     L.rom_out_proj.argtypes = [_vp, _vp, ctypes.POINTER(RoutingStruct), ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp,
@@ -186,6 +189,24 @@ def in_proj(X: torch.Tensor, routing: Routing, W_conv: torch.Tensor, W_gate: tor
                                _ptr(W_gate), _ptr(x_out), _ptr(z_out), _stream(X.device, stream))
     _check(status, "rom_in_proj")
     return x_out, z_out
+
+
+def in_proj_weighted(X: torch.Tensor, routing: Routing, W_in: torch.Tensor, y_out: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """rom_in_proj_weighted (Swimba): y = sum over the token's experts of p_t,e * W_in[e] X (token order)."""
+    _dev(X, "X")
+    _dev(W_in, "W_in")
+    T, dm = X.shape
+    E, dout, dm2 = W_in.shape
+    if dm2 != dm or W_in.dtype != X.dtype:
+        raise ValueError("W_in must be [E][d_out][d_model] in X's dtype")
+    if E != routing.E:
+        raise ValueError("expert count differs from the routing's")
+    y_out = torch.empty((T, dout), dtype=X.dtype, device=X.device) if y_out is None else _dev(y_out, "y_out")
+    status = lib().rom_in_proj_weighted(_ptr(X), ctypes.byref(routing.struct), _dtype_code(X), T, dm, dout,
+                                        _ptr(W_in), _ptr(y_out), _stream(X.device, stream))
+    _check(status, "rom_in_proj_weighted")
+    return y_out
 
 
 def out_proj_workspace_bytes(T: int, d_inner: int, dtype: torch.dtype) -> int:

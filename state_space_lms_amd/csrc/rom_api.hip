@@ -160,6 +160,27 @@ rom_status rom_in_proj(const void *X, const rom_routing *routing, rom_dtype dtyp
     return ROM_OK;
 }
 
+rom_status rom_in_proj_weighted(const void *X, const rom_routing *routing, rom_dtype dtype, int32_t T,
+                                int32_t d_model, int32_t d_out, const void *W_in, void *y_out, void *stream) {
+    g_last_error[0] = '\0';
+    rom_status s;
+    if ((s = check_dtype(dtype)) != ROM_OK) return s;
+    if ((s = check_dims(T, d_model, "d_model")) != ROM_OK) return s;
+    if ((s = check_dims(T, d_out, "d_out")) != ROM_OK) return s;
+    if ((s = check_routing_for_proj(routing, T)) != ROM_OK) return s;
+    if (T == 0) return ROM_OK;
+    ROM_CHECK_PTR(X, 16);
+    ROM_CHECK_PTR(W_in, 16);
+    ROM_CHECK_PTR(y_out, 16);
+    const size_t es = elem_size(dtype);
+    if (overlap(X, (size_t)T * d_model * es, y_out, (size_t)T * d_out * es))
+        return fail(ROM_ERR_INVALID_ARGUMENT, "X overlaps y_out");
+    hipError_t err = rom::launch_in_proj_weighted(X, *routing, dtype, T, d_model, d_out, W_in, y_out,
+                                                  static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, "rom_in_proj_weighted launch");
+    return ROM_OK;
+}
+
 size_t rom_out_proj_workspace_bytes(int32_t T, int32_t d_inner, rom_dtype dtype) {
     if (T <= 0 || d_inner <= 0 || (dtype != ROM_DTYPE_F32 && dtype != ROM_DTYPE_BF16)) return 0;
     return rom::out_proj_workspace_bytes(T, d_inner, dtype);

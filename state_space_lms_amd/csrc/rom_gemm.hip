@@ -28,7 +28,7 @@ namespace rom {
 
 struct GemmArgs {
     const void *A0;       // in-proj: X [T][K];  out-proj: z [T][K]
-    const void *A1;       // out-proj: h [T][K]
+    const void *A1;       // out-proj: h [T][K] (fp32 kernel only; NULL: A rows are used as they are)
     const void *B0;       // in-proj: W_conv [E][N0][K];  out-proj: W_out [E][N0][K]
     const void *B1;       // in-proj: W_gate [E][N0][K]
     void *C0;             // in-proj: x_out [T][N0];  out-proj: out [T][N0]
@@ -559,13 +559,14 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs p) {
     const int lr = tid >> 2, lk = (tid & 3) * 4;  // row 0..63, k offset 0,4,8,12
     const int tok = s_tok[lr];
     const float *a_src = tok >= 0 ? static_cast<const float *>(p.A0) + (size_t)tok * K + lk : nullptr;
-    const float *h_src = (OUT && tok >= 0) ? static_cast<const float *>(p.A1) + (size_t)tok * K + lk : nullptr;
+    const float *h_src =
+        (OUT && p.A1 != nullptr && tok >= 0) ? static_cast<const float *>(p.A1) + (size_t)tok * K + lk : nullptr;
     const float *b_src = Bsrc + (size_t)lr * K + lk;
     const int ty = tid >> 4, tx = tid & 15;
     float acc[4][4] = {};
     for (int k0 = 0; k0 < K; k0 += BK) {
         float4 a = a_src ? *reinterpret_cast<const float4 *>(a_src + k0) : make_float4(0, 0, 0, 0);
-        if (OUT && a_src) {
+        if (OUT && h_src) {
             const float4 h = *reinterpret_cast<const float4 *>(h_src + k0);
             a.x = silu_precise(a.x) * h.x;
             a.y = silu_precise(a.y) * h.y;
@@ -769,6 +770,32 @@ hipError_t launch_out_proj(const void *z, const void *h, const rom_routing &r, r
         a.A1 = nullptr;
         a.a_by_token = !slot_order;
     }
+    for (int k = 0; k < r.top_k; ++k) {
+        set_choice(a, r, T, k);
+        hipError_t err;
+        if (dt == ROM_DTYPE_F32) err = launch_f32<true>(a, 1, s);
+        else if (T <= kDecodeMaxT) err = launch_gemv<true>(a, 1, s);
+        else err = launch_bf16_auto<true>(a, 1, s);
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+// Routing-weighted in-projection (Swimba): y[t] = sum over the token's choices of p_t,e * W[e] X[t]. It is
+// the out-projection's grouped product (probability-scaled epilogue, rows gathered in token order through
+// perm) applied to X itself, with no gate.
+hipError_t launch_in_proj_weighted(const void *X, const rom_routing &r, rom_dtype dt, int T, int dm, int dout,
+                                   const void *W, void *y, hipStream_t s) {
+    GemmArgs a{};
+    a.A0 = X;
+    a.A1 = nullptr;
+    a.B0 = W;
+    a.C0 = y;
+    a.T = T;
+    a.K = dm;
+    a.N0 = dout;
+    a.E = r.E;
+    a.a_by_token = 1;
     for (int k = 0; k < r.top_k; ++k) {
         set_choice(a, r, T, k);
         hipError_t err;

@@ -32,7 +32,10 @@ hipError_t launch_in_proj(const void *X, const rom_routing &r, rom_dtype dt, int
 hipError_t launch_out_proj(const void *z, const void *h, const rom_routing &r, rom_dtype dt, int T, int dm, int di,
                            const void *Wo, void *out, void *workspace, hipStream_t s);
 
-// Workspace bytes the out-projection needs (the gated rows in slot order; 0 on the decode and fp32 paths).
+hipError_t launch_in_proj_weighted(const void *X, const rom_routing &r, rom_dtype dt, int T, int dm, int dout,
+                                   const void *W, void *y, hipStream_t s);
+
+// Workspace bytes the out-projection needs (the gated rows a, T * d_inner bf16 values; 0 for fp32 data).
 size_t out_proj_workspace_bytes(int T, int di, rom_dtype dt);
 
 }  // namespace rom

@@ -113,6 +113,25 @@ def test_in_proj_T0_noop(L):
     assert _in(L, X=None, T=0, Wc=None, Wg=None, xo=None, zo=None, r=_routing(0, 8)) == OK
 
 
+def _inw(L, X=A, T=512, dm=128, do=384, W=A, y=A + (1 << 24), r=None, dt=BF16):
+    rs = r if r is not None else _routing(T, 4)
+    return L.rom_in_proj_weighted(X, ctypes.byref(rs), dt, T, dm, do, W, y, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), INVALID), (dict(do=100), UNSUPPORTED), (dict(do=0), INVALID), (dict(dm=32), UNSUPPORTED),
+    (dict(X=None), INVALID), (dict(W=A + 8), INVALID), (dict(y=None), INVALID), (dict(y=A + 512), INVALID),
+    (dict(r=_routing(256, 4)), INVALID), (dict(r=_routing(512, 4, prob=None)), INVALID), (dict(dt=2), INVALID),
+    (dict(r=_routing(512, 4, top_k=3)), UNSUPPORTED), (dict(r=_routing(512, 1, top_k=2)), INVALID),
+])
+def test_in_proj_weighted_rejects(L, kw, code):
+    assert _inw(L, **kw) == code
+
+
+def test_in_proj_weighted_T0_noop(L):
+    assert _inw(L, X=None, T=0, W=None, y=None, r=_routing(0, 4)) == OK
+
+
 WS = A + (1 << 28)
 
 

@@ -279,3 +279,71 @@ def test_top2_full_samba_shape(rom, oracle):
     o_route = oracle.route(inp["X"], inp["W_router"], top_k=2)
     rows = parity.sample_rows(oracle.sort(o_route["ids"][:, :1].copy(), w.E), w.T)
     check_workload_top2(rom, oracle, w, inp, rows=rows, label="samba421m top-2")
+
+
+# ------------------------------------------------------------------------------------------------
+# Swimba's routing-weighted in-projection: y = sum over the token's choices of p * W_in[e] X
+
+def check_weighted(rom, orc, w, top_k=1, inp=None, rows=None, label=""):
+    import torch
+    inp = inp if inp is not None else workloads.make_inputs(w, which={"X", "W_router", "W_in"})
+    tol = parity.TOL[w.dtype]
+    print(f"[parity weighted] {label or w.name}: T={w.T} d_model={w.d_model} d_out={w.dout} E={w.E} "
+          f"top_k={top_k} {w.dtype}", flush=True)
+    X = parity.to_device(inp["X"], w.dtype)
+    Wr = parity.to_device(inp["W_router"], "f32")
+    W = parity.to_device(inp["W_in"], w.dtype)
+    bias = parity.to_device(inp["bias"], "f32") if inp.get("bias") is not None else None
+    r = rom.route(X, Wr, bias, top_k=top_k)
+    y = rom.in_proj_weighted(X, r, W)
+    torch.cuda.synchronize()
+    gr = _route_host(r, squeeze=False)
+    o_route = orc.route(inp["X"], inp["W_router"], inp.get("bias"), top_k=top_k, want_logits=True)
+    agree = parity.check_route_topk(gr, o_route, w.T, w.E, top_k, tol)
+    rows = np.arange(w.T) if rows is None else rows
+    rows = rows[agree[rows]]
+    y_o = orc.in_proj_weighted(inp["X"][rows], o_route["ids"][rows], o_route["prob"][rows], inp["W_in"])
+    ey = parity.norm_max_err(_rows(y, rows), y_o)
+    print(f"[parity weighted]   set-mismatch={int((~agree).sum())} y={ey:.2e} rows={len(rows)}", flush=True)
+    assert ey <= tol, f"y: normalised max error {ey:.3g} > {tol}"
+    return gr
+
+
+WEIGHTED = [
+    (workloads.custom_workload("w_f32", T=300, d_model=64, d_inner=96, E=4, dtype="f32", seed=301), 1),
+    (workloads.custom_workload("w_f32_top2", T=257, d_model=128, d_inner=64, E=4, dtype="f32", seed=302), 2),
+    (workloads.custom_workload("w_bf16_bn256", T=1000, d_model=256, d_inner=128, E=4, seed=303), 1),
+    (workloads.custom_workload("w_bf16_bn64_E3", T=777, d_model=192, d_inner=160, E=3, seed=304), 1),
+    (workloads.custom_workload("w_bf16_T4096", T=4096, d_model=512, d_inner=512, E=4, seed=305), 1),
+    (workloads.custom_workload("w_bf16_top2", T=513, d_model=128, d_inner=192, E=4, seed=306), 2),
+    (workloads.custom_workload("w_T1", T=1, d_model=256, d_inner=160, E=4, seed=307), 1),
+    (workloads.custom_workload("w_T5", T=5, d_model=512, d_inner=128, E=4, seed=308), 1),
+    (workloads.custom_workload("w_T40", T=40, d_model=256, d_inner=160, E=4, seed=309), 1),
+    (workloads.custom_workload("w_T64_top2", T=64, d_model=512, d_inner=256, E=4, seed=310), 2),
+]
+
+
+@pytest.mark.parametrize("w,k", WEIGHTED, ids=[w.name for w, _ in WEIGHTED])
+def test_weighted_in_proj_small_shapes(rom, oracle, w, k):
+    check_weighted(rom, oracle, w, top_k=k)
+
+
+def test_weighted_in_proj_one_expert_is_dense_scaled(rom, oracle):
+    """E = 1: p = 1 exactly, so the output is the dense projection (the oracle's E=1 special case)."""
+    w = workloads.custom_workload("w_E1", T=700, d_model=128, d_inner=128, E=1, seed=311)
+    gr = check_weighted(rom, oracle, w)
+    assert np.all(gr["prob"] == 1.0)
+
+
+@pytest.mark.parametrize("name", ["swimba_decode_T1", "swimba_decode_T8", "swimba_decode_T64"])
+def test_weighted_in_proj_swimba_decode(rom, oracle, name):
+    check_weighted(rom, oracle, workloads.get_workload(name))
+
+
+def test_weighted_in_proj_prefill_shape(rom, oracle):
+    """A 16K-token prefill at d_model 1024, d_out 4096, 4 experts: sampled tokens."""
+    w = workloads.custom_workload("w_prefill", T=16384, d_model=1024, d_inner=2048, E=4, seed=312)
+    inp = workloads.make_inputs(w, which={"X", "W_router", "W_in"})
+    o_route = oracle.route(inp["X"], inp["W_router"])
+    rows = parity.sample_rows(oracle.sort(o_route["ids"], w.E), w.T)
+    check_weighted(rom, oracle, w, inp=inp, rows=rows)

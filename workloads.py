@@ -30,7 +30,7 @@ from typing import Optional
 import numpy as np
 
 # Order of the per-tensor child streams; never reorder (it would change every input).
-_STREAMS = ("X", "W_router", "W_conv", "W_gate", "W_out", "h", "z")
+_STREAMS = ("X", "W_router", "W_conv", "W_gate", "W_out", "h", "z", "W_in")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -49,6 +49,12 @@ class Workload:
     z_std: float          # std of z when the out-projection is tested on its own
     skew: Optional[tuple] = None  # target expert loads (fractions) reached with a router bias
     top_k: int = 1
+    method: str = "rom"   # "rom": routed Conv/Gate/Out projections; "swimba": routing-weighted in-projection
+    d_out: Optional[int] = None  # Swimba in-projection width; None means 2 * d_inner
+
+    @property
+    def dout(self) -> int:
+        return self.d_out if self.d_out is not None else 2 * self.d_inner
 
     @property
     def router_std(self) -> float:
@@ -89,6 +95,13 @@ def decode_workload(T: int) -> Workload:
                     x_std=1.0, wr_std=None, w_std=0.02, h_std=1.0, z_std=1.0)
 
 
+def swimba_decode_workload(T: int) -> Workload:
+    """Swimba decode: T tokens in {1, 8, 64}, 4 experts, top-1, routing-weighted in-projection of
+    width 2 * d_inner (the x and z streams; the page gives no widths)."""
+    return Workload(f"swimba_decode_T{T}", T=T, d_model=4096, d_inner=8192, E=4, dtype="bf16", seed=60 + T,
+                    x_std=1.0, wr_std=None, w_std=0.02, h_std=1.0, z_std=1.0, method="swimba")
+
+
 def custom_workload(name, T, d_model, d_inner, E, dtype="bf16", seed=7, **kw) -> Workload:
     """A workload of arbitrary shape with the large-config value recipe (for edge-case tests)."""
     args = dict(x_std=1.0, wr_std=None, w_std=0.02, h_std=1.0, z_std=1.0)
@@ -99,6 +112,8 @@ def custom_workload(name, T, d_model, d_inner, E, dtype="bf16", seed=7, **kw) ->
 
 
 def get_workload(name: str) -> Workload:
+    if name.startswith("swimba_decode_T"):
+        return swimba_decode_workload(int(name[len("swimba_decode_T"):]))
     if name.startswith("decode_T"):
         return decode_workload(int(name[len("decode_T"):]))
     return WORKLOADS[name]
@@ -140,8 +155,10 @@ def make_inputs(w: Workload, router_bias: Optional[np.ndarray] = None, which=Non
 
     Keys: X [T][d_model], W_router [d_model][E] (always fp32), W_conv and W_gate [E][d_inner][d_model],
     W_out [E][d_model][d_inner], h [T][d_inner], z [T][d_inner] (only for testing the out-projection on its
-    own), bias [E] or None. Expert matrices are stored [out][in], i.e. K-contiguous.
-    ``which`` restricts generation to a subset of keys (the streams stay the same).
+    own), W_in [E][d_out][d_model] (Swimba's in-projection experts), bias [E] or None. Expert matrices are
+    stored [out][in], i.e. K-contiguous.
+    ``which`` restricts generation to a subset of keys (the streams stay the same); by default every key
+    but W_in is drawn, and W_in only when ``which`` names it.
     """
     children = np.random.SeedSequence(w.seed).spawn(len(_STREAMS))
     rngs = {k: np.random.Generator(np.random.PCG64(c)) for k, c in zip(_STREAMS, children)}
@@ -153,10 +170,11 @@ def make_inputs(w: Workload, router_bias: Optional[np.ndarray] = None, which=Non
         "W_out": ((w.E, w.d_model, w.d_inner), w.w_std, w.dtype),
         "h": ((w.T, w.d_inner), w.h_std, w.dtype),
         "z": ((w.T, w.d_inner), w.z_std, w.dtype),
+        "W_in": ((w.E, w.dout, w.d_model), w.w_std, w.dtype),
     }
     out = {}
     for k in _STREAMS:
-        if which is not None and k not in which:
+        if (which is None and k == "W_in") or (which is not None and k not in which):
             continue
         shape, std, storage = shapes[k]
         out[k] = _draw(rngs[k], shape, std, storage)
