@@ -64,6 +64,8 @@ class Oracle:
         lib.orom_out_proj.restype = None
         lib.orom_in_proj_weighted.argtypes = [_f32p, _i64, _i64, _i64, _i32p, _f32p, _i32, _f32p, _i32, _f64p]
         lib.orom_in_proj_weighted.restype = None
+        lib.orom_conv1d.argtypes = [_f32p, _i64, _i64, _i64, _f32p, ctypes.c_void_p, _i32, _i32, _f64p]
+        lib.orom_conv1d.restype = None
         self.lib = lib
 
     def threads(self) -> int:
@@ -155,6 +157,22 @@ class Oracle:
         assert ids.size == 0 or (ids.min() >= 0 and ids.max() < E)
         y = np.empty((n, dout), np.float64)
         self.lib.orom_in_proj_weighted(X, n, dm, dout, ids, prob, ids.shape[1], W, E, y)
+        return y
+
+    def conv1d(self, H, weight, bias=None, activation: bool = True):
+        """Shared short causal depthwise convolution of each sequence of H [nseq][L][C]; weight [C][w];
+        returns y [nseq][L][C] in float64."""
+        H = np.ascontiguousarray(H, dtype=np.float32)
+        nseq, L, C = H.shape
+        W = np.ascontiguousarray(weight, dtype=np.float32)
+        assert W.shape[0] == C and W.ndim == 2
+        b = None
+        if bias is not None:
+            b = np.ascontiguousarray(bias, dtype=np.float32)
+            assert b.shape == (C,)
+        y = np.empty((nseq, L, C), np.float64)
+        self.lib.orom_conv1d(H, nseq, L, C, W, None if b is None else b.ctypes.data, W.shape[1],
+                             1 if activation else 0, y)
         return y
 
     # -- the whole routed path for a subset of tokens --------------------------------------------

@@ -261,3 +261,35 @@ void orom_in_proj_weighted(const float *X, int64_t n, int64_t dm, int64_t dout, 
         }
     }
 }
+
+/* ---------------------------------------------------------------------------
+ * Shared short causal convolution (Routing Mamba landing page, Knowl 1: the
+ * short convolution applied to H_t before the selective SSM; Knowl 9: the 1D
+ * convolution is shared across experts, not expertized). The page gives no
+ * width, no bias convention and no activation; the reading taken here is a
+ * depthwise (per-channel) causal convolution of width w over each sequence
+ * separately, with zeros before a sequence's first token, an optional
+ * per-channel bias, and an optional SiLU on the result:
+ *   u[b][t][c] = bias[c] + sum_{j<w} W[c][j] * H[b][t - (w-1) + j][c]
+ *   y[b][t][c] = act ? SiLU(u) : u,   H[b][s][c] = 0 for s < 0
+ * so W[c][w-1] multiplies the current token and W[c][0] the oldest.
+ * H [nseq][L][C] fp32 (token order, sequences contiguous), W [C][w],
+ * bias [C] or NULL. Output y in double.
+ */
+void orom_conv1d(const float *H, int64_t nseq, int64_t L, int64_t C, const float *W, const float *bias,
+                 int32_t w, int32_t act, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t bt = 0; bt < nseq * L; ++bt) {
+        const int64_t b = bt / L, t = bt % L;
+        for (int64_t c = 0; c < C; ++c) {
+            double u = bias ? (double)bias[c] : 0.0;
+            for (int32_t j = 0; j < w; ++j) {
+                const int64_t s = t - (w - 1) + j;
+                if (s < 0) continue;
+                u += (double)W[c * w + j] * (double)H[(b * L + s) * C + c];
+            }
+            y[bt * C + c] = act ? u / (1.0 + exp(-u)) : u;
+        }
+    }
+}

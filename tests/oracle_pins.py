@@ -289,6 +289,55 @@ def pin_in_proj_weighted(orc):
     np.testing.assert_allclose(y, X.astype(np.float64) @ W[0].astype(np.float64).T, rtol=2e-6, atol=1e-9)
 
 
+def pin_conv1d(orc):
+    """The shared short causal convolution (RoM landing page, Knowl 1 and Knowl 9)."""
+    rng = np.random.default_rng(17)
+    # each channel of each sequence against numpy's full linear convolution, truncated to the causal part:
+    # numpy.convolve(h, k)[t] = sum_j h[t - j] k[j], so the taps go in reversed (newest-first) order
+    for (nseq, L, C, w) in [(2, 37, 5, 4), (3, 9, 3, 2), (1, 6, 4, 7)]:
+        H = _rand(rng, (nseq, L, C))
+        W = _rand(rng, (C, w), 0.5)
+        b = _rand(rng, (C,), 0.3)
+        u = orc.conv1d(H, W, b, activation=False)
+        y = orc.conv1d(H, W, b, activation=True)
+        ref = np.zeros((nseq, L, C))
+        for s in range(nseq):
+            for c in range(C):
+                ref[s, :, c] = np.convolve(H[s, :, c].astype(np.float64), W[c, ::-1].astype(np.float64))[:L] + b[c]
+        np.testing.assert_allclose(u, ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(y, ref * expit(ref), rtol=1e-12, atol=1e-12)
+    # width 1: a per-channel scale and shift, exactly
+    H = _rand(rng, (2, 11, 6))
+    W = _rand(rng, (6, 1))
+    b = _rand(rng, (6,))
+    np.testing.assert_array_equal(orc.conv1d(H, W, b, activation=False),
+                                  H.astype(np.float64) * W[:, 0].astype(np.float64) + b.astype(np.float64))
+    # impulse response: a unit impulse at time t0 of one sequence shows the taps in order W[c][w-1], ..., W[c][0]
+    # at times t0, t0+1, ..., and nothing before t0 or in the other sequence
+    nseq, L, C, w = 2, 12, 3, 4
+    H = np.zeros((nseq, L, C), np.float32)
+    H[1, 5, :] = 1.0
+    W = _rand(rng, (C, w))
+    y = orc.conv1d(H, W, None, activation=False)
+    assert np.all(y[0] == 0.0) and np.all(y[1, :5] == 0.0) and np.all(y[1, 5 + w:] == 0.0)
+    np.testing.assert_array_equal(y[1, 5:5 + w], W[:, ::-1].T.astype(np.float64))
+    # sequences are independent: a sequence's output does not depend on the one before it (the
+    # convolution starts from zeros at every sequence's first token)
+    H = _rand(rng, (2, 10, 4))
+    W = _rand(rng, (4, 4))
+    a = orc.conv1d(H, W, None)
+    H2 = H.copy()
+    H2[0] = 7.0
+    b2 = orc.conv1d(H2, W, None)
+    np.testing.assert_array_equal(a[1], b2[1])
+    # causality: changing token t changes no output before t
+    H3 = H.copy()
+    H3[1, 6] += 1.0
+    c3 = orc.conv1d(H3, W, None)
+    np.testing.assert_array_equal(a[1, :6], c3[1, :6])
+    assert np.all(c3[1, 6] != a[1, 6])
+
+
 # ------------------------------------------------------------------------------------------------
 # hand-worked example
 
@@ -357,4 +406,4 @@ def pin_handworked(orc):
 
 
 ALL_PINS = [pin_router_bruteforce, pin_router_special, pin_sort, pin_in_proj, pin_out_proj, pin_in_proj_weighted,
-            pin_handworked]
+            pin_conv1d, pin_handworked]

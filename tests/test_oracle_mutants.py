@@ -49,6 +49,13 @@ MUTANTS = [
     ("weighted_in_proj_transposed_weight", [("const float *w = W + (i * dout + c) * dm;", "const float *w = W + i * dout * dm + c;"),
                                             ("stream += (double)x[k] * (double)w[k];",
                                              "stream += (double)x[k] * (double)w[k * dout];")]),
+    ("conv1d_anticausal_taps", [("const int64_t s = t - (w - 1) + j;", "const int64_t s = t - j;")]),
+    # reads the previous sequence's last tokens instead of zeros
+    ("conv1d_crosses_sequences", [("if (s < 0) continue;", "if (b * L + s < 0) continue;")]),
+    ("conv1d_drops_bias", [("double u = bias ? (double)bias[c] : 0.0;", "double u = 0.0;")]),
+    ("conv1d_silu_sign", [("y[bt * C + c] = act ? u / (1.0 + exp(-u)) : u;", "y[bt * C + c] = act ? u / (1.0 + exp(u)) : u;")]),
+    ("conv1d_drops_oldest_tap", [("for (int32_t j = 0; j < w; ++j) {\n                const int64_t s",
+                                  "for (int32_t j = 1; j < w; ++j) {\n                const int64_t s")]),
 ]
 
 
