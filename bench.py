@@ -35,6 +35,7 @@ PEAK_HBM_GBS = 8000.0                                # MI355X HBM3E
 KERNEL_SOURCES = ["state_space_lms_amd/csrc/rom_gemm.hip", "state_space_lms_amd/csrc/rom_device.h"]
 COUNTERS_FILE = "profiles/counters_in_proj_{workload}.txt"
 COPY_PROBE_BYTES = 256 << 20
+CONV_WIDTH = 4   # the pages give no width for the short convolution; 4 is the value this benchmark takes
 
 
 def kernel_source_hash() -> str:
@@ -65,10 +66,11 @@ def measured_traffic(workload: str):
         return None
 
 
-def cpu_baseline(inp, w, target_seconds: float):
+def cpu_baseline(inp, w, target_seconds: float, conv: bool = False):
     """The CPU oracle as it stands, timed on a bounded prefix of the workload's tokens."""
     import numpy as np
     import oracle
+    import workloads
     orc = oracle.default()
 
     def run(n):
@@ -79,6 +81,9 @@ def cpu_baseline(inp, w, target_seconds: float):
             orc.in_proj_weighted(inp["X"][:n], r["ids"], r["prob"], inp["W_in"])
         else:
             x, z = orc.in_proj(inp["X"][:n], r["ids"], inp["W_conv"], inp["W_gate"])
+            if conv:
+                cin = workloads.make_conv_inputs(1, 1, w.d_inner, CONV_WIDTH, w.dtype, seed=w.seed)
+                orc.conv1d(x.astype(np.float32)[None], cin["weight"], cin["bias"])
             orc.out_proj(z, inp["h"][:n], r["ids"], r["prob"], inp["W_out"])
         return time.perf_counter() - t0
 
@@ -86,7 +91,8 @@ def cpu_baseline(inp, w, target_seconds: float):
     tp = run(probe)
     n = int(max(probe, min(w.T, probe * target_seconds / max(tp, 1e-6))))
     dt = run(n) if n > probe else tp
-    path = "in_proj_weighted" if w.method == "swimba" else "in_proj + out_proj"
+    path = "in_proj_weighted" if w.method == "swimba" else ("in_proj + conv1d + out_proj" if conv else
+                                                            "in_proj + out_proj")
     return {"value": n / dt, "unit": "tokens/s", "cores": orc.threads(), "kind": "oracle",
             "sample": f"first {n} of {w.T} tokens: route + histogram/sort + {path} in plain C "
                       f"(fp32 router, fp64 projection sums, OpenMP over tokens), {dt:.1f} s"}
@@ -100,6 +106,9 @@ def main() -> int:
     ap.add_argument("--workload", default="samba421m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--with-conv1d", action="store_true",
+                    help="add the shared short causal convolution (width 4, SiLU, bias) on the in-projection's x to "
+                         "the step (prefill RoM workloads)")
     ap.add_argument("--cold", action="store_true",
                     help="read a 1 GiB buffer before every step, so weights and inputs come from HBM (decode); the "
                          "step is then timed with GPU events around it")
@@ -117,6 +126,11 @@ def main() -> int:
 
     w = workloads.get_workload(args.workload)
     swimba = w.method == "swimba"
+    conv = args.with_conv1d
+    if conv and (swimba or w.T <= 64):
+        print("bench.py: --with-conv1d needs a prefill RoM workload (the decode-time convolution state is not "
+              "built)", file=sys.stderr)
+        return 2
     inp = workloads.make_inputs(w, which={"X", "W_router", "W_in"} if swimba else
                                 {"X", "W_router", "W_conv", "W_gate", "W_out", "h"})
     dev = torch.device("cuda:0")
@@ -140,6 +154,10 @@ def main() -> int:
         x = torch.empty((w.T, w.d_inner), dtype=X.dtype, device=dev)
         z = torch.empty_like(x)
         out = torch.empty((w.T, w.d_model), dtype=X.dtype, device=dev)
+    if conv:
+        cin = workloads.make_conv_inputs(1, 1, w.d_inner, CONV_WIDTH, w.dtype, seed=w.seed)
+        Wcv, bcv = up(cin["weight"], w.dtype), up(cin["bias"], w.dtype)
+        xc = torch.empty((w.T, w.d_inner), dtype=X.dtype, device=dev)
     # cold runs stream this buffer through the caches before each step; reading (not writing) it leaves no
     # dirty lines whose write-back would be charged to the step
     flush = torch.zeros((1 << 30) // 4, dtype=torch.int32, device=dev) if args.cold else None
@@ -151,23 +169,34 @@ def main() -> int:
     del cp_src, cp_dst
 
     stream = torch.cuda.current_stream(dev)
+    phases = ["route", "in"] + (["conv"] if conv else []) + ([] if swimba else ["out"])
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        rom.route(X, Wr, bias, top_k=w.top_k, routing=routing, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        if swimba:
-            rom.in_proj_weighted(X, routing, W_in, y, stream=stream)
+    def run_phase(ph):
+        if ph == "route":
+            rom.route(X, Wr, bias, top_k=w.top_k, routing=routing, stream=stream)
+        elif ph == "in":
+            if swimba:
+                rom.in_proj_weighted(X, routing, W_in, y, stream=stream)
+            else:
+                rom.in_proj(X, routing, Wc, Wg, x, z, stream=stream)
+        elif ph == "conv":
+            rom.conv1d(x, Wcv, bcv, n_seq=w.n_seq, activation=True, y=xc, stream=stream)
         else:
-            rom.in_proj(X, routing, Wc, Wg, x, z, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
-        if not swimba:
             rom.out_proj(z, h, routing, Wo, out, stream=stream)
+
+    def step(ev=None, around_in=None):
+        """ev: an event before every phase and one after the last; around_in: two events bracketing the
+        in-projection only."""
+        for i, ph in enumerate(phases):
+            if ev is not None:
+                ev[i].record(stream)
+            if around_in is not None and ph == "in":
+                around_in[0].record(stream)
+            run_phase(ph)
+            if around_in is not None and ph == "in":
+                around_in[1].record(stream)
         if ev is not None:
-            ev[3].record(stream)
+            ev[-1].record(stream)
 
     for _ in range(args.warmup):
         if flush is not None:
@@ -175,26 +204,36 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    new_ev = lambda n: [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    events = [new_ev(len(phases) + 1) for _ in range(args.steps)]
     if flush is None:
+        # warm: wall clock over K back-to-back steps; inside them only the in-projection is bracketed by
+        # events (the roofline's launch time), so the timed region carries two markers per step
+        ins = [new_ev(2) for _ in range(args.steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(args.steps):
-            step(events[k])
+            step(around_in=ins[k])
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
+        t_in_timed = np.array([e[0].elapsed_time(e[1]) for e in ins]) * 1e-3
+        # per-phase breakdown from a second, untimed pass of the same K steps
+        for k in range(args.steps):
+            step(ev=events[k])
+        torch.cuda.synchronize()
     else:
         # cold cache: the eviction runs between steps and stays outside the timed sum, which adds up the
-        # GPU time of each step (event before the router to event after the out-projection)
+        # GPU time of each step (event before the router to event after the last phase)
         for k in range(args.steps):
             flush.sum()
-            step(events[k])
+            step(ev=events[k])
         torch.cuda.synchronize()
-        elapsed = sum(e[0].elapsed_time(e[3]) for e in events) * 1e-3
+        elapsed = sum(e[0].elapsed_time(e[-1]) for e in events) * 1e-3
+        t_in_timed = None
 
-    t_route = np.array([e[0].elapsed_time(e[1]) for e in events]) * 1e-3
-    t_in = np.array([e[1].elapsed_time(e[2]) for e in events]) * 1e-3
-    t_out = np.array([e[2].elapsed_time(e[3]) for e in events]) * 1e-3
+    t_ph = {ph: np.array([e[i].elapsed_time(e[i + 1]) for e in events]) * 1e-3 for i, ph in enumerate(phases)}
+    t_route, t_in = t_ph["route"], (t_in_timed if t_in_timed is not None else t_ph["in"])
+    t_out = t_ph.get("out", np.zeros(1))
     # the in-projection's output width: Conv + Gate (2 * d_inner) for RoM, d_out for Swimba
     n_in = w.dout if swimba else 2 * w.d_inner
     fl_in = 2.0 * w.T * w.d_model * n_in * w.top_k
@@ -207,6 +246,7 @@ def main() -> int:
     bytes_in = es * (w.T * w.d_model + used * n_in * w.d_model + w.T * n_in)
     bytes_out = 0 if swimba else es * (2 * w.T * w.d_inner + used * w.d_model * w.d_inner + w.T * w.d_model) + 4 * w.T * 2
     bytes_route = es * w.T * w.d_model + 4 * w.d_model * w.E + 4 * w.T * 4
+    bytes_conv = es * (2 * w.T * w.d_inner + (CONV_WIDTH + 1) * w.d_inner)
     ms_per_step = elapsed / args.steps * 1e3
     mean_in, mean_out, mean_route = float(t_in.mean()), float(t_out.mean()), float(t_route.mean())
 
@@ -233,6 +273,8 @@ def main() -> int:
               "expert_loads": counts[0].tolist() if w.top_k == 1 else counts.tolist()}
     if swimba:
         config["d_out"] = w.dout
+    if conv:
+        config["conv1d"] = {"width": CONV_WIDTH, "activation": "silu", "bias": True, "n_seq": w.n_seq}
     result = {
         "metric": METRIC,
         "value": round(w.T * args.steps / elapsed, 1),
@@ -263,8 +305,13 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    if conv:
+        mean_conv = float(t_ph["conv"].mean())
+        result["breakdown"]["conv1d_us"] = round(mean_conv * 1e6, 2)
+        result["breakdown"]["conv1d_gbs"] = round(bytes_conv / mean_conv / 1e9, 1)
+        result["breakdown"]["conv1d_hbm_frac"] = round(bytes_conv / mean_conv / 1e9 / PEAK_HBM_GBS, 4)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_seconds, conv)
     print(json.dumps(result), flush=True)
     return 0
 

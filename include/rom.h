@@ -40,13 +40,14 @@
 extern "C" {
 #endif
 
-#define ROM_ABI_VERSION 4
+#define ROM_ABI_VERSION 5
 #ifndef ROM_API
 #define ROM_API __attribute__((visibility("default")))
 #endif
 #define ROM_MAX_EXPERTS 64
 #define ROM_MAX_TOP_K 2
 #define ROM_MAX_TOKENS (1 << 24)
+#define ROM_MAX_CONV_WIDTH 8
 
 typedef enum {
     ROM_OK = 0,
@@ -57,6 +58,8 @@ typedef enum {
 } rom_status;
 
 typedef enum { ROM_DTYPE_F32 = 0, ROM_DTYPE_BF16 = 1 } rom_dtype;
+
+typedef enum { ROM_ACT_NONE = 0, ROM_ACT_SILU = 1 } rom_activation;
 
 /*
  * The routing decision of one block for T tokens (Knowl 1: S_t and r_t,i), plus the grouping that the
@@ -135,6 +138,25 @@ ROM_API rom_status rom_in_proj(const void *X, const rom_routing *routing, rom_dt
  */
 ROM_API rom_status rom_in_proj_weighted(const void *X, const rom_routing *routing, rom_dtype dtype, int32_t T,
                                 int32_t d_model, int32_t d_out, const void *W_in, void *y_out, void *stream);
+
+/*
+ * The shared short causal convolution between the in-projection and the selective SSM (Knowl 1: the
+ * short convolution applied to H_t; Knowl 9: shared across experts, not expertized). The page fixes no
+ * width, bias or activation; this call takes a depthwise causal convolution of each sequence:
+ *   u[b][t][c] = bias[c] + sum_{j<width} weight[c][j] * x[b][t - (width-1) + j][c]
+ *   y[b][t][c] = activation == ROM_ACT_SILU ? SiLU(u) : u
+ * with x at times before a sequence's first token taken as zero (sequences never mix), so
+ * weight[c][width-1] multiplies the current token. Accumulation is fp32 in the order bias, oldest tap
+ * first; y is rounded once to dtype.
+ *   x, y      [n_seq][seq_len][channels] dtype, token order (x is rom_in_proj's x_out when
+ *             n_seq * seq_len = T); y may not overlap x
+ *   weight    [channels][width] dtype;  bias [channels] dtype or NULL (16-byte aligned)
+ *   width     1 .. ROM_MAX_CONV_WIDTH;  channels a multiple of 64;  activation ROM_ACT_NONE or ROM_ACT_SILU
+ * n_seq * seq_len == 0 is a no-op.
+ */
+ROM_API rom_status rom_conv1d(const void *x, rom_dtype dtype, int32_t n_seq, int32_t seq_len, int32_t channels,
+                      const void *weight, const void *bias, int32_t width, int32_t activation, void *y,
+                      void *stream);
 
 /* Bytes of device workspace rom_out_proj needs (T * d_inner bf16 values for bf16 data; 0 for fp32 data). */
 ROM_API size_t rom_out_proj_workspace_bytes(int32_t T, int32_t d_inner, rom_dtype dtype);

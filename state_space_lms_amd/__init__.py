@@ -22,15 +22,16 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["route", "in_proj", "in_proj_weighted", "out_proj", "Routing", "RomError", "lib", "LIB_PATH", "ABI_VERSION",
+__all__ = ["route", "in_proj", "in_proj_weighted", "out_proj", "conv1d", "Routing", "RomError", "lib", "LIB_PATH", "ABI_VERSION",
            "route_workspace_bytes", "out_proj_workspace_bytes"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "librom.so")
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 ROM_OK, ROM_ERR_INVALID_ARGUMENT, ROM_ERR_UNSUPPORTED, ROM_ERR_WORKSPACE_TOO_SMALL, ROM_ERR_HIP = range(5)
 ROM_DTYPE_F32, ROM_DTYPE_BF16 = 0, 1
-ABI_SYMBOLS = ("rom_abi_version", "rom_route_workspace_bytes", "rom_route", "rom_in_proj", "rom_in_proj_weighted",
+ROM_ACT_NONE, ROM_ACT_SILU = 0, 1
+ABI_SYMBOLS = ("rom_abi_version", "rom_route_workspace_bytes", "rom_route", "rom_in_proj", "rom_in_proj_weighted", "rom_conv1d",
                "rom_out_proj_workspace_bytes", "rom_out_proj", "rom_status_string", "rom_last_error")
 
 
@@ -71,6 +72,8 @@ def lib(path: str = LIB_PATH) -> ctypes.CDLL:
     L.rom_in_proj_weighted.argtypes = [_vp, ctypes.POINTER(RoutingStruct), ctypes.c_int, _i32, _i32, _i32, _vp, _vp,
                                        _vp]
     L.rom_in_proj_weighted.restype = ctypes.c_int
+    L.rom_conv1d.argtypes = [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _vp]
+    L.rom_conv1d.restype = ctypes.c_int
     L.rom_out_proj_workspace_bytes.argtypes = [_i32, _i32, ctypes.c_int]
     L.rom_out_proj_workspace_bytes.restype = _sz
     L.rom_out_proj.argtypes = [_vp, _vp, ctypes.POINTER(RoutingStruct), ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp,
@@ -207,6 +210,29 @@ def in_proj_weighted(X: torch.Tensor, routing: Routing, W_in: torch.Tensor, y_ou
                                         _ptr(W_in), _ptr(y_out), _stream(X.device, stream))
     _check(status, "rom_in_proj_weighted")
     return y_out
+
+
+def conv1d(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None, n_seq: int = 1,
+           activation: bool = True, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """rom_conv1d: the shared short causal depthwise convolution of each of n_seq sequences of x [T][C]
+    (T = n_seq * seq_len, token order), weight [C][width], optional bias [C], optional SiLU."""
+    _dev(x, "x")
+    _dev(weight, "weight")
+    T, C = x.shape
+    if n_seq <= 0 or T % n_seq != 0:
+        raise ValueError("T must be a multiple of n_seq")
+    if weight.dim() != 2 or weight.shape[0] != C or weight.dtype != x.dtype:
+        raise ValueError("weight must be [C][width] in x's dtype")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.shape != (C,) or bias.dtype != x.dtype:
+            raise ValueError("bias must be [C] in x's dtype")
+    y = torch.empty_like(x) if y is None else _dev(y, "y")
+    status = lib().rom_conv1d(_ptr(x), _dtype_code(x), n_seq, T // n_seq, C, _ptr(weight), _ptr(bias),
+                              weight.shape[1], ROM_ACT_SILU if activation else ROM_ACT_NONE, _ptr(y),
+                              _stream(x.device, stream))
+    _check(status, "rom_conv1d")
+    return y
 
 
 def out_proj_workspace_bytes(T: int, d_inner: int, dtype: torch.dtype) -> int:

@@ -181,6 +181,34 @@ rom_status rom_in_proj_weighted(const void *X, const rom_routing *routing, rom_d
     return ROM_OK;
 }
 
+rom_status rom_conv1d(const void *x, rom_dtype dtype, int32_t n_seq, int32_t seq_len, int32_t channels,
+                      const void *weight, const void *bias, int32_t width, int32_t activation, void *y,
+                      void *stream) {
+    g_last_error[0] = '\0';
+    rom_status s;
+    if ((s = check_dtype(dtype)) != ROM_OK) return s;
+    if (n_seq < 0 || seq_len < 0) return fail(ROM_ERR_INVALID_ARGUMENT, "n_seq = %d, seq_len = %d", n_seq, seq_len);
+    if ((int64_t)n_seq * seq_len > ROM_MAX_TOKENS)
+        return fail(ROM_ERR_UNSUPPORTED, "n_seq * seq_len exceeds ROM_MAX_TOKENS");
+    if ((s = check_dims(0, channels, "channels")) != ROM_OK) return s;
+    if (width < 1 || width > ROM_MAX_CONV_WIDTH)
+        return fail(width < 1 ? ROM_ERR_INVALID_ARGUMENT : ROM_ERR_UNSUPPORTED, "width = %d outside [1, %d]", width,
+                    ROM_MAX_CONV_WIDTH);
+    if (activation != ROM_ACT_NONE && activation != ROM_ACT_SILU)
+        return fail(ROM_ERR_INVALID_ARGUMENT, "unknown activation %d", activation);
+    if ((int64_t)n_seq * seq_len == 0) return ROM_OK;
+    ROM_CHECK_PTR(x, 16);
+    ROM_CHECK_PTR(weight, 16);
+    ROM_CHECK_PTR(y, 16);
+    if (bias != nullptr && !aligned(bias, 16)) return fail(ROM_ERR_INVALID_ARGUMENT, "bias is not 16-byte aligned");
+    const size_t xb = (size_t)n_seq * seq_len * channels * elem_size(dtype);
+    if (overlap(x, xb, y, xb)) return fail(ROM_ERR_INVALID_ARGUMENT, "y overlaps x");
+    hipError_t err = rom::launch_conv1d(x, dtype, n_seq, seq_len, channels, weight, bias, width, activation, y,
+                                        static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, "rom_conv1d launch");
+    return ROM_OK;
+}
+
 size_t rom_out_proj_workspace_bytes(int32_t T, int32_t d_inner, rom_dtype dtype) {
     if (T <= 0 || d_inner <= 0 || (dtype != ROM_DTYPE_F32 && dtype != ROM_DTYPE_BF16)) return 0;
     return rom::out_proj_workspace_bytes(T, d_inner, dtype);

@@ -9,6 +9,7 @@ namespace rom {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -56,8 +57,10 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
     return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
 
-// SiLU(v) = v / (1 + exp(-v)), the sigmoid-weighted linear unit.
+// SiLU(v) = v / (1 + exp(-v)), the sigmoid-weighted linear unit. silu_precise divides and uses the
+// library expf; silu_fast uses the hardware exp2 (v_exp_f32, on v * log2(e)) and reciprocal (v_rcp_f32),
+// about 1 ulp each, for results that are rounded to bf16 afterwards or feed an fp32 sum.
 __device__ __forceinline__ float silu_precise(float v) { return v / (1.0f + expf(-v)); }
-__device__ __forceinline__ float silu_fast(float v) { return v * __frcp_rn(1.0f + __expf(-v)); }
+__device__ __forceinline__ float silu_fast(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
 }  // namespace rom

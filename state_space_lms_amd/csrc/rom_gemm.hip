@@ -174,7 +174,6 @@ __device__ __forceinline__ void acc_to_ctile(const f32x16 (&acc)[FM][FN], uint16
 template <int BN, int NT>
 __device__ __forceinline__ void ctile_to_global(const uint16_t *ct, int nrows, int valid, const int *tok, uint16_t *C,
                                                 int N0, int n0, int tid) {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     constexpr int CPR = BN / 8;
 #pragma unroll 4
     for (int idx = tid; idx < nrows * CPR; idx += NT) {

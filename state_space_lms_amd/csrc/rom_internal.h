@@ -35,6 +35,9 @@ hipError_t launch_out_proj(const void *z, const void *h, const rom_routing &r, r
 hipError_t launch_in_proj_weighted(const void *X, const rom_routing &r, rom_dtype dt, int T, int dm, int dout,
                                    const void *W, void *y, hipStream_t s);
 
+hipError_t launch_conv1d(const void *x, rom_dtype dt, int nseq, int L, int C, const void *w, const void *bias,
+                         int width, int act, void *y, hipStream_t s);
+
 // Workspace bytes the out-projection needs (the gated rows a, T * d_inner bf16 values; 0 for fp32 data).
 size_t out_proj_workspace_bytes(int T, int di, rom_dtype dt);
 

@@ -132,6 +132,25 @@ def test_in_proj_weighted_T0_noop(L):
     assert _inw(L, X=None, T=0, W=None, y=None, r=_routing(0, 4)) == OK
 
 
+def _conv(L, x=A, dt=BF16, ns=4, sl=100, C=256, w=A + (1 << 26), b=None, width=4, act=1, y=A + (1 << 24)):
+    return L.rom_conv1d(x, dt, ns, sl, C, w, b, width, act, y, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ns=-1), INVALID), (dict(sl=-3), INVALID), (dict(C=0), INVALID), (dict(C=96), UNSUPPORTED),
+    (dict(width=0), INVALID), (dict(width=9), UNSUPPORTED), (dict(act=2), INVALID), (dict(dt=5), INVALID),
+    (dict(x=None), INVALID), (dict(w=None), INVALID), (dict(y=None), INVALID), (dict(w=A + 8), INVALID),
+    (dict(b=A + 4), INVALID), (dict(y=A + 1024), INVALID), (dict(ns=4096, sl=4097), UNSUPPORTED),
+])
+def test_conv1d_rejects(L, kw, code):
+    assert _conv(L, **kw) == code
+
+
+def test_conv1d_empty_is_noop(L):
+    assert _conv(L, x=None, w=None, y=None, ns=0) == OK
+    assert _conv(L, x=None, w=None, y=None, sl=0) == OK
+
+
 WS = A + (1 << 28)
 
 

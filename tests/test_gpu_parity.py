@@ -347,3 +347,38 @@ def test_weighted_in_proj_prefill_shape(rom, oracle):
     o_route = oracle.route(inp["X"], inp["W_router"])
     rows = parity.sample_rows(oracle.sort(o_route["ids"], w.E), w.T)
     check_weighted(rom, oracle, w, inp=inp, rows=rows)
+
+
+# ------------------------------------------------------------------------------------------------
+# the shared short causal convolution after the in-projection
+
+CONV = [
+    # (n_seq, seq_len, channels, width, activation, bias, dtype)
+    (2, 37, 64, 4, True, True, "f32"),
+    (3, 100, 192, 4, True, True, "bf16"),
+    (1, 1, 128, 4, True, True, "bf16"),
+    (5, 15, 128, 4, False, False, "bf16"),
+    (2, 16, 320, 3, True, False, "bf16"),
+    (2, 17, 256, 2, False, True, "f32"),
+    (4, 4096, 2048, 4, True, True, "bf16"),    # the Samba-421M-like block: 4 sequences of 4K, d_inner 2048
+    (1, 16384, 4096, 4, True, True, "bf16"),   # the 1.3B-scale block: one 16K sequence, d_inner 4096
+] + [(3, 50, 192, w, True, True, "bf16") for w in (1, 5, 6, 7, 8)]
+
+
+@pytest.mark.parametrize("case", CONV, ids=[f"ns{c[0]}_L{c[1]}_C{c[2]}_w{c[3]}_{'silu' if c[4] else 'lin'}"
+                                              f"{'_b' if c[5] else ''}_{c[6]}" for c in CONV])
+def test_conv1d(rom, oracle, case):
+    import torch
+    ns, L, C, w, act, with_bias, dt = case
+    print(f"[parity conv1d] n_seq={ns} seq_len={L} channels={C} width={w} act={act} bias={with_bias} {dt}",
+          flush=True)
+    inp = workloads.make_conv_inputs(ns, L, C, w, dt, seed=400 + w + L, with_bias=with_bias)
+    x = parity.to_device(inp["x"].reshape(ns * L, C), dt)
+    W = parity.to_device(inp["weight"], dt)
+    b = parity.to_device(inp["bias"], dt) if with_bias else None
+    y = rom.conv1d(x, W, b, n_seq=ns, activation=act)
+    torch.cuda.synchronize()
+    ref = oracle.conv1d(inp["x"], inp["weight"], inp["bias"], activation=act).reshape(ns * L, C)
+    err = parity.norm_max_err(parity.to_host(y), ref)
+    print(f"[parity conv1d]   y={err:.2e}", flush=True)
+    assert err <= parity.TOL[dt], f"conv1d: normalised max error {err:.3g}"

@@ -51,6 +51,7 @@ class Workload:
     top_k: int = 1
     method: str = "rom"   # "rom": routed Conv/Gate/Out projections; "swimba": routing-weighted in-projection
     d_out: Optional[int] = None  # Swimba in-projection width; None means 2 * d_inner
+    n_seq: int = 1        # sequences the T tokens form (the short convolution never crosses one)
 
     @property
     def dout(self) -> int:
@@ -75,17 +76,17 @@ WORKLOADS = {
     "tiny_f32": _tiny(),
     # Samba-421M-like block: per-GPU share of 4 x 4096 tokens, expand=2, 8 experts
     "samba421m": Workload("samba421m", T=16384, d_model=1024, d_inner=2048, E=8, dtype="bf16", seed=2,
-                          x_std=1.0, wr_std=None, w_std=0.02, h_std=1.0, z_std=1.0),
+                          x_std=1.0, wr_std=None, w_std=0.02, h_std=1.0, z_std=1.0, n_seq=4),
     # 1.3B-active-scale block on one 16K-token sequence
     "rom1p3b": Workload("rom1p3b", T=16384, d_model=2048, d_inner=4096, E=8, dtype="bf16", seed=3,
                         x_std=1.0, wr_std=0.02, w_std=0.02, h_std=1.0, z_std=1.0),
     # the same block with top-2 routing (the page's 8top2 setting); same seed, hence the same tensors
     "samba421m_top2": Workload("samba421m_top2", T=16384, d_model=1024, d_inner=2048, E=8, dtype="bf16", seed=2,
-                               x_std=1.0, wr_std=None, w_std=0.02, h_std=1.0, z_std=1.0, top_k=2),
+                               x_std=1.0, wr_std=None, w_std=0.02, h_std=1.0, z_std=1.0, top_k=2, n_seq=4),
     # skewed routing without a balance loss: a router bias gives loads 60/10/10/5/5/5/3/2 %
     "skewed": Workload("skewed", T=65536, d_model=2048, d_inner=4096, E=8, dtype="bf16", seed=4,
                        x_std=1.0, wr_std=0.02, w_std=0.02, h_std=1.0, z_std=1.0,
-                       skew=(0.60, 0.10, 0.10, 0.05, 0.05, 0.05, 0.03, 0.02)),
+                       skew=(0.60, 0.10, 0.10, 0.05, 0.05, 0.05, 0.03, 0.02), n_seq=16),
 }
 
 
@@ -181,6 +182,21 @@ def make_inputs(w: Workload, router_bias: Optional[np.ndarray] = None, which=Non
     if router_bias is None and w.skew is not None:
         router_bias = load_skew_bias(w)
     out["bias"] = None if router_bias is None else np.ascontiguousarray(router_bias, dtype=np.float32)
+    return out
+
+
+def make_conv_inputs(n_seq: int, seq_len: int, channels: int, width: int, dtype: str = "bf16", seed: int = 0,
+                     with_bias: bool = True) -> dict:
+    """Inputs of the shared short causal convolution: x [n_seq][seq_len][channels] ~ N(0, 1) (the Conv
+    projection's output), weight [channels][width] ~ N(0, 1/width), bias [channels] ~ N(0, 0.1^2) or None.
+    Same stream recipe as make_inputs (one PCG64 child stream per tensor)."""
+    children = np.random.SeedSequence(seed).spawn(3)
+    rng = [np.random.Generator(np.random.PCG64(c)) for c in children]
+    out = {
+        "x": _draw(rng[0], (n_seq, seq_len, channels), 1.0, dtype),
+        "weight": _draw(rng[1], (channels, width), float(1.0 / np.sqrt(width)), dtype),
+        "bias": _draw(rng[2], (channels,), 0.1, dtype) if with_bias else None,
+    }
     return out
 
 
