@@ -36,6 +36,7 @@ def build(source: str = SOURCE, output: str = LIBRARY, extra_flags=()) -> str:
 _i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
 _f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
 _f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+_i64p = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
 
@@ -66,6 +67,18 @@ class Oracle:
         lib.orom_in_proj_weighted.restype = None
         lib.orom_conv1d.argtypes = [_f32p, _i64, _i64, _i64, _f32p, ctypes.c_void_p, _i32, _i32, _f64p]
         lib.orom_conv1d.restype = None
+        lib.orom_out_proj_dgrad.argtypes = [_f32p, _f64p, _f32p, _i64, _i64, _i64, _i32p, _f32p, _i32, _f32p, _i32,
+                                            _f64p, _f64p]
+        lib.orom_out_proj_wgrad.argtypes = [_f32p, _f64p, _f32p, _i64, _i64, _i64, _i32p, _f32p, _i32, _i32, _f64p]
+        lib.orom_out_proj_wgrad_entries.argtypes = [_f32p, _f64p, _f32p, _i64, _i64, _i64, _i32p, _f32p, _i32, _i64p,
+                                                    _i64, _f64p]
+        lib.orom_in_proj_dgrad.argtypes = [_f32p, _f32p, _i64, _i64, _i64, _i32p, _i32, _f32p, _f32p, _i32, _f64p]
+        lib.orom_in_proj_wgrad.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i32p, _i32, _i32, _f64p, _f64p]
+        lib.orom_in_proj_wgrad_entries.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i32p, _i32, _i64p, _i64,
+                                                   _f64p, _f64p]
+        for f in ("orom_out_proj_dgrad", "orom_out_proj_wgrad", "orom_out_proj_wgrad_entries", "orom_in_proj_dgrad",
+                  "orom_in_proj_wgrad", "orom_in_proj_wgrad_entries"):
+            getattr(lib, f).restype = None
         self.lib = lib
 
     def threads(self) -> int:
@@ -174,6 +187,88 @@ class Oracle:
         self.lib.orom_conv1d(H, nseq, L, C, W, None if b is None else b.ctypes.data, W.shape[1],
                              1 if activation else 0, y)
         return y
+
+    # -- backward ---------------------------------------------------------------------------------
+    # Gradients of the routed projections with the router probabilities held fixed.
+
+    @staticmethod
+    def _out_args(g, z, h, ids, prob):
+        g = np.ascontiguousarray(g, dtype=np.float32)
+        z = np.ascontiguousarray(z, dtype=np.float64)
+        h = np.ascontiguousarray(h, dtype=np.float32)
+        n, di = z.shape
+        ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(n, -1)
+        prob = np.ascontiguousarray(prob, dtype=np.float32).reshape(n, -1)
+        assert h.shape == z.shape and g.shape[0] == n and prob.shape == ids.shape
+        return g, z, h, ids, prob, n, di, g.shape[1]
+
+    def out_proj_dgrad(self, g, z, h, ids, prob, W_out):
+        """dz, dh [n][d_inner] (float64) of out = sum_s prob * W_out[ids] (SiLU(z) * h) for upstream g [n][d_model]."""
+        g, z, h, ids, prob, n, di, dm = self._out_args(g, z, h, ids, prob)
+        Wo = np.ascontiguousarray(W_out, dtype=np.float32)
+        E = Wo.shape[0]
+        assert Wo.shape == (E, dm, di) and (ids.size == 0 or (ids.min() >= 0 and ids.max() < E))
+        dz = np.empty((n, di), np.float64)
+        dh = np.empty((n, di), np.float64)
+        self.lib.orom_out_proj_dgrad(g, z, h, n, di, dm, ids, prob, ids.shape[1], Wo, E, dz, dh)
+        return dz, dh
+
+    def out_proj_wgrad(self, g, z, h, ids, prob, E: int):
+        """dW_out [E][d_model][d_inner] (float64), summed over the given tokens."""
+        g, z, h, ids, prob, n, di, dm = self._out_args(g, z, h, ids, prob)
+        dW = np.empty((E, dm, di), np.float64)
+        self.lib.orom_out_proj_wgrad(g, z, h, n, di, dm, ids, prob, ids.shape[1], E, dW)
+        return dW
+
+    def out_proj_wgrad_entries(self, g, z, h, ids, prob, entries):
+        """dW_out[e][m][c] for each (e, m, c) row of entries."""
+        g, z, h, ids, prob, n, di, dm = self._out_args(g, z, h, ids, prob)
+        ent = np.ascontiguousarray(entries, dtype=np.int64).reshape(-1, 3)
+        out = np.empty((ent.shape[0],), np.float64)
+        self.lib.orom_out_proj_wgrad_entries(g, z, h, n, di, dm, ids, prob, ids.shape[1], ent, ent.shape[0], out)
+        return out
+
+    @staticmethod
+    def _in_args(X, dx, dz, ids):
+        X = np.ascontiguousarray(X, dtype=np.float32)
+        dx = np.ascontiguousarray(dx, dtype=np.float32)
+        dz = np.ascontiguousarray(dz, dtype=np.float32)
+        n, dm = X.shape
+        ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(n, -1)
+        assert dx.shape == dz.shape and dx.shape[0] == n
+        return X, dx, dz, ids, n, dm, dx.shape[1]
+
+    def in_proj_dgrad(self, dx, dz, ids, W_conv, W_gate):
+        """dX [n][d_model] (float64) of x = sum_s W_conv[ids] X, z = sum_s W_gate[ids] X for upstream dx, dz."""
+        dx = np.ascontiguousarray(dx, dtype=np.float32)
+        dz = np.ascontiguousarray(dz, dtype=np.float32)
+        n, di = dx.shape
+        ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(n, -1)
+        Wc = np.ascontiguousarray(W_conv, dtype=np.float32)
+        Wg = np.ascontiguousarray(W_gate, dtype=np.float32)
+        E, di2, dm = Wc.shape
+        assert di2 == di and Wg.shape == Wc.shape and dz.shape == dx.shape
+        assert ids.size == 0 or (ids.min() >= 0 and ids.max() < E)
+        dX = np.empty((n, dm), np.float64)
+        self.lib.orom_in_proj_dgrad(dx, dz, n, dm, di, ids, ids.shape[1], Wc, Wg, E, dX)
+        return dX
+
+    def in_proj_wgrad(self, X, dx, dz, ids, E: int):
+        """dW_conv, dW_gate [E][d_inner][d_model] (float64), summed over the given tokens."""
+        X, dx, dz, ids, n, dm, di = self._in_args(X, dx, dz, ids)
+        dWc = np.empty((E, di, dm), np.float64)
+        dWg = np.empty((E, di, dm), np.float64)
+        self.lib.orom_in_proj_wgrad(X, dx, dz, n, dm, di, ids, ids.shape[1], E, dWc, dWg)
+        return dWc, dWg
+
+    def in_proj_wgrad_entries(self, X, dx, dz, ids, entries):
+        """(dW_conv[e][c][k], dW_gate[e][c][k]) for each (e, c, k) row of entries."""
+        X, dx, dz, ids, n, dm, di = self._in_args(X, dx, dz, ids)
+        ent = np.ascontiguousarray(entries, dtype=np.int64).reshape(-1, 3)
+        oc = np.empty((ent.shape[0],), np.float64)
+        og = np.empty((ent.shape[0],), np.float64)
+        self.lib.orom_in_proj_wgrad_entries(X, dx, dz, n, dm, di, ids, ids.shape[1], ent, ent.shape[0], oc, og)
+        return oc, og
 
     # -- the whole routed path for a subset of tokens --------------------------------------------
     def forward_rows(self, inp: dict, rows: Optional[np.ndarray] = None, top_k: int = 1, routed=None):

@@ -293,3 +293,137 @@ void orom_conv1d(const float *H, int64_t nseq, int64_t L, int64_t C, const float
         }
     }
 }
+
+/* ---------------------------------------------------------------------------
+ * Backward of the routed projections: the exact derivatives of Knowl 1's
+ * H_t, G_t (pre-activation z) and O_t with respect to their inputs and expert
+ * weights, for n tokens. The router's probabilities are treated as given (the
+ * gradient that reaches the router through p, and through the selection S_t,
+ * is not computed here).
+ *
+ * Out-projection, with g = dL/dout [n][dm] and a = SiLU(z) * h:
+ *   da[t][c]      = sum_{s<K} prob[t][s] * sum_m Wo[ids[t][s]][m][c] * g[t][m]
+ *   dz[t][c]      = da[t][c] * h[t][c] * SiLU'(z[t][c]),
+ *                   SiLU'(v) = sig(v) * (1 + v * (1 - sig(v))), sig(v) = 1 / (1 + exp(-v))
+ *   dh[t][c]      = da[t][c] * SiLU(z[t][c])
+ *   dWo[i][m][c]  = sum over (t, s) with ids[t][s] = i of prob[t][s] * g[t][m] * a[t][c]
+ */
+void orom_out_proj_dgrad(const float *g, const double *z, const float *h, int64_t n, int64_t di, int64_t dm,
+                         const int32_t *ids, const float *prob, int32_t K, const float *Wo, int32_t E,
+                         double *dz, double *dh)
+{
+    (void)E;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        for (int64_t c = 0; c < di; ++c) {
+            double da = 0.0;
+            for (int32_t s = 0; s < K; ++s) {
+                const int64_t i = ids[t * K + s];
+                double col = 0.0;
+                for (int64_t m = 0; m < dm; ++m)
+                    col += (double)Wo[(i * dm + m) * di + c] * (double)g[t * dm + m];
+                da += (double)prob[t * K + s] * col;
+            }
+            const double v = z[t * di + c];
+            const double sg = 1.0 / (1.0 + exp(-v));
+            dz[t * di + c] = da * (double)h[t * di + c] * (sg * (1.0 + v * (1.0 - sg)));
+            dh[t * di + c] = da * (v * sg);
+        }
+    }
+}
+
+/* One weight-gradient entry dWo[i][m][c], summed over the tokens in ascending order. */
+static double out_wgrad_entry(const float *g, const double *z, const float *h, int64_t n, int64_t di, int64_t dm,
+                              const int32_t *ids, const float *prob, int32_t K, int64_t i, int64_t m, int64_t c)
+{
+    double acc = 0.0;
+    for (int64_t t = 0; t < n; ++t)
+        for (int32_t s = 0; s < K; ++s) {
+            if (ids[t * K + s] != i) continue;
+            const double v = z[t * di + c];
+            const double a = v / (1.0 + exp(-v)) * (double)h[t * di + c];
+            acc += (double)prob[t * K + s] * (double)g[t * dm + m] * a;
+        }
+    return acc;
+}
+
+/* The full dWo [E][dm][di]. */
+void orom_out_proj_wgrad(const float *g, const double *z, const float *h, int64_t n, int64_t di, int64_t dm,
+                         const int32_t *ids, const float *prob, int32_t K, int32_t E, double *dWo)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t q = 0; q < (int64_t)E * dm * di; ++q) {
+        const int64_t i = q / (dm * di), m = (q / di) % dm, c = q % di;
+        dWo[q] = out_wgrad_entry(g, z, h, n, di, dm, ids, prob, K, i, m, c);
+    }
+}
+
+/* Selected entries: entry j is dWo[ent[3j]][ent[3j+1]][ent[3j+2]]. */
+void orom_out_proj_wgrad_entries(const float *g, const double *z, const float *h, int64_t n, int64_t di,
+                                 int64_t dm, const int32_t *ids, const float *prob, int32_t K, const int64_t *ent,
+                                 int64_t nent, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < nent; ++j)
+        out[j] = out_wgrad_entry(g, z, h, n, di, dm, ids, prob, K, ent[3 * j], ent[3 * j + 1], ent[3 * j + 2]);
+}
+
+/* In-projection, with dx = dL/dH and dzg = dL/dz (the pre-activation gate):
+ *   dX[t][k]       = sum_{s<K} sum_c (Wc[ids[t][s]][c][k] * dx[t][c] + Wg[ids[t][s]][c][k] * dzg[t][c])
+ *   dWc[i][c][k]   = sum over (t, s) with ids[t][s] = i of dx[t][c] * X[t][k]   (dWg likewise with dzg)
+ * (the indicator 1[i in S_t] carries no probability, so neither does its derivative).
+ */
+void orom_in_proj_dgrad(const float *dx, const float *dzg, int64_t n, int64_t dm, int64_t di, const int32_t *ids,
+                        int32_t K, const float *Wc, const float *Wg, int32_t E, double *dX)
+{
+    (void)E;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        for (int64_t k = 0; k < dm; ++k) {
+            double acc = 0.0;
+            for (int32_t s = 0; s < K; ++s) {
+                const int64_t i = ids[t * K + s];
+                for (int64_t c = 0; c < di; ++c)
+                    acc += (double)Wc[(i * di + c) * dm + k] * (double)dx[t * di + c]
+                         + (double)Wg[(i * di + c) * dm + k] * (double)dzg[t * di + c];
+            }
+            dX[t * dm + k] = acc;
+        }
+    }
+}
+
+/* One entry of dWc (gate = 0) or dWg (gate = 1) [i][c][k], summed over the tokens in ascending order. */
+static double in_wgrad_entry(const float *X, const float *dy, int64_t n, int64_t dm, int64_t di,
+                             const int32_t *ids, int32_t K, int64_t i, int64_t c, int64_t k)
+{
+    double acc = 0.0;
+    for (int64_t t = 0; t < n; ++t)
+        for (int32_t s = 0; s < K; ++s) {
+            if (ids[t * K + s] != i) continue;
+            acc += (double)dy[t * di + c] * (double)X[t * dm + k];
+        }
+    return acc;
+}
+
+void orom_in_proj_wgrad(const float *X, const float *dx, const float *dzg, int64_t n, int64_t dm, int64_t di,
+                        const int32_t *ids, int32_t K, int32_t E, double *dWc, double *dWg)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t q = 0; q < (int64_t)E * di * dm; ++q) {
+        const int64_t i = q / (di * dm), c = (q / dm) % di, k = q % dm;
+        dWc[q] = in_wgrad_entry(X, dx, n, dm, di, ids, K, i, c, k);
+        dWg[q] = in_wgrad_entry(X, dzg, n, dm, di, ids, K, i, c, k);
+    }
+}
+
+/* Selected entries (i, c, k) of dWc and dWg. */
+void orom_in_proj_wgrad_entries(const float *X, const float *dx, const float *dzg, int64_t n, int64_t dm,
+                                int64_t di, const int32_t *ids, int32_t K, const int64_t *ent, int64_t nent,
+                                double *outc, double *outg)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < nent; ++j) {
+        outc[j] = in_wgrad_entry(X, dx, n, dm, di, ids, K, ent[3 * j], ent[3 * j + 1], ent[3 * j + 2]);
+        outg[j] = in_wgrad_entry(X, dzg, n, dm, di, ids, K, ent[3 * j], ent[3 * j + 1], ent[3 * j + 2]);
+    }
+}

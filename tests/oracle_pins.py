@@ -338,6 +338,125 @@ def pin_conv1d(orc):
     assert np.all(c3[1, 6] != a[1, 6])
 
 
+def _dyadic(rng, shape, scale=8):
+    """Small dyadic values k / scale, k in [-8, 8]: sums and differences of them are exact in float32."""
+    return (rng.integers(-8, 9, size=shape) / scale).astype(np.float32)
+
+
+def _dsilu64(v):
+    s = expit(v)
+    return s * (1.0 + v * (1.0 - s))
+
+
+def pin_out_proj_backward(orc):
+    """Gradients of the out-projection (Knowl 1, O_t) with the router probabilities held fixed."""
+    rng = np.random.default_rng(18)
+    for (T, dm, di, E, K) in [(20, 12, 16, 3, 1), (14, 8, 10, 5, 2)]:
+        _, _, _, Wo, h, ids, prob = _proj_case(rng, T, dm, di, E, K)
+        z = rng.standard_normal((T, di)) * 2
+        g = _rand(rng, (T, dm))
+        dz, dh = orc.out_proj_dgrad(g, z, h, ids, prob, Wo)
+        dW = orc.out_proj_wgrad(g, z, h, ids, prob, E)
+        # per-token float64 brute force
+        zb, hb, dWb = np.zeros((T, di)), np.zeros((T, di)), np.zeros((E, dm, di))
+        for t in range(T):
+            a = _silu64(z[t]) * h[t].astype(np.float64)
+            da = np.zeros(di)
+            for s in range(K):
+                e = ids[t, s]
+                da += float(prob[t, s]) * (Wo[e].astype(np.float64).T @ g[t].astype(np.float64))
+                dWb[e] += float(prob[t, s]) * np.outer(g[t].astype(np.float64), a)
+            zb[t] = da * h[t] * _dsilu64(z[t])
+            hb[t] = da * _silu64(z[t])
+        np.testing.assert_allclose(dz, zb, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(dh, hb, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(dW, dWb, rtol=1e-11, atol=1e-12)
+        ent = np.array([[e, m, c] for e in range(E) for m in (0, dm - 1) for c in (0, di // 2)])
+        np.testing.assert_array_equal(orc.out_proj_wgrad_entries(g, z, h, ids, prob, ent), dW[tuple(ent.T)])
+    # directional derivatives of L = <g, out> computed by the forward oracle: a central difference in z
+    # (smooth, float64 input), and exact differences in h and W_out, in which L is linear (dyadic values
+    # keep h +- U and W +- V exact in float32)
+    T, dm, di, E, K = 9, 6, 8, 3, 2
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    prob = (rng.integers(1, 8, size=(T, K)) / 8).astype(np.float32)
+    Wo, V = _dyadic(rng, (E, dm, di)), _dyadic(rng, (E, dm, di), 16)
+    h, U = _dyadic(rng, (T, di)), _dyadic(rng, (T, di), 16)
+    g = _dyadic(rng, (T, dm))
+    z = rng.standard_normal((T, di))
+    Vz = rng.standard_normal((T, di))
+    L = lambda z_, h_, W_: float(np.sum(g.astype(np.float64) * orc.out_proj(z_, h_, ids, prob, W_)))
+    dz, dh = orc.out_proj_dgrad(g, z, h, ids, prob, Wo)
+    dW = orc.out_proj_wgrad(g, z, h, ids, prob, E)
+    eps = 1e-5
+    fd = (L(z + eps * Vz, h, Wo) - L(z - eps * Vz, h, Wo)) / (2 * eps)
+    assert abs(fd - np.sum(dz * Vz)) <= 1e-7 * (1 + abs(fd)), (fd, np.sum(dz * Vz))
+    fd = (L(z, h + U, Wo) - L(z, h - U, Wo)) / 2
+    assert abs(fd - np.sum(dh * U)) <= 1e-10 * (1 + abs(fd)), (fd, np.sum(dh * U))
+    fd = (L(z, h, Wo + V) - L(z, h, Wo - V)) / 2
+    assert abs(fd - np.sum(dW * V)) <= 1e-10 * (1 + abs(fd)), (fd, np.sum(dW * V))
+    # E = 1 with p = 1: a dense layer, dW = g^T a (BLAS) and da = g W
+    _, _, _, Wo, h, _, _ = _proj_case(rng, 17, 10, 12, 1, 1)
+    z = rng.standard_normal((17, 12))
+    g = _rand(rng, (17, 10))
+    one, zero = np.ones((17, 1), np.float32), np.zeros((17, 1), np.int32)
+    a = _silu64(z) * h.astype(np.float64)
+    np.testing.assert_allclose(orc.out_proj_wgrad(g, z, h, zero, one, 1)[0], g.astype(np.float64).T @ a,
+                               rtol=1e-11, atol=1e-12)
+    _, dh = orc.out_proj_dgrad(g, z, h, zero, one, Wo)
+    np.testing.assert_allclose(dh, (g.astype(np.float64) @ Wo[0].astype(np.float64)) * _silu64(z), rtol=1e-11,
+                               atol=1e-12)
+
+
+def pin_in_proj_backward(orc):
+    """Gradients of the in-projections (Knowl 1, H_t and the argument of SiLU in G_t)."""
+    rng = np.random.default_rng(19)
+    for (T, dm, di, E, K) in [(20, 12, 16, 3, 1), (14, 8, 10, 5, 2)]:
+        X, Wc, Wg, _, _, ids, _ = _proj_case(rng, T, dm, di, E, K)
+        dx, dz = _rand(rng, (T, di)), _rand(rng, (T, di))
+        dX = orc.in_proj_dgrad(dx, dz, ids, Wc, Wg)
+        dWc, dWg = orc.in_proj_wgrad(X, dx, dz, ids, E)
+        Xb, Wcb, Wgb = np.zeros((T, dm)), np.zeros((E, di, dm)), np.zeros((E, di, dm))
+        for t in range(T):
+            for s in range(K):
+                e = ids[t, s]
+                Xb[t] += Wc[e].astype(np.float64).T @ dx[t] + Wg[e].astype(np.float64).T @ dz[t]
+                Wcb[e] += np.outer(dx[t].astype(np.float64), X[t])
+                Wgb[e] += np.outer(dz[t].astype(np.float64), X[t])
+        np.testing.assert_allclose(dX, Xb, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(dWc, Wcb, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(dWg, Wgb, rtol=1e-11, atol=1e-12)
+        ent = np.array([[e, c, k] for e in range(E) for c in (0, di - 1) for k in (1, dm // 2)])
+        oc, og = orc.in_proj_wgrad_entries(X, dx, dz, ids, ent)
+        np.testing.assert_array_equal(oc, dWc[tuple(ent.T)])
+        np.testing.assert_array_equal(og, dWg[tuple(ent.T)])
+    # L = <dx, x> + <dz, z> from the forward oracle is linear in X, W_conv and W_gate: exact differences
+    T, dm, di, E, K = 11, 6, 8, 4, 2
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    X, U = _dyadic(rng, (T, dm)), _dyadic(rng, (T, dm), 16)
+    Wc, Vc = _dyadic(rng, (E, di, dm)), _dyadic(rng, (E, di, dm), 16)
+    Wg, Vg = _dyadic(rng, (E, di, dm)), _dyadic(rng, (E, di, dm), 16)
+    dx, dz = _dyadic(rng, (T, di)), _dyadic(rng, (T, di))
+
+    def L(X_, Wc_, Wg_):
+        x, z = orc.in_proj(X_, ids, Wc_, Wg_)
+        return float(np.sum(dx * x) + np.sum(dz * z))
+    dX = orc.in_proj_dgrad(dx, dz, ids, Wc, Wg)
+    dWc, dWg = orc.in_proj_wgrad(X, dx, dz, ids, E)
+    for fd, an in (((L(X + U, Wc, Wg) - L(X - U, Wc, Wg)) / 2, np.sum(dX * U)),
+                   ((L(X, Wc + Vc, Wg) - L(X, Wc - Vc, Wg)) / 2, np.sum(dWc * Vc)),
+                   ((L(X, Wc, Wg + Vg) - L(X, Wc, Wg - Vg)) / 2, np.sum(dWg * Vg))):
+        assert abs(fd - an) <= 1e-10 * (1 + abs(fd)), (fd, an)
+    # E = 1: a dense layer, dX = dx W_conv + dz W_gate and dW_conv = dx^T X (BLAS)
+    X, Wc, Wg, _, _, _, _ = _proj_case(rng, 15, 10, 12, 1, 1)
+    dx, dz = _rand(rng, (15, 12)), _rand(rng, (15, 12))
+    zero = np.zeros((15, 1), np.int32)
+    np.testing.assert_allclose(orc.in_proj_dgrad(dx, dz, zero, Wc, Wg),
+                               dx.astype(np.float64) @ Wc[0] + dz.astype(np.float64) @ Wg[0], rtol=1e-11, atol=1e-12)
+    dWc, dWg = orc.in_proj_wgrad(X, dx, dz, zero, 1)
+    np.testing.assert_allclose(dWc[0], dx.astype(np.float64).T @ X, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dWg[0], dz.astype(np.float64).T @ X, rtol=1e-11, atol=1e-12)
+
+
 # ------------------------------------------------------------------------------------------------
 # hand-worked example
 
@@ -406,4 +525,4 @@ def pin_handworked(orc):
 
 
 ALL_PINS = [pin_router_bruteforce, pin_router_special, pin_sort, pin_in_proj, pin_out_proj, pin_in_proj_weighted,
-            pin_conv1d, pin_handworked]
+            pin_conv1d, pin_out_proj_backward, pin_in_proj_backward, pin_handworked]

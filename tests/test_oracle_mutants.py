@@ -56,6 +56,19 @@ MUTANTS = [
     ("conv1d_silu_sign", [("y[bt * C + c] = act ? u / (1.0 + exp(-u)) : u;", "y[bt * C + c] = act ? u / (1.0 + exp(u)) : u;")]),
     ("conv1d_drops_oldest_tap", [("for (int32_t j = 0; j < w; ++j) {\n                const int64_t s",
                                   "for (int32_t j = 1; j < w; ++j) {\n                const int64_t s")]),
+    ("dsilu_drops_second_term", [("(sg * (1.0 + v * (1.0 - sg)))", "(sg)")]),
+    ("dh_uses_z_not_silu", [("dh[t * di + c] = da * (v * sg);", "dh[t * di + c] = da * v;")]),
+    ("out_dgrad_unscaled", [("da += (double)prob[t * K + s] * col;", "da += col;")]),
+    ("out_dgrad_transposed_weight", [("col += (double)Wo[(i * dm + m) * di + c] * (double)g[t * dm + m];",
+                                      "col += (double)Wo[(i * di + c) * dm + m] * (double)g[t * dm + m];")]),
+    ("out_wgrad_unscaled", [("acc += (double)prob[t * K + s] * (double)g[t * dm + m] * a;",
+                             "acc += (double)g[t * dm + m] * a;")]),
+    ("in_dgrad_drops_gate", [("acc += (double)Wc[(i * di + c) * dm + k] * (double)dx[t * di + c]\n"
+                              "                         + (double)Wg[(i * di + c) * dm + k] * (double)dzg[t * di + c];",
+                              "acc += (double)Wc[(i * di + c) * dm + k] * (double)dx[t * di + c];")]),
+    ("in_wgrad_gate_uses_dx", [("dWg[q] = in_wgrad_entry(X, dzg,", "dWg[q] = in_wgrad_entry(X, dx,")]),
+    ("in_wgrad_transposed", [("acc += (double)dy[t * di + c] * (double)X[t * dm + k];",
+                              "acc += (double)dy[t * di + k % di] * (double)X[t * dm + c % dm];")]),
 ]
 
 
