@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define ROM_ABI_VERSION 5
+#define ROM_ABI_VERSION 6
 #ifndef ROM_API
 #define ROM_API __attribute__((visibility("default")))
 #endif
@@ -157,6 +157,48 @@ ROM_API rom_status rom_in_proj_weighted(const void *X, const rom_routing *routin
 ROM_API rom_status rom_conv1d(const void *x, rom_dtype dtype, int32_t n_seq, int32_t seq_len, int32_t channels,
                       const void *weight, const void *bias, int32_t width, int32_t activation, void *y,
                       void *stream);
+
+/*
+ * Backward of the routed projections: the exact derivatives of Knowl 1's H_t, G_t and O_t (the
+ * forward entry points above) with the router probabilities held fixed, for bf16 data (fp32
+ * accumulation). The gradient that reaches the router through p_t,e or through the selection S_t is
+ * not computed (the page's training recipe handles the router separately). Weight gradients are
+ * written (not accumulated) in fp32, in the weights' [E][out][in] layout; an expert that received no
+ * token gets zeros. Both calls need a caller-provided device workspace of at least
+ * rom_backward_workspace_bytes(T, d_model, d_inner, E, top_k) bytes, 256-byte aligned, whose contents
+ * on entry do not matter (the transposed weight stacks and token-contiguous copies of the operands
+ * are built there). Outputs may not overlap the inputs, the workspace or each other.
+ */
+ROM_API size_t rom_backward_workspace_bytes(int32_t T, int32_t d_model, int32_t d_inner, int32_t E, int32_t top_k);
+
+/*
+ * Out-projection backward. With g = d_out (dL/dout [T][d_model]) and a = SiLU(z) * h:
+ *   da[t]     = sum_{e in S_t} p_t,e * W_out[e]^T g[t]            (accumulated in fp32, rounded to bf16)
+ *   dz[t][n]  = da[t][n] * h[t][n] * SiLU'(z[t][n]),  SiLU'(v) = s (1 + v (1 - s)), s = sigmoid(v)
+ *   dh[t][n]  = da[t][n] * SiLU(z[t][n])
+ *   dW_out[e] = sum over the tokens t with e in S_t of p_t,e * g[t] a[t]^T   (a rounded to bf16, as in
+ *               the forward)
+ *   d_out [T][d_model], z, h, dz, dh [T][d_inner], W_out [E][d_model][d_inner] bf16; dW_out
+ *   [E][d_model][d_inner] fp32.
+ */
+ROM_API rom_status rom_out_proj_backward(const void *d_out, const void *z, const void *h, const rom_routing *routing,
+                                 rom_dtype dtype, int32_t T, int32_t d_model, int32_t d_inner, const void *W_out,
+                                 void *dz, void *dh, float *dW_out, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/*
+ * In-projection backward. With dx = dL/dx_out and dz = dL/dz_out (the pre-activation gate, as
+ * rom_out_proj_backward returns it):
+ *   dX[t]      = sum_{e in S_t} (W_conv[e]^T dx[t] + W_gate[e]^T dz[t])   (one fp32 sum per choice; the
+ *                choices are added in the order k = 0, 1 as in the forward)
+ *   dW_conv[e] = sum over the tokens t with e in S_t of dx[t] X[t]^T;  dW_gate[e] likewise with dz
+ *   X, dX [T][d_model], dx, dz [T][d_inner], W_conv, W_gate [E][d_inner][d_model] bf16; dW_conv,
+ *   dW_gate [E][d_inner][d_model] fp32.
+ */
+ROM_API rom_status rom_in_proj_backward(const void *X, const void *dx, const void *dz, const rom_routing *routing,
+                                rom_dtype dtype, int32_t T, int32_t d_model, int32_t d_inner, const void *W_conv,
+                                const void *W_gate, void *dX, float *dW_conv, float *dW_gate, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace rom_out_proj needs (T * d_inner bf16 values for bf16 data; 0 for fp32 data). */
 ROM_API size_t rom_out_proj_workspace_bytes(int32_t T, int32_t d_inner, rom_dtype dtype);

@@ -22,16 +22,18 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["route", "in_proj", "in_proj_weighted", "out_proj", "conv1d", "Routing", "RomError", "lib", "LIB_PATH", "ABI_VERSION",
+__all__ = ["route", "in_proj", "in_proj_weighted", "out_proj", "conv1d", "out_proj_backward", "in_proj_backward",
+           "backward_workspace_bytes", "Routing", "RomError", "lib", "LIB_PATH", "ABI_VERSION",
            "route_workspace_bytes", "out_proj_workspace_bytes"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "librom.so")
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 ROM_OK, ROM_ERR_INVALID_ARGUMENT, ROM_ERR_UNSUPPORTED, ROM_ERR_WORKSPACE_TOO_SMALL, ROM_ERR_HIP = range(5)
 ROM_DTYPE_F32, ROM_DTYPE_BF16 = 0, 1
 ROM_ACT_NONE, ROM_ACT_SILU = 0, 1
 ABI_SYMBOLS = ("rom_abi_version", "rom_route_workspace_bytes", "rom_route", "rom_in_proj", "rom_in_proj_weighted", "rom_conv1d",
+               "rom_backward_workspace_bytes", "rom_out_proj_backward", "rom_in_proj_backward",
                "rom_out_proj_workspace_bytes", "rom_out_proj", "rom_status_string", "rom_last_error")
 
 
@@ -74,6 +76,14 @@ def lib(path: str = LIB_PATH) -> ctypes.CDLL:
     L.rom_in_proj_weighted.restype = ctypes.c_int
     L.rom_conv1d.argtypes = [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _vp]
     L.rom_conv1d.restype = ctypes.c_int
+    L.rom_backward_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
+    L.rom_backward_workspace_bytes.restype = _sz
+    L.rom_out_proj_backward.argtypes = [_vp, _vp, _vp, ctypes.POINTER(RoutingStruct), ctypes.c_int, _i32, _i32, _i32,
+                                        _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    L.rom_out_proj_backward.restype = ctypes.c_int
+    L.rom_in_proj_backward.argtypes = [_vp, _vp, _vp, ctypes.POINTER(RoutingStruct), ctypes.c_int, _i32, _i32, _i32,
+                                       _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    L.rom_in_proj_backward.restype = ctypes.c_int
     L.rom_out_proj_workspace_bytes.argtypes = [_i32, _i32, ctypes.c_int]
     L.rom_out_proj_workspace_bytes.restype = _sz
     L.rom_out_proj.argtypes = [_vp, _vp, ctypes.POINTER(RoutingStruct), ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp,
@@ -143,6 +153,7 @@ class Routing:
         self.workspace = torch.empty(max(route_workspace_bytes(T, E), 256), dtype=torch.uint8, device=device)
         self.x_perm: Optional[torch.Tensor] = None
         self.out_workspace: Optional[torch.Tensor] = None  # gated rows for rom_out_proj, sized on first use
+        self.bwd_workspace: Optional[torch.Tensor] = None  # the backward calls' workspace, sized on first use
         self.struct = RoutingStruct(0, E, top_k, 0, _ptr(self.expert_id), _ptr(self.prob), _ptr(self.counts),
                                     _ptr(self.offsets), _ptr(self.perm), _ptr(self.inv_perm))
 
@@ -233,6 +244,57 @@ def conv1d(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] =
                               _stream(x.device, stream))
     _check(status, "rom_conv1d")
     return y
+
+
+def backward_workspace_bytes(T: int, d_model: int, d_inner: int, E: int, top_k: int = 1) -> int:
+    return int(lib().rom_backward_workspace_bytes(T, d_model, d_inner, E, top_k))
+
+
+def _bwd_workspace(routing: "Routing", T: int, dm: int, di: int, device) -> torch.Tensor:
+    need = backward_workspace_bytes(T, dm, di, routing.E, routing.top_k)
+    if routing.bwd_workspace is None or routing.bwd_workspace.numel() < need:
+        routing.bwd_workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return routing.bwd_workspace
+
+
+def out_proj_backward(d_out: torch.Tensor, z: torch.Tensor, h: torch.Tensor, routing: "Routing", W_out: torch.Tensor,
+                      stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """rom_out_proj_backward: (dz, dh, dW_out) for the upstream gradient d_out, router probabilities held fixed.
+    dW_out is fp32."""
+    for t, n in ((d_out, "d_out"), (z, "z"), (h, "h"), (W_out, "W_out")):
+        _dev(t, n)
+    T, di = z.shape
+    E, dm, di2 = W_out.shape
+    if di2 != di or h.shape != z.shape or d_out.shape != (T, dm) or E != routing.E:
+        raise ValueError("shapes: d_out [T][d_model], z, h [T][d_inner], W_out [E][d_model][d_inner]")
+    dz, dh = torch.empty_like(z), torch.empty_like(z)
+    dW = torch.empty((E, dm, di), dtype=torch.float32, device=z.device)
+    ws = _bwd_workspace(routing, T, dm, di, z.device)
+    status = lib().rom_out_proj_backward(_ptr(d_out), _ptr(z), _ptr(h), ctypes.byref(routing.struct), _dtype_code(z),
+                                         T, dm, di, _ptr(W_out), _ptr(dz), _ptr(dh), _ptr(dW), _ptr(ws), ws.numel(),
+                                         _stream(z.device, stream))
+    _check(status, "rom_out_proj_backward")
+    return dz, dh, dW
+
+
+def in_proj_backward(X: torch.Tensor, dx: torch.Tensor, dz: torch.Tensor, routing: "Routing", W_conv: torch.Tensor,
+                     W_gate: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """rom_in_proj_backward: (dX, dW_conv, dW_gate) for the upstream gradients dx, dz; weight gradients are fp32."""
+    for t, n in ((X, "X"), (dx, "dx"), (dz, "dz"), (W_conv, "W_conv"), (W_gate, "W_gate")):
+        _dev(t, n)
+    T, dm = X.shape
+    E, di, dm2 = W_conv.shape
+    if dm2 != dm or W_gate.shape != W_conv.shape or dx.shape != (T, di) or dz.shape != (T, di) or E != routing.E:
+        raise ValueError("shapes: X [T][d_model], dx, dz [T][d_inner], W_conv, W_gate [E][d_inner][d_model]")
+    dX = torch.empty_like(X)
+    dWc = torch.empty((E, di, dm), dtype=torch.float32, device=X.device)
+    dWg = torch.empty_like(dWc)
+    ws = _bwd_workspace(routing, T, dm, di, X.device)
+    status = lib().rom_in_proj_backward(_ptr(X), _ptr(dx), _ptr(dz), ctypes.byref(routing.struct), _dtype_code(X), T,
+                                        dm, di, _ptr(W_conv), _ptr(W_gate), _ptr(dX), _ptr(dWc), _ptr(dWg), _ptr(ws),
+                                        ws.numel(), _stream(X.device, stream))
+    _check(status, "rom_in_proj_backward")
+    return dX, dWc, dWg
 
 
 def out_proj_workspace_bytes(T: int, d_inner: int, dtype: torch.dtype) -> int:

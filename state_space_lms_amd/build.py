@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIBRARY = os.path.join(OUT_DIR, "librom.so")
-SOURCES = ["rom_api.hip", "rom_route.hip", "rom_gemm.hip", "rom_conv.hip"]
+SOURCES = ["rom_api.hip", "rom_route.hip", "rom_gemm.hip", "rom_conv.hip", "rom_bwd.hip"]
 ARCH = "gfx950"
 
 

@@ -75,6 +75,23 @@ rom_status check_routing_for_proj(const rom_routing *r, int32_t T) {
     return ROM_OK;
 }
 
+rom_status check_bwd_common(rom_dtype dtype, const rom_routing *routing, int32_t T, int32_t d_model, int32_t d_inner,
+                            void *workspace, size_t workspace_bytes) {
+    rom_status s;
+    if ((s = check_dtype(dtype)) != ROM_OK) return s;
+    if (dtype != ROM_DTYPE_BF16) return fail(ROM_ERR_UNSUPPORTED, "the backward supports bf16 data only");
+    if ((s = check_dims(T, d_model, "d_model")) != ROM_OK) return s;
+    if ((s = check_dims(T, d_inner, "d_inner")) != ROM_OK) return s;
+    if ((s = check_routing_for_proj(routing, T)) != ROM_OK) return s;
+    if (T == 0) return ROM_OK;
+    const size_t need = rom::backward_workspace_bytes(T, d_model, d_inner, routing->E, routing->top_k);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(ROM_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed",
+                    workspace == nullptr ? (size_t)0 : workspace_bytes, need);
+    if (!aligned(workspace, 256)) return fail(ROM_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    return ROM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -206,6 +223,82 @@ rom_status rom_conv1d(const void *x, rom_dtype dtype, int32_t n_seq, int32_t seq
     hipError_t err = rom::launch_conv1d(x, dtype, n_seq, seq_len, channels, weight, bias, width, activation, y,
                                         static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return hip_fail(err, "rom_conv1d launch");
+    return ROM_OK;
+}
+
+size_t rom_backward_workspace_bytes(int32_t T, int32_t d_model, int32_t d_inner, int32_t E, int32_t top_k) {
+    if (T <= 0 || d_model <= 0 || d_inner <= 0 || E < 1 || E > ROM_MAX_EXPERTS || top_k < 1 || top_k > ROM_MAX_TOP_K)
+        return 0;
+    return rom::backward_workspace_bytes(T, d_model, d_inner, E, top_k);
+}
+
+
+rom_status rom_out_proj_backward(const void *d_out, const void *z, const void *h, const rom_routing *routing,
+                                 rom_dtype dtype, int32_t T, int32_t d_model, int32_t d_inner, const void *W_out,
+                                 void *dz, void *dh, float *dW_out, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+    g_last_error[0] = '\0';
+    rom_status s = check_bwd_common(dtype, routing, T, d_model, d_inner, workspace, workspace_bytes);
+    if (s != ROM_OK || T == 0) return s;
+    ROM_CHECK_PTR(d_out, 16);
+    ROM_CHECK_PTR(z, 16);
+    ROM_CHECK_PTR(h, 16);
+    ROM_CHECK_PTR(W_out, 16);
+    ROM_CHECK_PTR(dz, 16);
+    ROM_CHECK_PTR(dh, 16);
+    ROM_CHECK_PTR(dW_out, 16);
+    const size_t ib = (size_t)T * d_inner * 2, gb = (size_t)T * d_model * 2;
+    const size_t wb = (size_t)routing->E * d_model * d_inner * 4;
+    const size_t need = rom::backward_workspace_bytes(T, d_model, d_inner, routing->E, routing->top_k);
+    const void *ins[4] = {d_out, z, h, workspace};
+    const size_t insb[4] = {gb, ib, ib, need};
+    void *outs[3] = {dz, dh, dW_out};
+    const size_t outsb[3] = {ib, ib, wb};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 4; ++i)
+            if (overlap(outs[o], outsb[o], ins[i], insb[i]))
+                return fail(ROM_ERR_INVALID_ARGUMENT, "an output overlaps an input or the workspace");
+        for (int q = o + 1; q < 3; ++q)
+            if (overlap(outs[o], outsb[o], outs[q], outsb[q])) return fail(ROM_ERR_INVALID_ARGUMENT, "outputs overlap");
+    }
+    hipError_t err = rom::launch_out_proj_backward(d_out, z, h, *routing, T, d_model, d_inner, W_out, dz, dh, dW_out,
+                                                   workspace, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, "rom_out_proj_backward launch");
+    return ROM_OK;
+}
+
+rom_status rom_in_proj_backward(const void *X, const void *dx, const void *dz, const rom_routing *routing,
+                                rom_dtype dtype, int32_t T, int32_t d_model, int32_t d_inner, const void *W_conv,
+                                const void *W_gate, void *dX, float *dW_conv, float *dW_gate, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+    g_last_error[0] = '\0';
+    rom_status s = check_bwd_common(dtype, routing, T, d_model, d_inner, workspace, workspace_bytes);
+    if (s != ROM_OK || T == 0) return s;
+    ROM_CHECK_PTR(X, 16);
+    ROM_CHECK_PTR(dx, 16);
+    ROM_CHECK_PTR(dz, 16);
+    ROM_CHECK_PTR(W_conv, 16);
+    ROM_CHECK_PTR(W_gate, 16);
+    ROM_CHECK_PTR(dX, 16);
+    ROM_CHECK_PTR(dW_conv, 16);
+    ROM_CHECK_PTR(dW_gate, 16);
+    const size_t xb = (size_t)T * d_model * 2, ib = (size_t)T * d_inner * 2;
+    const size_t wb = (size_t)routing->E * d_model * d_inner * 4;
+    const size_t need = rom::backward_workspace_bytes(T, d_model, d_inner, routing->E, routing->top_k);
+    const void *ins[4] = {X, dx, dz, workspace};
+    const size_t insb[4] = {xb, ib, ib, need};
+    void *outs[3] = {dX, dW_conv, dW_gate};
+    const size_t outsb[3] = {xb, wb, wb};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 4; ++i)
+            if (overlap(outs[o], outsb[o], ins[i], insb[i]))
+                return fail(ROM_ERR_INVALID_ARGUMENT, "an output overlaps an input or the workspace");
+        for (int q = o + 1; q < 3; ++q)
+            if (overlap(outs[o], outsb[o], outs[q], outsb[q])) return fail(ROM_ERR_INVALID_ARGUMENT, "outputs overlap");
+    }
+    hipError_t err = rom::launch_in_proj_backward(X, dx, dz, *routing, T, d_model, d_inner, W_conv, W_gate, dX,
+                                                  dW_conv, dW_gate, workspace, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, "rom_in_proj_backward launch");
     return ROM_OK;
 }
 

@@ -63,4 +63,28 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 __device__ __forceinline__ float silu_precise(float v) { return v / (1.0f + expf(-v)); }
 __device__ __forceinline__ float silu_fast(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
+// ---- MFMA operand staging (shared by the forward and backward GEMMs)
+// gfx950 LDS serves a 16-byte-per-lane read 16 lanes at a time across 256 bytes of banks: 16 slots of
+// 16 bytes. An MFMA operand read has 16 consecutive lanes on 16 consecutive rows at one logical chunk,
+// so the swizzle must send those 16 rows to 16 different slots. With 128-byte rows (BK = 64) a row's
+// parity picks the half of the 256-byte window and (row >> 1) & 7 permutes the chunk within it; with
+// 64-byte rows (BK = 32) row & 3 picks the quarter and (row >> 2) & 3 permutes within it.
+template <int KCH>
+__device__ __forceinline__ int lds_swz(int row) {
+    return KCH == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
+
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n and lgkmcnt == 0, expcnt untouched.
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4); }
+
+// Wait until at most `ahead` K steps of copies (PER_STEP instructions each) are still in flight.
+template <int PER_STEP, int MAXAHEAD>
+__device__ __forceinline__ void wait_copies(int ahead) {
+    static_assert(PER_STEP * MAXAHEAD < 64, "vmcnt range");
+    if (MAXAHEAD >= 3 && ahead >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(3 * PER_STEP));
+    else if (MAXAHEAD >= 2 && ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * PER_STEP));
+    else if (MAXAHEAD >= 1 && ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(PER_STEP));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+}
+
 }  // namespace rom

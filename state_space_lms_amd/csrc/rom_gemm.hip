@@ -22,29 +22,11 @@
 #include <stdlib.h>
 
 #include "rom_device.h"
+#include "rom_gemm.h"
 #include "rom_internal.h"
 
 namespace rom {
 
-struct GemmArgs {
-    const void *A0;       // in-proj: X [T][K];  out-proj: z [T][K]
-    const void *A1;       // out-proj: h [T][K] (fp32 kernel only; NULL: A rows are used as they are)
-    const void *B0;       // in-proj: W_conv [E][N0][K];  out-proj: W_out [E][N0][K]
-    const void *B1;       // in-proj: W_gate [E][N0][K]
-    void *C0;             // in-proj: x_out [T][N0];  out-proj: out [T][N0]
-    void *C1;             // in-proj: z_out [T][N0]
-    const int32_t *offsets;
-    const int32_t *perm;
-    const float *prob;
-    int T, K, N0, E;
-    int n_tiles;          // N-tiles over the concatenated columns (nB * N0 / BN)
-    int n_tiles_per_b;    // N0 / BN
-    int m_tiles;          // M-tiles launched (upper bound of the real ones)
-    int group_m;          // XCD-aware order: M-tiles per group (0: plain row-major order)
-    int per_xcd;          // XCD-aware order: tiles assigned to each of the 8 XCDs
-    int accumulate;       // 1: add to the values already in C (the second choice of a top-2 routing)
-    int a_by_token;       // out-projection: A rows are in token order (gathered through perm), not slot order
-};
 
 // Tile (mt, nt) of workgroup blockIdx.x; false if the workgroup has no tile.
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on XCD b % 8), each with its
@@ -107,29 +89,6 @@ __device__ __forceinline__ bool locate_mtile(const int32_t *__restrict__ offsets
 // a 32x32 block belong to ONE token row (lane % 32) and hold 4 runs of 4 consecutive output columns,
 // so the epilogue scales them by that token's probability and writes 8-byte packed stores straight
 // to the token's output row (the un-permute).
-// gfx950 LDS serves a 16-byte-per-lane read 16 lanes at a time across 256 bytes of banks: 16 slots of
-// 16 bytes. An MFMA operand read has 16 consecutive lanes on 16 consecutive rows at one logical chunk,
-// so the swizzle must send those 16 rows to 16 different slots. With 128-byte rows (BK = 64) a row's
-// parity picks the half of the 256-byte window and (row >> 1) & 7 permutes the chunk within it; with
-// 64-byte rows (BK = 32) row & 3 picks the quarter and (row >> 2) & 3 permutes within it.
-template <int KCH>
-__device__ __forceinline__ int lds_swz(int row) {
-    return KCH == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
-}
-
-// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n and lgkmcnt == 0, expcnt untouched.
-constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4); }
-
-// Wait until at most `ahead` K steps of copies (PER_STEP instructions each) are still in flight.
-template <int PER_STEP, int MAXAHEAD>
-__device__ __forceinline__ void wait_copies(int ahead) {
-    static_assert(PER_STEP * MAXAHEAD < 64, "vmcnt range");
-    if (MAXAHEAD >= 3 && ahead >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(3 * PER_STEP));
-    else if (MAXAHEAD >= 2 && ahead == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * PER_STEP));
-    else if (MAXAHEAD >= 1 && ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(PER_STEP));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-}
-
 // ---- staged epilogue. Scattering the C^T-layout accumulators straight to the token rows costs one
 // store instruction per 8 bytes and touches 32 rows (cache lines) per instruction. Instead each wave
 // writes its block, converted to bf16 and scaled per row, into an LDS tile of BM x BN, and the
@@ -236,11 +195,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
     const int dr = lane / KCH, dpc = lane % KCH;
     const uint16_t *a_dma[A_DMA];
     const uint16_t *b_dma[B_DMA];
+    const uint16_t *a_hi[A_DMA];
+    const int k_lo = p.k_split > 0 ? p.k_split : K;  // row length of A0
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) {
         const int row = (wave * A_DMA + j) * RG + dr;
         const int c = dpc ^ lds_swz<KCH>(row);
-        a_dma[j] = static_cast<const uint16_t *>(p.A0) + (size_t)s_arow[row] * K + c * 8;
+        a_dma[j] = static_cast<const uint16_t *>(p.A0) + (size_t)s_arow[row] * k_lo + c * 8;
+        a_hi[j] = static_cast<const uint16_t *>(p.k_split > 0 ? p.A_hi : p.A0) + (size_t)s_arow[row] * (K - k_lo) + c * 8;
     }
 #pragma unroll
     for (int j = 0; j < B_DMA; ++j) {
@@ -252,8 +214,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
         uint16_t *as = smem + stage * STAGE;
         uint16_t *bs = as + BM * BK;
         const int k0 = kt * BK;
+        const bool hi = k0 >= k_lo;  // uniform; never true without a split
 #pragma unroll
-        for (int j = 0; j < A_DMA; ++j) dma16_to_lds(a_dma[j] + k0, as + (wave * A_DMA + j) * RG * BK);
+        for (int j = 0; j < A_DMA; ++j)
+            dma16_to_lds(hi ? a_hi[j] + (k0 - k_lo) : a_dma[j] + k0, as + (wave * A_DMA + j) * RG * BK);
 #pragma unroll
         for (int j = 0; j < B_DMA; ++j) dma16_to_lds(b_dma[j] + k0, bs + (wave * B_DMA + j) * RG * BK);
     };
@@ -804,6 +768,10 @@ hipError_t launch_in_proj_weighted(const void *X, const rom_routing &r, rom_dtyp
         if (err != hipSuccess) return err;
     }
     return hipSuccess;
+}
+
+hipError_t launch_grouped_bf16(const GemmArgs &a, bool out, int nB, hipStream_t s) {
+    return out ? launch_bf16_auto<true>(a, nB, s) : launch_bf16_auto<false>(a, nB, s);
 }
 
 size_t out_proj_workspace_bytes(int T, int di, rom_dtype dt) {

@@ -38,6 +38,16 @@ hipError_t launch_in_proj_weighted(const void *X, const rom_routing &r, rom_dtyp
 hipError_t launch_conv1d(const void *x, rom_dtype dt, int nseq, int L, int C, const void *w, const void *bias,
                          int width, int act, void *y, hipStream_t s);
 
+hipError_t launch_out_proj_backward(const void *g, const void *z, const void *h, const rom_routing &r, int T, int dm,
+                                    int di, const void *Wo, void *dz, void *dh, float *dWo, void *ws, hipStream_t s);
+
+hipError_t launch_in_proj_backward(const void *X, const void *dx, const void *dzg, const rom_routing &r, int T, int dm,
+                                   int di, const void *Wc, const void *Wg, void *dX, float *dWc, float *dWg, void *ws,
+                                   hipStream_t s);
+
+// Workspace bytes either backward call needs for T tokens, E experts and top_k choices (bf16 data).
+size_t backward_workspace_bytes(int T, int dm, int di, int E, int top_k);
+
 // Workspace bytes the out-projection needs (the gated rows a, T * d_inner bf16 values; 0 for fp32 data).
 size_t out_proj_workspace_bytes(int T, int di, rom_dtype dt);
 

@@ -151,6 +151,52 @@ def test_conv1d_empty_is_noop(L):
     assert _conv(L, x=None, w=None, y=None, sl=0) == OK
 
 
+BWS = A + (1 << 32)  # 256-byte aligned fake workspace, far from the other fake buffers
+
+
+def _obwd(L, g=A, z=A + (1 << 24), h=A + (2 << 24), T=512, dm=128, di=256, Wo=A + (3 << 24), dz=A + (4 << 24),
+          dh=A + (5 << 24), dW=A + (6 << 24), r=None, dt=BF16, ws=BWS, wsb=1 << 30):
+    rs = r if r is not None else _routing(T, 8)
+    return L.rom_out_proj_backward(g, z, h, ctypes.byref(rs), dt, T, dm, di, Wo, dz, dh, dW, ws, wsb, None)
+
+
+def _ibwd(L, X=A, dx=A + (1 << 24), dz=A + (2 << 24), T=512, dm=128, di=256, Wc=A + (3 << 24), Wg=A + (4 << 24),
+          dX=A + (5 << 24), dWc=A + (6 << 24), dWg=A + (7 << 24), r=None, dt=BF16, ws=BWS, wsb=1 << 30):
+    rs = r if r is not None else _routing(T, 8)
+    return L.rom_in_proj_backward(X, dx, dz, ctypes.byref(rs), dt, T, dm, di, Wc, Wg, dX, dWc, dWg, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=rom.ROM_DTYPE_F32), UNSUPPORTED), (dict(dt=9), INVALID), (dict(T=-1), INVALID), (dict(di=96), UNSUPPORTED),
+    (dict(g=None), INVALID), (dict(dW=A + 8), INVALID), (dict(ws=None), WS_SMALL), (dict(wsb=1024), WS_SMALL),
+    (dict(ws=BWS + 16), INVALID), (dict(dz=A + (2 << 24)), INVALID), (dict(dh=A + (4 << 24)), INVALID),
+    (dict(r=_routing(256, 8)), INVALID), (dict(r=_routing(512, 8, top_k=3)), UNSUPPORTED),
+])
+def test_out_proj_backward_rejects(L, kw, code):
+    assert _obwd(L, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=rom.ROM_DTYPE_F32), UNSUPPORTED), (dict(dm=0), INVALID), (dict(dx=None), INVALID),
+    (dict(dWg=None), INVALID), (dict(dX=A + 64), INVALID), (dict(dWg=A + (6 << 24)), INVALID),
+    (dict(wsb=0), WS_SMALL), (dict(r=_routing(512, 8, offsets=None)), INVALID),
+])
+def test_in_proj_backward_rejects(L, kw, code):
+    assert _ibwd(L, **kw) == code
+
+
+def test_backward_T0_noop_and_workspace_bytes(L):
+    assert _obwd(L, g=None, z=None, h=None, Wo=None, dz=None, dh=None, dW=None, ws=None, wsb=0, T=0,
+                 r=_routing(0, 8)) == OK
+    assert _ibwd(L, X=None, dx=None, dz=None, Wc=None, Wg=None, dX=None, dWc=None, dWg=None, ws=None, wsb=0, T=0,
+                 r=_routing(0, 8)) == OK
+    assert L.rom_backward_workspace_bytes(0, 128, 256, 8, 1) == 0
+    b1 = L.rom_backward_workspace_bytes(16384, 1024, 2048, 8, 1)
+    b2 = L.rom_backward_workspace_bytes(16384, 1024, 2048, 8, 2)
+    # at least the transposed in-projection stacks and token-contiguous copies of dx, dz and X
+    assert b1 >= 8 * 1024 * 4096 * 2 + (2 * 2048 + 1024) * 16384 * 2 and b2 > b1
+
+
 WS = A + (1 << 28)
 
 

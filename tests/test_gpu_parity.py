@@ -382,3 +382,110 @@ def test_conv1d(rom, oracle, case):
     err = parity.norm_max_err(parity.to_host(y), ref)
     print(f"[parity conv1d]   y={err:.2e}", flush=True)
     assert err <= parity.TOL[dt], f"conv1d: normalised max error {err:.3g}"
+
+
+# ------------------------------------------------------------------------------------------------
+# backward of the routed projections (router probabilities held fixed)
+
+def _entries(rng, E, R, C, n):
+    return np.stack([rng.integers(0, E, n), rng.integers(0, R, n), rng.integers(0, C, n)], axis=1)
+
+
+def check_backward(rom, orc, w, top_k=1, inp=None, rows=None, n_entries=None, label=""):
+    """GPU out_proj_backward and in_proj_backward against the oracle. rows=None compares every token and the
+    full weight gradients; otherwise the given tokens and n_entries sampled weight-gradient entries."""
+    import torch
+    inp = inp if inp is not None else workloads.make_inputs(w)
+    gr_in = workloads.make_grad_inputs(w)
+    tol = parity.TOL[w.dtype]
+    print(f"[parity bwd] {label or w.name}: T={w.T} d_model={w.d_model} d_inner={w.d_inner} E={w.E} "
+          f"top_k={top_k}", flush=True)
+    d = lambda a: parity.to_device(a, w.dtype)
+    X, z, h = d(inp["X"]), d(inp["z"]), d(inp["h"])
+    Wc, Wg, Wo = d(inp["W_conv"]), d(inp["W_gate"]), d(inp["W_out"])
+    g, dx, dzu = d(gr_in["d_out"]), d(gr_in["dx"]), d(gr_in["dz"])
+    Wr = parity.to_device(inp["W_router"], "f32")
+    bias = parity.to_device(inp["bias"], "f32") if inp.get("bias") is not None else None
+    r = rom.route(X, Wr, bias, top_k=top_k)
+    dz, dh, dWo = rom.out_proj_backward(g, z, h, r, Wo)
+    dX, dWc, dWg = rom.in_proj_backward(X, dx, dzu, r, Wc, Wg)
+    torch.cuda.synchronize()
+    gr = _route_host(r, squeeze=False)
+    o_route = orc.route(inp["X"], inp["W_router"], inp.get("bias"), top_k=top_k, want_logits=True)
+    agree = parity.check_route_topk(gr, o_route, w.T, w.E, top_k, tol)
+    ids_o, prob_o = o_route["ids"], o_route["prob"]
+    # weight gradients sum over all tokens: compare only experts untouched by a token whose expert set differs
+    bad = set(np.unique(ids_o[~agree]).tolist()) | set(np.unique(gr["expert_id"][:, ~agree]).tolist())
+    zf = inp["z"].astype(np.float64)
+    full = rows is None
+    rows = np.arange(w.T) if full else rows
+    rows = rows[agree[rows]]
+    dz_o, dh_o = orc.out_proj_dgrad(gr_in["d_out"][rows], zf[rows], inp["h"][rows], ids_o[rows], prob_o[rows],
+                                    inp["W_out"])
+    dX_o = orc.in_proj_dgrad(gr_in["dx"][rows], gr_in["dz"][rows], ids_o[rows], inp["W_conv"], inp["W_gate"])
+    errs = {"dz": parity.norm_max_err(_rows(dz, rows), dz_o), "dh": parity.norm_max_err(_rows(dh, rows), dh_o),
+            "dX": parity.norm_max_err(_rows(dX, rows), dX_o)}
+    keep_e = np.array([e for e in range(w.E) if e not in bad], dtype=np.int64)
+    if full:
+        dWo_o = orc.out_proj_wgrad(gr_in["d_out"], zf, inp["h"], ids_o, prob_o, w.E)
+        dWc_o, dWg_o = orc.in_proj_wgrad(inp["X"], gr_in["dx"], gr_in["dz"], ids_o, w.E)
+        errs["dW_out"] = parity.norm_max_err(parity.to_host(dWo)[keep_e], dWo_o[keep_e])
+        errs["dW_conv"] = parity.norm_max_err(parity.to_host(dWc)[keep_e], dWc_o[keep_e])
+        errs["dW_gate"] = parity.norm_max_err(parity.to_host(dWg)[keep_e], dWg_o[keep_e])
+        # an expert that received no token has an exactly zero gradient
+        used = np.unique(ids_o)
+        for e in range(w.E):
+            if e not in used and e not in bad:
+                assert not parity.to_host(dWo)[e].any() and not parity.to_host(dWc)[e].any()
+    else:
+        rng = np.random.default_rng(7)
+        eo = _entries(rng, w.E, w.d_model, w.d_inner, n_entries)
+        eo = eo[np.isin(eo[:, 0], keep_e)]
+        ei = _entries(rng, w.E, w.d_inner, w.d_model, n_entries)
+        ei = ei[np.isin(ei[:, 0], keep_e)]
+        vo = orc.out_proj_wgrad_entries(gr_in["d_out"], zf, inp["h"], ids_o, prob_o, eo)
+        vc, vg = orc.in_proj_wgrad_entries(inp["X"], gr_in["dx"], gr_in["dz"], ids_o, ei)
+        # normalised by the largest magnitude of the whole GPU tensor (the oracle has only the samples)
+        host = {k: parity.to_host(t) for k, t in (("o", dWo), ("c", dWc), ("g", dWg))}
+        for name, key, ent, ref in (("dW_out", "o", eo, vo), ("dW_conv", "c", ei, vc), ("dW_gate", "g", ei, vg)):
+            got = host[key][tuple(ent.T)]
+            errs[name] = float(np.max(np.abs(got - ref)) / np.max(np.abs(host[key]))) if len(ent) else 0.0
+    print("[parity bwd]   set-mismatch=%d rows=%d " % (int((~agree).sum()), len(rows))
+          + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for name, err in errs.items():
+        assert err <= tol, f"{name}: normalised max error {err:.3g} > {tol}"
+    return gr
+
+
+BWD = [
+    (workloads.custom_workload("bwd_T300", T=300, d_model=128, d_inner=256, E=4, seed=501), 1),
+    (workloads.custom_workload("bwd_T1000_tiles128", T=1000, d_model=256, d_inner=384, E=8, seed=502), 1),
+    (workloads.custom_workload("bwd_T777_tiles64", T=777, d_model=192, d_inner=320, E=3, seed=503), 1),
+    (workloads.custom_workload("bwd_T5", T=5, d_model=256, d_inner=128, E=8, seed=504), 1),
+    (workloads.custom_workload("bwd_top2_T513", T=513, d_model=128, d_inner=192, E=4, seed=505), 2),
+    (workloads.custom_workload("bwd_top2_T64", T=64, d_model=256, d_inner=256, E=4, seed=506), 2),
+    (workloads.custom_workload("bwd_top2_E16", T=2000, d_model=320, d_inner=192, E=16, seed=507), 2),
+    (workloads.custom_workload("bwd_T4096_tiles256", T=4096, d_model=512, d_inner=512, E=8, seed=508), 1),
+]
+
+
+@pytest.mark.parametrize("w,k", BWD, ids=[w.name for w, _ in BWD])
+def test_backward_small_shapes(rom, oracle, w, k):
+    check_backward(rom, oracle, w, top_k=k)
+
+
+def test_backward_hot_expert(rom, oracle):
+    """Every token on expert 2: the other experts' weight gradients are exactly zero."""
+    w = workloads.custom_workload("bwd_hot", T=900, d_model=128, d_inner=256, E=8, seed=509)
+    bias = np.zeros(8, np.float32)
+    bias[2] = 1e3
+    check_backward(rom, oracle, w, inp=workloads.make_inputs(w, router_bias=bias), label="all tokens on expert 2")
+
+
+@pytest.mark.parametrize("top_k", [1, 2])
+def test_backward_full_samba_shape(rom, oracle, top_k):
+    w = workloads.get_workload("samba421m")
+    inp = workloads.make_inputs(w)
+    o_route = oracle.route(inp["X"], inp["W_router"], top_k=top_k)
+    rows = parity.sample_rows(oracle.sort(o_route["ids"][:, :1].copy(), w.E), w.T, n_random=96)
+    check_backward(rom, oracle, w, top_k=top_k, inp=inp, rows=rows, n_entries=600, label=f"samba421m top-{top_k}")

@@ -200,6 +200,18 @@ def make_conv_inputs(n_seq: int, seq_len: int, channels: int, width: int, dtype:
     return out
 
 
+def make_grad_inputs(w: Workload, seed: int = 1000) -> dict:
+    """Upstream gradients for the backward: d_out [T][d_model] (dL/dout), dx and dz [T][d_inner] (dL/dx_out,
+    dL/dz_out), each ~ N(0, 1) in the workload's storage type, one PCG64 child stream per tensor."""
+    children = np.random.SeedSequence([w.seed, seed]).spawn(3)
+    rng = [np.random.Generator(np.random.PCG64(c)) for c in children]
+    return {
+        "d_out": _draw(rng[0], (w.T, w.d_model), 1.0, w.dtype),
+        "dx": _draw(rng[1], (w.T, w.d_inner), 1.0, w.dtype),
+        "dz": _draw(rng[2], (w.T, w.d_inner), 1.0, w.dtype),
+    }
+
+
 _BIAS_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tests", "golden", "skewed_router_bias.json")
 
 
