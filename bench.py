@@ -66,7 +66,7 @@ def measured_traffic(workload: str):
         return None
 
 
-def cpu_baseline(inp, w, target_seconds: float, conv: bool = False):
+def cpu_baseline(inp, w, target_seconds: float, conv: bool = False, bwd: bool = False):
     """The CPU oracle as it stands, timed on a bounded prefix of the workload's tokens."""
     import numpy as np
     import oracle
@@ -85,6 +85,14 @@ def cpu_baseline(inp, w, target_seconds: float, conv: bool = False):
                 cin = workloads.make_conv_inputs(1, 1, w.d_inner, CONV_WIDTH, w.dtype, seed=w.seed)
                 orc.conv1d(x.astype(np.float32)[None], cin["weight"], cin["bias"])
             orc.out_proj(z, inp["h"][:n], r["ids"], r["prob"], inp["W_out"])
+            if bwd:
+                gin = workloads.make_grad_inputs(w)
+                g, hh = gin["d_out"][:n], inp["h"][:n]
+                dz, _ = orc.out_proj_dgrad(g, z, hh, r["ids"], r["prob"], inp["W_out"])
+                orc.out_proj_wgrad(g, z, hh, r["ids"], r["prob"], w.E)
+                dz32 = dz.astype(np.float32)
+                orc.in_proj_dgrad(gin["dx"][:n], dz32, r["ids"], inp["W_conv"], inp["W_gate"])
+                orc.in_proj_wgrad(inp["X"][:n], gin["dx"][:n], dz32, r["ids"], w.E)
         return time.perf_counter() - t0
 
     probe = min(w.T, 32)
@@ -93,6 +101,8 @@ def cpu_baseline(inp, w, target_seconds: float, conv: bool = False):
     dt = run(n) if n > probe else tp
     path = "in_proj_weighted" if w.method == "swimba" else ("in_proj + conv1d + out_proj" if conv else
                                                             "in_proj + out_proj")
+    if bwd:
+        path += " + both backwards"
     return {"value": n / dt, "unit": "tokens/s", "cores": orc.threads(), "kind": "oracle",
             "sample": f"first {n} of {w.T} tokens: route + histogram/sort + {path} in plain C "
                       f"(fp32 router, fp64 projection sums, OpenMP over tokens), {dt:.1f} s"}
@@ -109,6 +119,9 @@ def main() -> int:
     ap.add_argument("--with-conv1d", action="store_true",
                     help="add the shared short causal convolution (width 4, SiLU, bias) on the in-projection's x to "
                          "the step (prefill RoM workloads)")
+    ap.add_argument("--backward", action="store_true",
+                    help="add the backward of both projections (out_proj_backward, then in_proj_backward on its dz) to "
+                         "the step: a forward + backward pass of the routed projections (prefill RoM workloads)")
     ap.add_argument("--cold", action="store_true",
                     help="read a 1 GiB buffer before every step, so weights and inputs come from HBM (decode); the "
                          "step is then timed with GPU events around it")
@@ -127,6 +140,10 @@ def main() -> int:
     w = workloads.get_workload(args.workload)
     swimba = w.method == "swimba"
     conv = args.with_conv1d
+    bwd = args.backward
+    if bwd and (swimba or w.dtype != "bf16"):
+        print("bench.py: --backward needs a bf16 RoM workload", file=sys.stderr)
+        return 2
     if conv and (swimba or w.T <= 64):
         print("bench.py: --with-conv1d needs a prefill RoM workload (the decode-time convolution state is not "
               "built)", file=sys.stderr)
@@ -154,6 +171,10 @@ def main() -> int:
         x = torch.empty((w.T, w.d_inner), dtype=X.dtype, device=dev)
         z = torch.empty_like(x)
         out = torch.empty((w.T, w.d_model), dtype=X.dtype, device=dev)
+    if bwd:
+        gin = workloads.make_grad_inputs(w)
+        g_out, dx_up = up(gin["d_out"], w.dtype), up(gin["dx"], w.dtype)
+        bwd_res = {}
     if conv:
         cin = workloads.make_conv_inputs(1, 1, w.d_inner, CONV_WIDTH, w.dtype, seed=w.seed)
         Wcv, bcv = up(cin["weight"], w.dtype), up(cin["bias"], w.dtype)
@@ -169,7 +190,7 @@ def main() -> int:
     del cp_src, cp_dst
 
     stream = torch.cuda.current_stream(dev)
-    phases = ["route", "in"] + (["conv"] if conv else []) + ([] if swimba else ["out"])
+    phases = ["route", "in"] + (["conv"] if conv else []) + ([] if swimba else ["out"]) + (["obwd", "ibwd"] if bwd else [])
 
     def run_phase(ph):
         if ph == "route":
@@ -181,6 +202,10 @@ def main() -> int:
                 rom.in_proj(X, routing, Wc, Wg, x, z, stream=stream)
         elif ph == "conv":
             rom.conv1d(x, Wcv, bcv, n_seq=w.n_seq, activation=True, y=xc, stream=stream)
+        elif ph == "obwd":
+            bwd_res["o"] = rom.out_proj_backward(g_out, z, h, routing, Wo, stream=stream)
+        elif ph == "ibwd":
+            bwd_res["i"] = rom.in_proj_backward(X, dx_up, bwd_res["o"][0], routing, Wc, Wg, stream=stream)
         else:
             rom.out_proj(z, h, routing, Wo, out, stream=stream)
 
@@ -305,13 +330,23 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    if bwd:
+        for ph, key, mult in (("obwd", "out_proj_backward", 4), ("ibwd", "in_proj_backward", 8)):
+            tm = float(t_ph[ph].mean())
+            fl = mult * w.T * w.d_model * w.d_inner * w.top_k
+            result["breakdown"][key + "_us"] = round(tm * 1e6, 2)
+            result["breakdown"][key + "_tflops"] = round(fl / tm / 1e12, 1)
+        fwd_fl = fl_in + fl_out
+        all_fl = fwd_fl + 12.0 * w.T * w.d_model * w.d_inner * w.top_k
+        result["breakdown"]["fwd_bwd_tflops"] = round(all_fl / (elapsed / args.steps) / 1e12, 1)
+        config["backward"] = True
     if conv:
         mean_conv = float(t_ph["conv"].mean())
         result["breakdown"]["conv1d_us"] = round(mean_conv * 1e6, 2)
         result["breakdown"]["conv1d_gbs"] = round(bytes_conv / mean_conv / 1e9, 1)
         result["breakdown"]["conv1d_hbm_frac"] = round(bytes_conv / mean_conv / 1e9 / PEAK_HBM_GBS, 4)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_seconds, conv)
+        result["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_seconds, conv, bwd)
     print(json.dumps(result), flush=True)
     return 0
 
