@@ -32,7 +32,8 @@ sys.path.insert(0, ROOT)
 METRIC = "routed-projection tokens/sec + % bf16 MFMA peak (GEMM) / % HBM peak (decode)"
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA peaks
 PEAK_HBM_GBS = 8000.0                                # MI355X HBM3E
-KERNEL_SOURCES = ["state_space_lms_amd/csrc/rom_gemm.hip", "state_space_lms_amd/csrc/rom_device.h"]
+KERNEL_SOURCES = ["state_space_lms_amd/csrc/rom_gemm.hip", "state_space_lms_amd/csrc/rom_gemm.h",
+                  "state_space_lms_amd/csrc/rom_device.h"]
 COUNTERS_FILE = "profiles/counters_in_proj_{workload}.txt"
 COPY_PROBE_BYTES = 256 << 20
 CONV_WIDTH = 4   # the pages give no width for the short convolution; 4 is the value this benchmark takes
