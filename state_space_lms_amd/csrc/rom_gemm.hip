@@ -149,7 +149,7 @@ constexpr size_t gemm_lds_bytes(int BM, int BN, int BK, int NSTAGE) {
     return (size_t)(NSTAGE * (BM + BN) * BK > BM * BN ? NSTAGE * (BM + BN) * BK : BM * BN) * 2;
 }
 
-template <int BM, int BN, int BK, int NSTAGE, int WGM, int WGN, bool OUT, int SCHED>
+template <int BM, int BN, int BK, int NSTAGE, int WGM, int WGN, bool OUT, int SCHED, bool KSPLIT>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p) {
     constexpr int NW = WGM * WGN;
     constexpr int NT = 64 * NW;
@@ -196,13 +196,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
     const uint16_t *a_dma[A_DMA];
     const uint16_t *b_dma[B_DMA];
     const uint16_t *a_hi[A_DMA];
-    const int k_lo = p.k_split > 0 ? p.k_split : K;  // row length of A0
+    const int k_lo = KSPLIT ? p.k_split : K;  // row length of A0
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) {
         const int row = (wave * A_DMA + j) * RG + dr;
         const int c = dpc ^ lds_swz<KCH>(row);
         a_dma[j] = static_cast<const uint16_t *>(p.A0) + (size_t)s_arow[row] * k_lo + c * 8;
-        a_hi[j] = static_cast<const uint16_t *>(p.k_split > 0 ? p.A_hi : p.A0) + (size_t)s_arow[row] * (K - k_lo) + c * 8;
+        a_hi[j] = KSPLIT ? static_cast<const uint16_t *>(p.A_hi) + (size_t)s_arow[row] * (K - k_lo) + c * 8 : a_dma[j];
     }
 #pragma unroll
     for (int j = 0; j < B_DMA; ++j) {
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
         uint16_t *as = smem + stage * STAGE;
         uint16_t *bs = as + BM * BK;
         const int k0 = kt * BK;
-        const bool hi = k0 >= k_lo;  // uniform; never true without a split
+        const bool hi = KSPLIT && k0 >= k_lo;  // uniform
 #pragma unroll
         for (int j = 0; j < A_DMA; ++j)
             dma16_to_lds(hi ? a_hi[j] + (k0 - k_lo) : a_dma[j] + k0, as + (wave * A_DMA + j) * RG * BK);
@@ -582,7 +582,7 @@ static int group_m_choice() {
     return cached;
 }
 
-template <int BM, int BN, int BK, int NSTAGE, int WGM, int WGN, bool OUT, int SCHED>
+template <int BM, int BN, int BK, int NSTAGE, int WGM, int WGN, bool OUT, int SCHED, bool KSPLIT>
 static hipError_t launch_bf16(const GemmArgs &a0, int nB, hipStream_t s) {
     GemmArgs a = a0;
     a.n_tiles_per_b = a.N0 / BN;
@@ -602,12 +602,12 @@ static hipError_t launch_bf16(const GemmArgs &a0, int nB, hipStream_t s) {
     static bool attr_set = false;  // per process; the attribute is per function
     if (!attr_set) {
         hipError_t err = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&k_grouped_gemm_bf16<BM, BN, BK, NSTAGE, WGM, WGN, OUT, SCHED>),
+            reinterpret_cast<const void *>(&k_grouped_gemm_bf16<BM, BN, BK, NSTAGE, WGM, WGN, OUT, SCHED, KSPLIT>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (err != hipSuccess) return err;
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, BK, NSTAGE, WGM, WGN, OUT, SCHED>), dim3(grid), dim3(64 * WGM * WGN),
+    hipLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, BK, NSTAGE, WGM, WGN, OUT, SCHED, KSPLIT>), dim3(grid), dim3(64 * WGM * WGN),
                        smem, s, a);
     return hipGetLastError();
 }
@@ -648,19 +648,19 @@ static int default_tile(const GemmArgs &a, bool out) {
     return 5;
 }
 
-template <bool OUT>
+template <bool OUT, bool KSPLIT = false>
 static hipError_t launch_bf16_auto(const GemmArgs &a, int nB, hipStream_t s) {
     int t = tile_override(OUT);
     if (t < 0 || a.N0 % kTiles[t].bn != 0) t = default_tile(a, OUT);
     switch (t) {
-        case 0: return launch_bf16<256, 256, 64, 2, 2, 4, OUT, 0>(a, nB, s);
-        case 1: return launch_bf16<256, 256, 32, 4, 2, 4, OUT, 0>(a, nB, s);
-        case 2: return launch_bf16<256, 256, 64, 2, 2, 4, OUT, 1>(a, nB, s);
-        case 3: return launch_bf16<256, 128, 64, 3, 2, 2, OUT, 0>(a, nB, s);
-        case 4: return launch_bf16<128, 128, 64, 4, 2, 2, OUT, 0>(a, nB, s);
-        case 6: return launch_bf16<256, 256, 32, 4, 2, 4, OUT, 1>(a, nB, s);
-        case 7: return launch_bf16<256, 256, 64, 2, 2, 2, OUT, 1>(a, nB, s);
-        default: return launch_bf16<128, 64, 64, 4, 2, 2, OUT, 0>(a, nB, s);
+        case 0: return launch_bf16<256, 256, 64, 2, 2, 4, OUT, 0, KSPLIT>(a, nB, s);
+        case 1: return launch_bf16<256, 256, 32, 4, 2, 4, OUT, 0, KSPLIT>(a, nB, s);
+        case 2: return launch_bf16<256, 256, 64, 2, 2, 4, OUT, 1, KSPLIT>(a, nB, s);
+        case 3: return launch_bf16<256, 128, 64, 3, 2, 2, OUT, 0, KSPLIT>(a, nB, s);
+        case 4: return launch_bf16<128, 128, 64, 4, 2, 2, OUT, 0, KSPLIT>(a, nB, s);
+        case 6: return launch_bf16<256, 256, 32, 4, 2, 4, OUT, 1, KSPLIT>(a, nB, s);
+        case 7: return launch_bf16<256, 256, 64, 2, 2, 2, OUT, 1, KSPLIT>(a, nB, s);
+        default: return launch_bf16<128, 64, 64, 4, 2, 2, OUT, 0, KSPLIT>(a, nB, s);
     }
 }
 
@@ -771,6 +771,7 @@ hipError_t launch_in_proj_weighted(const void *X, const rom_routing &r, rom_dtyp
 }
 
 hipError_t launch_grouped_bf16(const GemmArgs &a, bool out, int nB, hipStream_t s) {
+    if (a.k_split > 0) return out ? hipErrorInvalidValue : launch_bf16_auto<false, true>(a, nB, s);
     return out ? launch_bf16_auto<true>(a, nB, s) : launch_bf16_auto<false>(a, nB, s);
 }
 
