@@ -145,8 +145,12 @@ __device__ __forceinline__ void ctile_to_global(const uint16_t *ct, int nrows, i
 }
 
 // LDS of a bf16 tile configuration: the pipeline stages, or the C tile of the epilogue if larger.
-constexpr size_t gemm_lds_bytes(int BM, int BN, int BK, int NSTAGE) {
-    return (size_t)(NSTAGE * (BM + BN) * BK > BM * BN ? NSTAGE * (BM + BN) * BK : BM * BN) * 2;
+// The C tile goes through LDS in one pass when BM x BN bf16 fits in 144 KiB, otherwise in WGM passes of
+// BM / WGM rows (one row band of waves at a time).
+constexpr int ctile_passes(int BM, int BN, int WGM) { return BM * BN * 2 <= 144 * 1024 ? 1 : WGM; }
+constexpr size_t gemm_lds_bytes(int BM, int BN, int BK, int NSTAGE, int WGM) {
+    const int crows = BM / ctile_passes(BM, BN, WGM);
+    return (size_t)(NSTAGE * (BM + BN) * BK > crows * BN ? NSTAGE * (BM + BN) * BK : crows * BN) * 2;
 }
 
 template <int BM, int BN, int BK, int NSTAGE, int WGM, int WGN, bool OUT, int SCHED, bool KSPLIT>
@@ -324,14 +328,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
         }
         return;
     }
-    // through LDS (no copies are in flight after the last step)
-    __syncthreads();
+    // through LDS (no copies are in flight after the last step), in one pass or one band of waves at a time
     float sc[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) sc[i] = OUT ? s_prob[wm * WM + i * 32 + (lane & 31)] : 1.0f;
-    acc_to_ctile<FM, FN, BN>(acc, smem, wm * WM, wn * WN, lane, sc);
-    __syncthreads();
-    ctile_to_global<BN, NT>(smem, BM, rows, s_tok, C, p.N0, n0, tid);
+    constexpr int PASSES = ctile_passes(BM, BN, WGM);
+    if constexpr (PASSES == 1) {
+        __syncthreads();
+        acc_to_ctile<FM, FN, BN>(acc, smem, wm * WM, wn * WN, lane, sc);
+        __syncthreads();
+        ctile_to_global<BN, NT>(smem, BM, rows, s_tok, C, p.N0, n0, tid);
+    } else {
+#pragma unroll
+        for (int q = 0; q < PASSES; ++q) {
+            __syncthreads();
+            if (wm == q) acc_to_ctile<FM, FN, BN>(acc, smem, 0, wn * WN, lane, sc);
+            __syncthreads();
+            ctile_to_global<BN, NT>(smem, WM, rows - q * WM, s_tok + q * WM, C, p.N0, n0, tid);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -598,7 +613,7 @@ static hipError_t launch_bf16(const GemmArgs &a0, int nB, hipStream_t s) {
     } else {
         grid = (unsigned)a.m_tiles * a.n_tiles;
     }
-    const size_t smem = gemm_lds_bytes(BM, BN, BK, NSTAGE);
+    const size_t smem = gemm_lds_bytes(BM, BN, BK, NSTAGE, WGM);
     static bool attr_set = false;  // per process; the attribute is per function
     if (!attr_set) {
         hipError_t err = hipFuncSetAttribute(
@@ -623,6 +638,7 @@ constexpr TileCfg kTiles[] = {
     {128, 64, 64, 4, 2, 2, 0},   // 5: 4 waves (64x32 each), BK 64, 4 stages (96 KiB)
     {256, 256, 32, 4, 2, 4, 1},  // 6: as 1, interleaved
     {256, 256, 64, 2, 2, 2, 1},  // 7: 4 waves (128x128 each), BK 64, 2 stages, interleaved
+    {320, 256, 64, 2, 2, 4, 1},  // 8: 8 waves (160x64 each), BK 64, 2 stages (144 KiB), C tile in 2 passes
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -638,12 +654,31 @@ static int tile_override(bool out) {
     return c;
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 // Default tile shape by problem: 256x256 blocks of 8 waves with interleaved fragment reads when there
-// are enough rows and columns (measured best on MI355X at T = 16384), smaller blocks for small T or
-// narrow N.
-static int default_tile(const GemmArgs &a, bool out) {
-    (void)out;
-    if (a.T >= 4096 && a.N0 % 256 == 0) return 2;
+// are enough rows and columns (measured best on MI355X at T = 16384), unless 320-row blocks need fewer
+// rounds of workgroups over the compute units for the same rows (rounds x rows per tile smaller; the
+// tile count is the launch's upper bound, as the host never reads the expert counts). Smaller blocks
+// for small T or narrow N.
+static int default_tile(const GemmArgs &a, int nB) {
+    if (a.T >= 4096 && a.N0 % 256 == 0) {
+        const long cus = device_cus(), nt = (long)nB * (a.N0 / 256);
+        const long t256 = (long)((a.T + (long)a.E * 255) / 256) * nt, t320 = (long)((a.T + (long)a.E * 319) / 320) * nt;
+        const long r256 = (t256 + cus - 1) / cus, r320 = (t320 + cus - 1) / cus;
+        return r320 * 320 < r256 * 256 ? 8 : 2;
+    }
     if (a.N0 % 128 == 0) return 4;
     return 5;
 }
@@ -651,7 +686,7 @@ static int default_tile(const GemmArgs &a, bool out) {
 template <bool OUT, bool KSPLIT = false>
 static hipError_t launch_bf16_auto(const GemmArgs &a, int nB, hipStream_t s) {
     int t = tile_override(OUT);
-    if (t < 0 || a.N0 % kTiles[t].bn != 0) t = default_tile(a, OUT);
+    if (t < 0 || a.N0 % kTiles[t].bn != 0) t = default_tile(a, nB);
     switch (t) {
         case 0: return launch_bf16<256, 256, 64, 2, 2, 4, OUT, 0, KSPLIT>(a, nB, s);
         case 1: return launch_bf16<256, 256, 32, 4, 2, 4, OUT, 0, KSPLIT>(a, nB, s);
@@ -660,6 +695,7 @@ static hipError_t launch_bf16_auto(const GemmArgs &a, int nB, hipStream_t s) {
         case 4: return launch_bf16<128, 128, 64, 4, 2, 2, OUT, 0, KSPLIT>(a, nB, s);
         case 6: return launch_bf16<256, 256, 32, 4, 2, 4, OUT, 1, KSPLIT>(a, nB, s);
         case 7: return launch_bf16<256, 256, 64, 2, 2, 2, OUT, 1, KSPLIT>(a, nB, s);
+        case 8: return launch_bf16<320, 256, 64, 2, 2, 4, OUT, 1, KSPLIT>(a, nB, s);
         default: return launch_bf16<128, 64, 64, 4, 2, 2, OUT, 0, KSPLIT>(a, nB, s);
     }
 }
