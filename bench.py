@@ -15,7 +15,8 @@ bf16 data. Prints ONE JSON line: whole-step tokens/s, the roofline of the domina
 in-projection grouped GEMM, timed live with HIP events on the stream it runs on), and the CPU oracle
 timed on a bounded sample of the same workload on the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--cold]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--cold] [--backward]
+                    [--with-conv1d] [--event-every N]
 """
 from __future__ import annotations
 
@@ -113,7 +114,12 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first: the GPU needs some tens of milliseconds of work to leave its idle "
+                         "clocks (the first ~50 Samba-size steps run ~40%% slower)")
+    ap.add_argument("--event-every", type=int, default=5,
+                    help="bracket the in-projection with HIP events on every n-th timed step (events cost a few "
+                         "microseconds of GPU time each, which matters at decode sizes)")
     ap.add_argument("--workload", default="samba421m")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -233,16 +239,17 @@ def main() -> int:
     new_ev = lambda n: [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     events = [new_ev(len(phases) + 1) for _ in range(args.steps)]
     if flush is None:
-        # warm: wall clock over K back-to-back steps; inside them only the in-projection is bracketed by
-        # events (the roofline's launch time), so the timed region carries two markers per step
-        ins = [new_ev(2) for _ in range(args.steps)]
+        # warm: wall clock over K back-to-back steps; inside them the in-projection is bracketed by events
+        # (the roofline's launch time) on every n-th step, so the timed region carries few markers
+        every = max(1, args.event_every)
+        ins = {k: new_ev(2) for k in range(0, args.steps, every)}
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(args.steps):
-            step(around_in=ins[k])
+            step(around_in=ins.get(k))
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-        t_in_timed = np.array([e[0].elapsed_time(e[1]) for e in ins]) * 1e-3
+        t_in_timed = np.array([e[0].elapsed_time(e[1]) for e in ins.values()]) * 1e-3
         # per-phase breakdown from a second, untimed pass of the same K steps
         for k in range(args.steps):
             step(ev=events[k])
