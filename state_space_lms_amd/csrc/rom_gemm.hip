@@ -12,11 +12,13 @@
 // last real tile exit at once. A rows are gathered through perm (token order -> slot order) while
 // they are staged into LDS; the epilogue scatters rows back to token order (the un-permute).
 //
-// bf16 path (T > 64): workgroups of WGM x WGN waves (8 for the default 256 x 256 tile), each wave owning a
-// (BM/WGM) x (BN/WGN) block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16, fp32 accumulators). Operand
-// rows are copied global -> LDS directly (no register round trip), NSTAGE - 1 K steps ahead of the MFMAs;
-// LDS rows are XOR-swizzled so that MFMA operand reads are free of bank conflicts. The tile is written
-// back through LDS as whole 16-byte row chunks. Details at k_grouped_gemm_bf16.
+// bf16 path (T > 64): workgroups of WGM x WGN waves (8 for the default 256 x 256 tile, and for the 320 x 256
+// tile chosen when it needs fewer rounds over the compute units), each wave owning a (BM/WGM) x (BN/WGN)
+// block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16, fp32 accumulators). Operand rows are copied
+// global -> LDS directly (no register round trip), NSTAGE - 1 K steps ahead of the MFMAs; LDS rows are
+// XOR-swizzled so that MFMA operand reads are free of bank conflicts. The tile is written back through LDS
+// as whole 16-byte row chunks. Details at k_grouped_gemm_bf16. The backward's data gradients run the same
+// kernels on transposed weight stacks (KSPLIT: the A rows switch source at k_split).
 //
 // Decode path (T <= 64): weight-streaming kernels (k_grouped_gemv_bf16). fp32 data: k_grouped_gemm_f32.
 #include <stdlib.h>
