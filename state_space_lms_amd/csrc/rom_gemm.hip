@@ -15,8 +15,9 @@
 // bf16 path (T > 64): workgroups of WGM x WGN waves (8 for the default 256 x 256 tile, and for the 320 x 256
 // tile chosen when it needs fewer rounds over the compute units), each wave owning a (BM/WGM) x (BN/WGN)
 // block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16, fp32 accumulators). Operand rows are copied
-// global -> LDS directly (no register round trip), NSTAGE - 1 K steps ahead of the MFMAs; LDS rows are
-// XOR-swizzled so that MFMA operand reads are free of bank conflicts. The tile is written back through LDS
+// global -> LDS directly (no register round trip), NSTAGE - 1 K steps ahead of the MFMAs; in the default
+// two-stage schedule each step's barrier sits ahead of its last MFMAs, which then cover the first operand
+// reads of the next step. LDS rows are XOR-swizzled so that MFMA operand reads are free of bank conflicts. The tile is written back through LDS
 // as whole 16-byte row chunks. Details at k_grouped_gemm_bf16. The backward's data gradients run the same
 // kernels on transposed weight stacks (KSPLIT: the A rows switch source at k_split).
 //
@@ -286,6 +287,87 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
     };
 
     const int nk = K / BK;
+    if constexpr (SCHED == 2) {
+        // Two stages, the barrier moved ahead of the last sub-step's MFMAs: once a wave's fragment reads
+        // of stage kt and its copies of stage kt+1 are complete it joins the barrier, then issues the
+        // copies of step kt+2 into the stage just read and the first fragment reads of stage kt+1, and
+        // only then the last MFMAs of step kt, which cover the latency of those reads. The loop body is
+        // one block split only by the barrier (the step after the last copies again its own data into
+        // the free stage, in bounds and never read), so that the fragment reads can be slotted between
+        // the MFMAs.
+        static_assert(NSTAGE == 2 && BK == 64, "early-barrier schedule");
+        constexpr int NR = FM + FN, NM = FM * FN;
+        constexpr int NG = (NR + 1) / 2;  // MFMAs that get fragment reads slotted after them
+        static_assert(NM > NG, "read slots");
+        bf16x8 af[2][FM], bfr[2][FN];
+        auto load_frags = [&](int stg, int kk, int set) {
+            const uint16_t *st = smem + stg * STAGE;
+            const int co = ((kk * 2 + half) ^ swz) * 8;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) af[set][i] = *reinterpret_cast<const bf16x8 *>(st + a_frag[i] + co);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bfr[set][j] = *reinterpret_cast<const bf16x8 *>(st + b_frag[j] + co);
+        };
+        auto mfmas = [&](int set) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[set][j], af[set][i], acc[i][j], 0, 0, 0);
+        };
+        // issue order of one sub-step: an MFMA, two fragment reads of the next sub-step, ..., then the
+        // remaining MFMAs
+        auto slot_reads = [&]() {
+#pragma unroll
+            for (int q = 0; q < NR / 2; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            if constexpr (NR % 2 == 1) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NM - NG, 0);
+        };
+        auto barrier = [&]() {
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        };
+        issue_copies(0, 0);
+        wait_copies<PER_STEP, 0>(0);
+        barrier();
+        if (nk > 1) issue_copies(1, 1);
+        load_frags(0, 0, 0);
+        int stage = 0;
+        for (int kt = 0; kt + 1 < nk; ++kt) {
+            load_frags(stage, 1, 1);
+            mfmas(0);
+            load_frags(stage, 2, 0);
+            mfmas(1);
+            load_frags(stage, 3, 1);
+            mfmas(0);
+            slot_reads();
+            slot_reads();
+            slot_reads();
+            wait_copies<PER_STEP, 0>(0);
+            barrier();
+            issue_copies(min(kt + 2, nk - 1), stage);
+            load_frags(stage ^ 1, 0, 0);
+            mfmas(1);
+            __builtin_amdgcn_sched_group_barrier(0x020, PER_STEP, 0);
+            slot_reads();
+            stage ^= 1;
+        }
+        load_frags(stage, 1, 1);
+        mfmas(0);
+        load_frags(stage, 2, 0);
+        mfmas(1);
+        load_frags(stage, 3, 1);
+        mfmas(0);
+        mfmas(1);
+        wait_copies<PER_STEP, 0>(0);  // the spare copy
+    } else {
 #pragma unroll
     for (int s = 0; s < NSTAGE - 1; ++s)
         if (s < nk) issue_copies(s, s);
@@ -301,6 +383,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
         if (kt + NSTAGE - 1 < nk) issue_copies(kt + NSTAGE - 1, (stage + NSTAGE - 1) % NSTAGE);
         compute(stage);
         stage = (stage + 1) % NSTAGE;
+    }
     }
 
     // epilogue; rows go back to their tokens, scaled by p_t for the out-projection
@@ -641,6 +724,8 @@ constexpr TileCfg kTiles[] = {
     {256, 256, 32, 4, 2, 4, 1},  // 6: as 1, interleaved
     {256, 256, 64, 2, 2, 2, 1},  // 7: 4 waves (128x128 each), BK 64, 2 stages, interleaved
     {320, 256, 64, 2, 2, 4, 1},  // 8: 8 waves (160x64 each), BK 64, 2 stages (144 KiB), C tile in 2 passes
+    {256, 256, 64, 2, 2, 4, 2},  // 9: as 0, barrier ahead of each step's last MFMAs
+    {320, 256, 64, 2, 2, 4, 2},  // 10: as 8, barrier ahead of each step's last MFMAs
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -669,7 +754,7 @@ static int device_cus() {
     return cached[dev];
 }
 
-// Default tile shape by problem: 256x256 blocks of 8 waves with interleaved fragment reads when there
+// Default tile shape by problem: 256x256 blocks of 8 waves with the early-barrier schedule when there
 // are enough rows and columns (measured best on MI355X at T = 16384), unless 320-row blocks need fewer
 // rounds of workgroups over the compute units for the same rows (rounds x rows per tile smaller; the
 // tile count is the launch's upper bound, as the host never reads the expert counts). Smaller blocks
@@ -679,7 +764,7 @@ static int default_tile(const GemmArgs &a, int nB) {
         const long cus = device_cus(), nt = (long)nB * (a.N0 / 256);
         const long t256 = (long)((a.T + (long)a.E * 255) / 256) * nt, t320 = (long)((a.T + (long)a.E * 319) / 320) * nt;
         const long r256 = (t256 + cus - 1) / cus, r320 = (t320 + cus - 1) / cus;
-        return r320 * 320 < r256 * 256 ? 8 : 2;
+        return r320 * 320 < r256 * 256 ? 10 : 9;
     }
     if (a.N0 % 128 == 0) return 4;
     return 5;
@@ -698,6 +783,8 @@ static hipError_t launch_bf16_auto(const GemmArgs &a, int nB, hipStream_t s) {
         case 6: return launch_bf16<256, 256, 32, 4, 2, 4, OUT, 1, KSPLIT>(a, nB, s);
         case 7: return launch_bf16<256, 256, 64, 2, 2, 2, OUT, 1, KSPLIT>(a, nB, s);
         case 8: return launch_bf16<320, 256, 64, 2, 2, 4, OUT, 1, KSPLIT>(a, nB, s);
+        case 9: return launch_bf16<256, 256, 64, 2, 2, 4, OUT, 2, KSPLIT>(a, nB, s);
+        case 10: return launch_bf16<320, 256, 64, 2, 2, 4, OUT, 2, KSPLIT>(a, nB, s);
         default: return launch_bf16<128, 64, 64, 4, 2, 2, OUT, 0, KSPLIT>(a, nB, s);
     }
 }
