@@ -21,7 +21,7 @@ struct GemmArgs {
     int n_tiles_per_b;    // N0 / BN
     int m_tiles;          // M-tiles launched (upper bound of the real ones)
     int group_m;          // XCD-aware order: M-tiles per group (0: plain row-major order)
-    int per_xcd;          // XCD-aware order: tiles assigned to each of the 8 XCDs
+    int per_xcd;          // XCD-aware order: tiles per chunk (the compute units of one XCD)
     int accumulate;       // 1: add to the values already in C (the second choice of a top-2 routing)
     int a_by_token;       // out-projection: A rows are in token order (gathered through perm), not slot order
     const void *A_hi;     // bf16 kernel, k_split > 0: columns [k_split, K) of the A rows come from A_hi

@@ -33,14 +33,16 @@ namespace rom {
 
 // Tile (mt, nt) of workgroup blockIdx.x; false if the workgroup has no tile.
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on XCD b % 8), each with its
-// own L2. With group_m > 0, XCD x takes the contiguous range [x * per_xcd, (x + 1) * per_xcd) of a
-// grouped order in which group_m consecutive M-tiles share every N-tile: the workgroups resident on
-// one XCD at a time then need group_m A tiles and about 32 / group_m B tiles, so most operand reads
-// hit that XCD's L2.
+// own L2. With group_m > 0 the tiles follow a grouped order in which group_m consecutive M-tiles share
+// every N-tile, cut into chunks of per_xcd tiles (the compute units of one XCD), and XCD x takes chunks
+// x, x + 8, x + 16, ...: the workgroups resident on one XCD at a time then need group_m A tiles and
+// per_xcd / group_m B tiles, so more operand reads hit that XCD's L2, and as the real tiles are a
+// prefix of the grouped order every XCD gets nearly the same number of them.
 __device__ __forceinline__ bool tile_of_block(const GemmArgs &p, int &mt, int &nt) {
     int L = blockIdx.x;
     if (p.group_m > 0) {
-        L = (blockIdx.x & 7) * p.per_xcd + (blockIdx.x >> 3);
+        const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+        L = ((j / p.per_xcd) * 8 + x) * p.per_xcd + j % p.per_xcd;
         const int span = p.group_m * p.n_tiles;
         const int g = L / span, in = L - g * span;
         mt = g * p.group_m + in % p.group_m;
@@ -288,14 +290,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
 
     const int nk = K / BK;
     if constexpr (SCHED == 2) {
-        // Two stages, the barrier moved ahead of the last sub-step's MFMAs: once a wave's fragment reads
-        // of stage kt and its copies of stage kt+1 are complete it joins the barrier, then issues the
-        // copies of step kt+2 into the stage just read and the first fragment reads of stage kt+1, and
-        // only then the last MFMAs of step kt, which cover the latency of those reads. The loop body is
-        // one block split only by the barrier (the step after the last copies again its own data into
-        // the free stage, in bounds and never read), so that the fragment reads can be slotted between
-        // the MFMAs.
-        static_assert(NSTAGE == 2 && BK == 64, "early-barrier schedule");
+        // Early-barrier schedule: once a wave's fragment reads of stage kt and its copies of step kt+1
+        // are complete it joins the barrier, then issues the copies of step kt+NSTAGE into the stage just
+        // read and the first fragment reads of step kt+1, and only then the last MFMAs of step kt, which
+        // cover the latency of those reads. Copies are in flight for NSTAGE-1 steps. The loop body is one
+        // block split only by the barrier: steps past the last copy the last step's data again into a
+        // stage that no later step reads (in bounds, never read), so the number of copies in flight is
+        // the same at every barrier and the fragment reads can be slotted between the MFMAs.
+        constexpr int NKK = BK / 16;  // MFMA sub-steps per K step
+        static_assert(NKK == 2 || NKK == 4, "early-barrier schedule");
         constexpr int NR = FM + FN, NM = FM * FN;
         constexpr int NG = (NR + 1) / 2;  // MFMAs that get fragment reads slotted after them
         static_assert(NM > NG, "read slots");
@@ -334,39 +337,39 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
             __builtin_amdgcn_s_barrier();
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
         };
-        issue_copies(0, 0);
-        wait_copies<PER_STEP, 0>(0);
+        // sub-steps 0 .. NKK-2 of the step in `stage`, each with the next sub-step's reads
+        auto body = [&](int stg) {
+#pragma unroll
+            for (int kk = 1; kk < NKK; ++kk) {
+                load_frags(stg, kk, kk & 1);
+                mfmas((kk - 1) & 1);
+            }
+#pragma unroll
+            for (int kk = 1; kk < NKK; ++kk) slot_reads();
+        };
+#pragma unroll
+        for (int s = 0; s + 1 < NSTAGE; ++s) issue_copies(min(s, nk - 1), s);
+        wait_copies<PER_STEP, NSTAGE - 2>(NSTAGE - 2);
         barrier();
-        if (nk > 1) issue_copies(1, 1);
+        issue_copies(min(NSTAGE - 1, nk - 1), NSTAGE - 1);
         load_frags(0, 0, 0);
         int stage = 0;
         for (int kt = 0; kt + 1 < nk; ++kt) {
-            load_frags(stage, 1, 1);
-            mfmas(0);
-            load_frags(stage, 2, 0);
-            mfmas(1);
-            load_frags(stage, 3, 1);
-            mfmas(0);
-            slot_reads();
-            slot_reads();
-            slot_reads();
-            wait_copies<PER_STEP, 0>(0);
+            body(stage);
+            __builtin_amdgcn_sched_barrier(0);  // the step's MFMAs stay ahead of the wait (they cover the reads)
+            wait_copies<PER_STEP, NSTAGE - 2>(NSTAGE - 2);
             barrier();
-            issue_copies(min(kt + 2, nk - 1), stage);
-            load_frags(stage ^ 1, 0, 0);
-            mfmas(1);
+            issue_copies(min(kt + NSTAGE, nk - 1), stage);
+            const int next = stage + 1 == NSTAGE ? 0 : stage + 1;
+            load_frags(next, 0, 0);
+            mfmas((NKK - 1) & 1);
             __builtin_amdgcn_sched_group_barrier(0x020, PER_STEP, 0);
             slot_reads();
-            stage ^= 1;
+            stage = next;
         }
-        load_frags(stage, 1, 1);
-        mfmas(0);
-        load_frags(stage, 2, 0);
-        mfmas(1);
-        load_frags(stage, 3, 1);
-        mfmas(0);
-        mfmas(1);
-        wait_copies<PER_STEP, 0>(0);  // the spare copy
+        body(stage);
+        mfmas((NKK - 1) & 1);
+        wait_copies<PER_STEP, 0>(0);  // the spare copies
     } else {
 #pragma unroll
     for (int s = 0; s < NSTAGE - 1; ++s)
@@ -671,6 +674,19 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs p) {
 
 // ---------------------------------------------------------------------------------------------
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 // XCD-aware grouping of M-tiles (0 = off); ROM_GROUP_M overrides it for tuning sweeps.
 static int group_m_choice() {
     static int cached = -2;
@@ -693,8 +709,9 @@ static hipError_t launch_bf16(const GemmArgs &a0, int nB, hipStream_t s) {
     if (a.group_m > 0) {
         const int groups = (a.m_tiles + a.group_m - 1) / a.group_m;
         const long total = (long)groups * a.group_m * a.n_tiles;
-        a.per_xcd = (int)((total + 7) / 8);
-        grid = (unsigned)a.per_xcd * 8;
+        a.per_xcd = max(1, device_cus() / 8);
+        const long round = 8L * a.per_xcd;
+        grid = (unsigned)((total + round - 1) / round * round);
     } else {
         grid = (unsigned)a.m_tiles * a.n_tiles;
     }
@@ -741,30 +758,20 @@ static int tile_override(bool out) {
     return c;
 }
 
-// Compute units of the current device (cached per device).
-static int device_cus() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
 
 // Default tile shape by problem: 256x256 blocks of 8 waves with the early-barrier schedule when there
 // are enough rows and columns (measured best on MI355X at T = 16384), unless 320-row blocks need fewer
 // rounds of workgroups over the compute units for the same rows (rounds x rows per tile smaller; the
-// tile count is the launch's upper bound, as the host never reads the expert counts). Smaller blocks
-// for small T or narrow N.
-static int default_tile(const GemmArgs &a, int nB) {
+// tile count is the launch's upper bound, as the host never reads the expert counts). The 320-row tile
+// with two A sources (KSPLIT) keeps the interleaved schedule: under the early-barrier one it spills
+// registers (the second set of copy pointers). Smaller blocks for small T or narrow N.
+static int default_tile(const GemmArgs &a, int nB, bool ksplit) {
     if (a.T >= 4096 && a.N0 % 256 == 0) {
         const long cus = device_cus(), nt = (long)nB * (a.N0 / 256);
         const long t256 = (long)((a.T + (long)a.E * 255) / 256) * nt, t320 = (long)((a.T + (long)a.E * 319) / 320) * nt;
         const long r256 = (t256 + cus - 1) / cus, r320 = (t320 + cus - 1) / cus;
-        return r320 * 320 < r256 * 256 ? 10 : 9;
+        if (r320 * 320 < r256 * 256) return ksplit ? 8 : 10;
+        return 9;
     }
     if (a.N0 % 128 == 0) return 4;
     return 5;
@@ -773,7 +780,7 @@ static int default_tile(const GemmArgs &a, int nB) {
 template <bool OUT, bool KSPLIT = false>
 static hipError_t launch_bf16_auto(const GemmArgs &a, int nB, hipStream_t s) {
     int t = tile_override(OUT);
-    if (t < 0 || a.N0 % kTiles[t].bn != 0) t = default_tile(a, nB);
+    if (t < 0 || a.N0 % kTiles[t].bn != 0) t = default_tile(a, nB, KSPLIT);
     switch (t) {
         case 0: return launch_bf16<256, 256, 64, 2, 2, 4, OUT, 0, KSPLIT>(a, nB, s);
         case 1: return launch_bf16<256, 256, 32, 4, 2, 4, OUT, 0, KSPLIT>(a, nB, s);
