@@ -391,27 +391,61 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
 
     // epilogue; rows go back to their tokens, scaled by p_t for the out-projection
     if (p.accumulate) {
-        // C += result, straight from the C^T-layout registers (one rounding of the sum): register r of
-        // block (i, j) holds column 8*(r/4) + 4*half + r%4 of token row lane%32
+        // C += result (one rounding of the sum), through LDS in fp32: pass q takes block rows
+        // [q*IPP, q*IPP + IPP) of every wave, i.e. rows wm*WM + i*32 + (0..31) of the tile. Register r of block
+        // (i, j) holds column 8*(r/4) + 4*half + r%4 of row lane%32; it is written as 4-float chunks
+        // (16-byte chunk index XOR-swizzled by the pass row), then every thread adds 8 consecutive columns to
+        // the stored bf16 values of a token row with 16-byte loads and stores.
+        constexpr int CPR4 = BN / 4;                                  // 16-byte fp32 chunks per row
+        constexpr int PROWS = WGM * 32;                               // pass rows per block row
+        constexpr int IPP = (int)(gemm_lds_bytes(BM, BN, BK, NSTAGE, WGM) / ((size_t)PROWS * BN * 4));
+        static_assert(IPP >= 1, "fp32 accumulate pass");
+        constexpr int NPASS = (FM + IPP - 1) / IPP;
+        constexpr int SWM = (CPR4 < 32 ? CPR4 : 32) - 1;             // chunk swizzle mask (stays in the row)
+        float *ct = reinterpret_cast<float *>(smem);
+        auto prow_of = [&](int wmr, int ii, int r) { return (ii * WGM + wmr) * 32 + r; };  // LDS row
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int row = wm * WM + i * 32 + (lane & 31);
-            if (row < rows) {
-                const float sc = OUT ? s_prob[row] : 1.0f;
-                uint16_t *crow = C + (size_t)s_tok[row] * p.N0 + n0 + wn * WN + 4 * half;
+        for (int q = 0; q < NPASS; ++q) {
+            __syncthreads();
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
+            for (int ii = 0; ii < IPP; ++ii) {
+                const int i = q * IPP + ii;
+                if (i < FM) {
+                    const int lr = prow_of(wm, ii, lane & 31);
+                    const float sc = OUT ? s_prob[wm * WM + i * 32 + (lane & 31)] : 1.0f;
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        uint2 *dst = reinterpret_cast<uint2 *>(crow + j * 32 + 8 * g);
-                        const uint2 old = *dst;
-                        uint2 pk;
-                        pk.x = pack_bf16x2(fmaf(acc[i][j][4 * g], sc, __uint_as_float(old.x << 16)),
-                                           fmaf(acc[i][j][4 * g + 1], sc, __uint_as_float(old.x & 0xFFFF0000u)));
-                        pk.y = pack_bf16x2(fmaf(acc[i][j][4 * g + 2], sc, __uint_as_float(old.y << 16)),
-                                           fmaf(acc[i][j][4 * g + 3], sc, __uint_as_float(old.y & 0xFFFF0000u)));
-                        *dst = pk;
-                    }
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const int ch = (wn * WN + j * 32 + 8 * g + 4 * half) >> 2;
+                            float4 v;
+                            v.x = acc[i][j][4 * g] * sc;
+                            v.y = acc[i][j][4 * g + 1] * sc;
+                            v.z = acc[i][j][4 * g + 2] * sc;
+                            v.w = acc[i][j][4 * g + 3] * sc;
+                            *reinterpret_cast<float4 *>(ct + lr * BN + ((ch ^ (lr & SWM)) << 2)) = v;
+                        }
+                }
+            }
+            __syncthreads();
+            constexpr int CPR = BN / 8;  // 8-column units per row
+            const int units = IPP * PROWS * CPR;
+            for (int u = tid; u < units; u += NT) {
+                const int lr = u / CPR, c = u % CPR;
+                const int ii = lr / PROWS, wmr = (lr / 32) % WGM, i = q * IPP + ii;
+                const int row = wmr * WM + i * 32 + (lr & 31);  // tile row
+                if (i < FM && row < rows) {
+                    uint4 *dst = reinterpret_cast<uint4 *>(C + (size_t)s_tok[row] * p.N0 + n0 + c * 8);
+                    const uint4 old = *dst;
+                    const float4 a = *reinterpret_cast<const float4 *>(ct + lr * BN + (((2 * c) ^ (lr & SWM)) << 2));
+                    const float4 b = *reinterpret_cast<const float4 *>(ct + lr * BN + (((2 * c + 1) ^ (lr & SWM)) << 2));
+                    uint4 pk;
+                    pk.x = pack_bf16x2(__uint_as_float(old.x << 16) + a.x, __uint_as_float(old.x & 0xFFFF0000u) + a.y);
+                    pk.y = pack_bf16x2(__uint_as_float(old.y << 16) + a.z, __uint_as_float(old.y & 0xFFFF0000u) + a.w);
+                    pk.z = pack_bf16x2(__uint_as_float(old.z << 16) + b.x, __uint_as_float(old.z & 0xFFFF0000u) + b.y);
+                    pk.w = pack_bf16x2(__uint_as_float(old.w << 16) + b.z, __uint_as_float(old.w & 0xFFFF0000u) + b.w);
+                    *dst = pk;
+                }
             }
         }
         return;
@@ -739,10 +773,9 @@ constexpr TileCfg kTiles[] = {
     {128, 128, 64, 4, 2, 2, 0},  // 4: 4 waves (64x64 each), BK 64, 4 stages (128 KiB)
     {128, 64, 64, 4, 2, 2, 0},   // 5: 4 waves (64x32 each), BK 64, 4 stages (96 KiB)
     {256, 256, 32, 4, 2, 4, 1},  // 6: as 1, interleaved
-    {256, 256, 64, 2, 2, 2, 1},  // 7: 4 waves (128x128 each), BK 64, 2 stages, interleaved
-    {320, 256, 64, 2, 2, 4, 1},  // 8: 8 waves (160x64 each), BK 64, 2 stages (144 KiB), C tile in 2 passes
-    {256, 256, 64, 2, 2, 4, 2},  // 9: as 0, barrier ahead of each step's last MFMAs
-    {320, 256, 64, 2, 2, 4, 2},  // 10: as 8, barrier ahead of each step's last MFMAs
+    {320, 256, 64, 2, 2, 4, 1},  // 7: 8 waves (160x64 each), BK 64, 2 stages (144 KiB), C tile in 2 passes
+    {256, 256, 64, 2, 2, 4, 2},  // 8: as 0, barrier ahead of each step's last MFMAs
+    {320, 256, 64, 2, 2, 4, 2},  // 9: as 7, barrier ahead of each step's last MFMAs
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -770,8 +803,8 @@ static int default_tile(const GemmArgs &a, int nB, bool ksplit) {
         const long cus = device_cus(), nt = (long)nB * (a.N0 / 256);
         const long t256 = (long)((a.T + (long)a.E * 255) / 256) * nt, t320 = (long)((a.T + (long)a.E * 319) / 320) * nt;
         const long r256 = (t256 + cus - 1) / cus, r320 = (t320 + cus - 1) / cus;
-        if (r320 * 320 < r256 * 256) return ksplit ? 8 : 10;
-        return 9;
+        if (r320 * 320 < r256 * 256) return ksplit ? 7 : 9;
+        return 8;
     }
     if (a.N0 % 128 == 0) return 4;
     return 5;
@@ -788,10 +821,9 @@ static hipError_t launch_bf16_auto(const GemmArgs &a, int nB, hipStream_t s) {
         case 3: return launch_bf16<256, 128, 64, 3, 2, 2, OUT, 0, KSPLIT>(a, nB, s);
         case 4: return launch_bf16<128, 128, 64, 4, 2, 2, OUT, 0, KSPLIT>(a, nB, s);
         case 6: return launch_bf16<256, 256, 32, 4, 2, 4, OUT, 1, KSPLIT>(a, nB, s);
-        case 7: return launch_bf16<256, 256, 64, 2, 2, 2, OUT, 1, KSPLIT>(a, nB, s);
-        case 8: return launch_bf16<320, 256, 64, 2, 2, 4, OUT, 1, KSPLIT>(a, nB, s);
-        case 9: return launch_bf16<256, 256, 64, 2, 2, 4, OUT, 2, KSPLIT>(a, nB, s);
-        case 10: return launch_bf16<320, 256, 64, 2, 2, 4, OUT, 2, KSPLIT>(a, nB, s);
+        case 7: return launch_bf16<320, 256, 64, 2, 2, 4, OUT, 1, KSPLIT>(a, nB, s);
+        case 8: return launch_bf16<256, 256, 64, 2, 2, 4, OUT, 2, KSPLIT>(a, nB, s);
+        case 9: return launch_bf16<320, 256, 64, 2, 2, 4, OUT, 2, KSPLIT>(a, nB, s);
         default: return launch_bf16<128, 64, 64, 4, 2, 2, OUT, 0, KSPLIT>(a, nB, s);
     }
 }
