@@ -86,14 +86,15 @@ __device__ __forceinline__ bool locate_mtile(const int32_t *__restrict__ offsets
 // Staging: A and B rows are copied global -> LDS directly (global_load_lds_dwordx4: lane i of a
 // wave writes 16 bytes at LDS base + 16*i), NSTAGE-1 K steps ahead of the MFMAs, with no register
 // round trip; before each step a wave waits only until its copies for that step have landed
-// (vmcnt counts the later steps' copies still in flight), then the workgroup meets at a barrier.
+// (vmcnt counts the later steps' copies still in flight), then the workgroup meets at a barrier
+// (in the default schedule, ahead of the step's last MFMAs: see the main loop).
 // LDS rows hold BK bf16 values as BK/8 16-byte chunks; chunk c of row r sits at c ^ swz(r) so the
 // MFMA operand reads (16 lanes = 16 consecutive rows, one chunk each) spread over all banks.
 //
 // The MFMA computes the transposed tile C^T = W A^T (W operand first): a lane's 16 accumulators of
 // a 32x32 block belong to ONE token row (lane % 32) and hold 4 runs of 4 consecutive output columns,
-// so the epilogue scales them by that token's probability and writes 8-byte packed stores straight
-// to the token's output row (the un-permute).
+// which the epilogue scales by that token's probability and sends to the token's output row (the
+// un-permute).
 // ---- staged epilogue. Scattering the C^T-layout accumulators straight to the token rows costs one
 // store instruction per 8 bytes and touches 32 rows (cache lines) per instruction. Instead each wave
 // writes its block, converted to bf16 and scaled per row, into an LDS tile of BM x BN, and the
@@ -151,7 +152,8 @@ __device__ __forceinline__ void ctile_to_global(const uint16_t *ct, int nrows, i
 
 // LDS of a bf16 tile configuration: the pipeline stages, or the C tile of the epilogue if larger.
 // The C tile goes through LDS in one pass when BM x BN bf16 fits in 144 KiB, otherwise in WGM passes of
-// BM / WGM rows (one row band of waves at a time).
+// BM / WGM rows (one row band of waves at a time). The accumulate epilogue (second choice of a top-2
+// routing) reuses the same bytes for its fp32 passes.
 constexpr int ctile_passes(int BM, int BN, int WGM) { return BM * BN * 2 <= 144 * 1024 ? 1 : WGM; }
 constexpr size_t gemm_lds_bytes(int BM, int BN, int BK, int NSTAGE, int WGM) {
     const int crows = BM / ctile_passes(BM, BN, WGM);
