@@ -28,25 +28,21 @@ namespace rom {
 constexpr int kRouteLdsW = 64 * 1024;
 
 // W_r [d_model][E] -> LDS as float4 words: word (kk, x4, c) holds W_r[8c+kk][4*x4 .. 4*x4+4), stored at
-// ((kk * E/4 + x4) * nchunk + c), so lanes reading consecutive chunks c read consecutive words.
-// Requires E % 4 == 0. Reads global W_r coalesced; every thread of the workgroup takes part.
+// d = ((kk * E/4 + x4) * nchunk + c), so lanes reading consecutive chunks c read consecutive words.
+// Requires E % 4 == 0. The words are copied global -> LDS directly (global_load_lds_dwordx4, no register
+// stage): copy m of the workgroup fills words [64 m, 64 m + 64), lane i reading the source word of
+// destination word 64 m + i, and wave w issues copies w, w + 4, ... (dm * E/4 is a multiple of 64, as
+// d_model is). Completion is tracked by vmcnt like any load: call it before the X rows are issued, and
+// wait for all loads (vmcnt(0)) before the barrier that precedes the reads.
 __device__ __forceinline__ void stage_router_weight(const float *__restrict__ Wr, int dm, int E, float4 *wl) {
-    // W_r as dm*E/4 float4 words, at most kRouteLdsW/16 = 4096 of them: a 256-thread workgroup moves
-    // at most 16 words per thread. All loads are issued before any store (indices past the end are
-    // clamped and not stored). Requires E/4 to be a power of two.
     const int e4 = E >> 2, nchunk = dm >> 3, n4 = dm * e4;
-    const int sh = __builtin_ctz(e4);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const float4 *src = reinterpret_cast<const float4 *>(Wr);
-    float4 v[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = src[min((int)threadIdx.x + j * 256, n4 - 1)];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int g = threadIdx.x + j * 256;
-        if (g < n4) {
-            const int k = g >> sh, x4 = g & (e4 - 1);
-            wl[((k & 7) * e4 + x4) * nchunk + (k >> 3)] = v[j];
-        }
+    for (int m = wave; m * 64 < n4; m += 4) {
+        const int d = m * 64 + lane;
+        const int q = d / nchunk, c = d - q * nchunk;  // q = kk * e4 + x4
+        const int kk = q / e4, x4 = q - kk * e4;
+        dma16_to_lds(src + (8 * c + kk) * e4 + x4, wl + m * 64);
     }
 }
 
@@ -336,13 +332,14 @@ __global__ __launch_bounds__(256) void k_route_logits(const TX *__restrict__ X, 
     __shared__ float s_red[WPG == 4 ? 4 : 1][8][EMAX];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int i = tid; i < K * E; i += 256) hist[i] = 0;
+    if (use_lds) stage_router_weight(Wr, dm, E, wl_dyn);
     XRows<TX> xr;
     {
         int g0, jl;
         wg_token_group<WPG>(blockIdx.x * TPW, g0, jl);
         xrows_issue<TX, WPG * 64>(xr, X, T, dm, g0, jl);
     }
-    if (use_lds) stage_router_weight(Wr, dm, E, wl_dyn);
+    if (use_lds) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // the W_r copies (and the X rows) have landed
     __syncthreads();
     float lg[EMAX];
     const int tok0 = wg_logits<TX, EG, EMAX, WPG>(xr, X, T, dm, Wr, use_lds ? wl_dyn : nullptr, E, blockIdx.x * TPW,
@@ -445,13 +442,14 @@ __global__ __launch_bounds__(256) void k_route_small(const TX *__restrict__ X, i
     __shared__ int s_pos[kRouteSmallT];
     __shared__ float s_red[4][8][EMAX];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (use_lds) stage_router_weight(Wr, dm, E, wl_dyn);
     XRows<TX> xr;
     {
         int g0, jl;
         wg_token_group<4>(0, g0, jl);
         xrows_issue<TX, 256>(xr, X, T, dm, g0, jl);
     }
-    if (use_lds) stage_router_weight(Wr, dm, E, wl_dyn);
+    if (use_lds) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // the W_r copies (and the X rows) have landed
     __syncthreads();
     float lg[EMAX];
     wg_logits<TX, EG, EMAX, 4>(xr, X, T, dm, Wr, use_lds ? wl_dyn : nullptr, E, 0, lg, s_red);
