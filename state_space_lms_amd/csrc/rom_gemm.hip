@@ -794,18 +794,21 @@ static int tile_override(bool out) {
 }
 
 
-// Default tile shape by problem: 256x256 blocks of 8 waves with the early-barrier schedule when there
-// are enough rows and columns (measured best on MI355X at T = 16384), unless 320-row blocks need fewer
-// rounds of workgroups over the compute units for the same rows (rounds x rows per tile smaller; the
-// tile count is the launch's upper bound, as the host never reads the expert counts). The 320-row tile
-// with two A sources (KSPLIT) keeps the interleaved schedule: under the early-barrier one it spills
-// registers (the second set of copy pointers). Smaller blocks for small T or narrow N.
+// Default tile shape by problem: with enough rows and columns, 8-wave blocks of 320 x 256 or 256 x 256 with
+// the early-barrier schedule (measured best on MI355X at T = 16384 and 65536). 320-row blocks move 10% fewer
+// operand bytes per flop (operand copies, not MFMAs, limit these kernels), so they are taken unless their extra
+// padding is large: the launch's upper bound on padded rows, T + E*(BM-1), must grow by at most 5% over
+// 256-row blocks, or the 320-row blocks must need fewer rounds of workgroups over the compute units for the
+// same rows (rounds x rows per tile smaller; the host never reads the expert counts). The 320-row tile with two
+// A sources (KSPLIT) keeps the interleaved schedule: under the early-barrier one it spills registers (the
+// second set of copy pointers). Smaller blocks for small T or narrow N.
 static int default_tile(const GemmArgs &a, int nB, bool ksplit) {
     if (a.T >= 4096 && a.N0 % 256 == 0) {
         const long cus = device_cus(), nt = (long)nB * (a.N0 / 256);
-        const long t256 = (long)((a.T + (long)a.E * 255) / 256) * nt, t320 = (long)((a.T + (long)a.E * 319) / 320) * nt;
+        const long rows256 = a.T + (long)a.E * 255, rows320 = a.T + (long)a.E * 319;
+        const long t256 = rows256 / 256 * nt, t320 = rows320 / 320 * nt;
         const long r256 = (t256 + cus - 1) / cus, r320 = (t320 + cus - 1) / cus;
-        if (r320 * 320 < r256 * 256) return ksplit ? 7 : 9;
+        if (rows320 * 20 <= rows256 * 21 || r320 * 320 < r256 * 256) return ksplit ? 7 : 9;
         return 8;
     }
     if (a.N0 % 128 == 0) return 4;
