@@ -206,14 +206,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
     const int dr = lane / KCH, dpc = lane % KCH;
     const uint16_t *a_dma[A_DMA];
     const uint16_t *b_dma[B_DMA];
-    const uint16_t *a_hi[A_DMA];
     const int k_lo = KSPLIT ? p.k_split : K;  // row length of A0
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) {
         const int row = (wave * A_DMA + j) * RG + dr;
         const int c = dpc ^ lds_swz<KCH>(row);
         a_dma[j] = static_cast<const uint16_t *>(p.A0) + (size_t)s_arow[row] * k_lo + c * 8;
-        a_hi[j] = KSPLIT ? static_cast<const uint16_t *>(p.A_hi) + (size_t)s_arow[row] * (K - k_lo) + c * 8 : a_dma[j];
     }
 #pragma unroll
     for (int j = 0; j < B_DMA; ++j) {
@@ -221,14 +219,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
         const int c = dpc ^ lds_swz<KCH>(row);
         b_dma[j] = Bsrc + (size_t)row * K + c * 8;
     }
+    // KSPLIT: copies are issued in increasing k, so the A sources switch to A_hi once, at the first step at
+    // or past k_split (rows re-read from LDS; a second pointer set would cost registers all along)
+    bool a_in_hi = false;
     auto issue_copies = [&](int kt, int stage) {
         uint16_t *as = smem + stage * STAGE;
         uint16_t *bs = as + BM * BK;
         const int k0 = kt * BK;
-        const bool hi = KSPLIT && k0 >= k_lo;  // uniform
+        if (KSPLIT && !a_in_hi && k0 >= k_lo) {  // uniform
 #pragma unroll
-        for (int j = 0; j < A_DMA; ++j)
-            dma16_to_lds(hi ? a_hi[j] + (k0 - k_lo) : a_dma[j] + k0, as + (wave * A_DMA + j) * RG * BK);
+            for (int j = 0; j < A_DMA; ++j) {
+                const int row = (wave * A_DMA + j) * RG + dr;
+                const int c = dpc ^ lds_swz<KCH>(row);
+                a_dma[j] = static_cast<const uint16_t *>(p.A_hi) + (size_t)s_arow[row] * (K - k_lo) + c * 8;
+            }
+            a_in_hi = true;
+        }
+        const int ka = KSPLIT && a_in_hi ? k0 - k_lo : k0;
+#pragma unroll
+        for (int j = 0; j < A_DMA; ++j) dma16_to_lds(a_dma[j] + ka, as + (wave * A_DMA + j) * RG * BK);
 #pragma unroll
         for (int j = 0; j < B_DMA; ++j) dma16_to_lds(b_dma[j] + k0, bs + (wave * B_DMA + j) * RG * BK);
     };
@@ -799,16 +808,15 @@ static int tile_override(bool out) {
 // operand bytes per flop (operand copies, not MFMAs, limit these kernels), so they are taken unless their extra
 // padding is large: the launch's upper bound on padded rows, T + E*(BM-1), must grow by at most 5% over
 // 256-row blocks, or the 320-row blocks must need fewer rounds of workgroups over the compute units for the
-// same rows (rounds x rows per tile smaller; the host never reads the expert counts). The 320-row tile with two
-// A sources (KSPLIT) keeps the interleaved schedule: under the early-barrier one it spills registers (the
-// second set of copy pointers). Smaller blocks for small T or narrow N.
-static int default_tile(const GemmArgs &a, int nB, bool ksplit) {
+// same rows (rounds x rows per tile smaller; the host never reads the expert counts). Smaller blocks for small T
+// or narrow N.
+static int default_tile(const GemmArgs &a, int nB) {
     if (a.T >= 4096 && a.N0 % 256 == 0) {
         const long cus = device_cus(), nt = (long)nB * (a.N0 / 256);
         const long rows256 = a.T + (long)a.E * 255, rows320 = a.T + (long)a.E * 319;
         const long t256 = rows256 / 256 * nt, t320 = rows320 / 320 * nt;
         const long r256 = (t256 + cus - 1) / cus, r320 = (t320 + cus - 1) / cus;
-        if (rows320 * 20 <= rows256 * 21 || r320 * 320 < r256 * 256) return ksplit ? 7 : 9;
+        if (rows320 * 20 <= rows256 * 21 || r320 * 320 < r256 * 256) return 9;
         return 8;
     }
     if (a.N0 % 128 == 0) return 4;
@@ -818,7 +826,7 @@ static int default_tile(const GemmArgs &a, int nB, bool ksplit) {
 template <bool OUT, bool KSPLIT = false>
 static hipError_t launch_bf16_auto(const GemmArgs &a, int nB, hipStream_t s) {
     int t = tile_override(OUT);
-    if (t < 0 || a.N0 % kTiles[t].bn != 0) t = default_tile(a, nB, KSPLIT);
+    if (t < 0 || a.N0 % kTiles[t].bn != 0) t = default_tile(a, nB);
     switch (t) {
         case 0: return launch_bf16<256, 256, 64, 2, 2, 4, OUT, 0, KSPLIT>(a, nB, s);
         case 1: return launch_bf16<256, 256, 32, 4, 2, 4, OUT, 0, KSPLIT>(a, nB, s);
