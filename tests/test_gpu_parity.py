@@ -256,6 +256,8 @@ TOP2 = [
     workloads.custom_workload("top2_T40_decode", T=40, d_model=256, d_inner=320, E=4, seed=206),
     workloads.custom_workload("top2_T64_decode", T=64, d_model=512, d_inner=256, E=8, seed=207),
     workloads.custom_workload("top2_wide_route", T=16400, d_model=128, d_inner=128, E=8, seed=208),
+    # 256-row early-barrier tiles (their padding rules out 320 rows here) with the fp32 accumulate epilogue
+    workloads.custom_workload("top2_T4096_tiles256", T=4096, d_model=512, d_inner=512, E=8, seed=210),
 ]
 
 
