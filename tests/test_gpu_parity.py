@@ -266,6 +266,33 @@ def test_top2_small_shapes(rom, oracle, w):
     check_workload_top2(rom, oracle, w)
 
 
+def _random_shapes(n, seed):
+    """Seeded random shapes over the supported range: T, E (including odd and non-power-of-two counts), widths,
+    top-1 or top-2, bf16 or fp32. Every token is compared."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 3, 4, 5, 8, 16, 33, 64]))
+        k = 2 if E >= 2 and rng.random() < 0.4 else 1
+        T = int(rng.integers(1, 2500))
+        dm, di = 64 * int(rng.integers(1, 9)), 64 * int(rng.integers(1, 9))
+        dtype = "f32" if rng.random() < 0.2 else "bf16"
+        name = f"rand{i}_T{T}_dm{dm}_di{di}_E{E}_top{k}_{dtype}"
+        out.append((workloads.custom_workload(name, T=T, d_model=dm, d_inner=di, E=E, dtype=dtype, seed=700 + i), k))
+    return out
+
+
+RANDOM = _random_shapes(24, 2024)
+
+
+@pytest.mark.parametrize("w,k", RANDOM, ids=[w.name for w, _ in RANDOM])
+def test_random_shapes(rom, oracle, w, k):
+    if k == 1:
+        check_workload(rom, oracle, w)
+    else:
+        check_workload_top2(rom, oracle, w)
+
+
 def test_top2_hot_expert(rom, oracle):
     """A dominant bias: every token's first choice is expert 3, the second spreads over the others."""
     w = workloads.custom_workload("top2_hot", T=700, d_model=128, d_inner=128, E=8, seed=209)
