@@ -32,16 +32,19 @@ constexpr int kRouteLdsW = 64 * 1024;
 // Requires E % 4 == 0. The words are copied global -> LDS directly (global_load_lds_dwordx4, no register
 // stage): copy m of the workgroup fills words [64 m, 64 m + 64), lane i reading the source word of
 // destination word 64 m + i, and wave w issues copies w, w + 4, ... (dm * E/4 is a multiple of 64, as
-// d_model is). Completion is tracked by vmcnt like any load: call it before the X rows are issued, and
-// wait for all loads (vmcnt(0)) before the barrier that precedes the reads.
+// d_model is). Completion is tracked by vmcnt like any load, in issue order: call it before the X rows
+// are issued, and before the barrier that precedes the reads wait until at most the loads issued after
+// it are in flight. Requires E/4 to be a power of two and dm * E/4 <= 4096 words (64 KiB): d / nchunk is
+// then umulhi(d, floor((2^32 - 1) / nchunk) + 1), exact for d * nchunk < 2^32, and the rest are shifts.
 __device__ __forceinline__ void stage_router_weight(const float *__restrict__ Wr, int dm, int E, float4 *wl) {
-    const int e4 = E >> 2, nchunk = dm >> 3, n4 = dm * e4;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const unsigned e4 = (unsigned)E >> 2, nchunk = (unsigned)dm >> 3, n4 = (unsigned)dm * e4;
+    const unsigned lg_e4 = __builtin_ctz(e4), magic = 0xFFFFFFFFu / nchunk + 1u;
+    const unsigned lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const float4 *src = reinterpret_cast<const float4 *>(Wr);
-    for (int m = wave; m * 64 < n4; m += 4) {
-        const int d = m * 64 + lane;
-        const int q = d / nchunk, c = d - q * nchunk;  // q = kk * e4 + x4
-        const int kk = q / e4, x4 = q - kk * e4;
+    for (unsigned m = wave; m * 64 < n4; m += 4) {
+        const unsigned d = m * 64 + lane;
+        const unsigned q = __umulhi(d, magic), c = d - q * nchunk;  // q = kk * e4 + x4
+        const unsigned kk = q >> lg_e4, x4 = q & (e4 - 1);
         dma16_to_lds(src + (8 * c + kk) * e4 + x4, wl + m * 64);
     }
 }
@@ -80,6 +83,17 @@ template <typename TX> struct XRows {
     const TX *row[8];
     Chunk8<TX> a[8], b[8];
 };
+
+// s_barrier without the memory fence of __syncthreads(): the caller has waited for what the other
+// waves read after it.
+__device__ __forceinline__ void barrier_no_fence() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Vector loads per chunk set of XRows (one set = one 8-element chunk of each of the 8 rows).
+template <typename TX> constexpr int kXrowsSetLoads = 8 * (int)sizeof(TX) / 2;
 
 // Issues the loads of chunks jl and jl+LPT. Called before the router weight is staged, so that the first
 // X fetches overlap the staging.
@@ -333,14 +347,20 @@ __global__ __launch_bounds__(256) void k_route_logits(const TX *__restrict__ X, 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int i = tid; i < K * E; i += 256) hist[i] = 0;
     if (use_lds) stage_router_weight(Wr, dm, E, wl_dyn);
+    __builtin_amdgcn_sched_barrier(0);  // the W_r copies stay ahead of the X loads (vmcnt counts in issue order)
     XRows<TX> xr;
     {
         int g0, jl;
         wg_token_group<WPG>(blockIdx.x * TPW, g0, jl);
         xrows_issue<TX, WPG * 64>(xr, X, T, dm, g0, jl);
     }
-    if (use_lds) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // the W_r copies (and the X rows) have landed
-    __syncthreads();
+    // This wave's W_r copies have landed once at most the first chunk set of its 8 rows (8 loads per
+    // set, 16 for fp32) is in flight, and its LDS stores at lgkmcnt(0). Then a plain barrier: the fence of
+    // __syncthreads() would also wait for every X load, while kept in flight they let the FMAs of the
+    // first chunks start as those arrive instead of after the last row's.
+    if (use_lds) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kXrowsSetLoads<TX>));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+    barrier_no_fence();
     float lg[EMAX];
     const int tok0 = wg_logits<TX, EG, EMAX, WPG>(xr, X, T, dm, Wr, use_lds ? wl_dyn : nullptr, E, blockIdx.x * TPW,
                                                   lg, s_red);

@@ -105,6 +105,9 @@ SMALL = [
     workloads.custom_workload("bf16_T9_split_route", T=9, d_model=512, d_inner=128, E=4, seed=114),
     workloads.custom_workload("bf16_wide_route_E64", T=16400, d_model=128, d_inner=128, E=64, seed=115),
     workloads.custom_workload("bf16_wide_route_E3", T=16421, d_model=192, d_inner=128, E=3, seed=116),
+    # wide router with W_r in LDS and fp32 rows: 144 chunks per row, so every lane has a second chunk in
+    # flight at the barrier and some refill a third time
+    workloads.custom_workload("f32_wide_route_dm1152", T=16400, d_model=1152, d_inner=128, E=8, dtype="f32", seed=117),
     workloads.custom_workload("f32_E5", T=333, d_model=128, d_inner=192, E=5, dtype="f32", seed=111),
     workloads.custom_workload("f32_T1000_E8", T=1000, d_model=64, d_inner=128, E=8, dtype="f32", seed=112),
 ]
