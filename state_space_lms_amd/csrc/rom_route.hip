@@ -17,8 +17,12 @@
 //
 // Launches: T <= 8: one workgroup does everything. Otherwise (1) logits + top-1 + per-workgroup
 // histogram, 32 tokens per workgroup when that gives >= 512 workgroups (one wave per 8 tokens), else
-// 8 tokens per workgroup (the four waves split d_model); (2) per-expert totals and bases, stable
-// scatter (ballot ranks inside each 256-token workgroup), optional permute.
+// 8 tokens per workgroup (the four waves split d_model); on that wide path bf16 rows with 8 experts and
+// d_model in {512, 1024, 1536, 2048} go to the matrix cores instead (k_route_logits_mfma, 64 tokens per
+// workgroup); (2) per-expert totals and bases, stable scatter (ballot ranks inside each 256-token
+// workgroup), optional permute.
+#include <type_traits>
+
 #include "rom_device.h"
 #include "rom_internal.h"
 
@@ -382,6 +386,139 @@ __global__ __launch_bounds__(256) void k_route_logits(const TX *__restrict__ X, 
     for (int i = tid; i < K * E; i += 256) wg_counts[(size_t)i * nwg + blockIdx.x] = hist[i];
 }
 
+// Multi-workgroup path, kernel 1 on the matrix cores (bf16 X, E = 8, d_model = 32 NKS with NKS a
+// multiple of 16 up to 64): logits, top-K, probability and this workgroup's histogram for 64 tokens (16
+// per wave), with the same outputs as k_route_logits.
+//
+// fp32 W_r is split exactly into three bf16 parts, w = hi + mid + lo: hi = bf16(w), mid = bf16(w - hi),
+// lo = w - hi - mid (both differences are exact in fp32, and lo has at most 8 significant bits, so bf16
+// holds it). A bf16 x times a bf16 part is exact in fp32 and the MFMA adds in fp32, so every logit is an
+// fp32 sum of the exact products x_k * w_k, in another order than the VALU kernel's.
+//
+// v_mfma_f32_16x16x32_bf16 with the parts as the first operand (16 rows) and 16 tokens as the second:
+// lane l supplies row (or token) l % 16 and features 8 (l / 16) .. + 8 of a 32-feature step, and
+// receives rows 4 (l / 16) + i, i = 0..3, of token l % 16. One MFMA per step on the main table (rows
+// 0..7 hi of experts 0..7, rows 8..15 mid) and one on the low table (rows 0..7 lo, rows 8..15 zero).
+// Lanes 0..15 then hold hi + lo of experts 0..3, lanes 16..31 of experts 4..7, lanes 32..63 the mids:
+// two shuffles give lanes 0..15 all 8 logits of their token.
+//
+// LDS tables, in 16-byte words, for feature octet o = 4 s + g (features 8 o .. 8 o + 7):
+//   main[o * 16 + r]: r < 8 hi of expert r, r >= 8 mid of expert r - 8;  low[o * 8 + r]: lo of expert r.
+// At step s lane l reads main word 64 s + l (one contiguous KiB per wave) and low word 32 s + 8 g + (l & 7).
+//
+// Each lane streams its token row through a ring of kRouteMfmaRing 16-byte loads, refilled as the MFMAs
+// consume them; everything is unrolled at compile time, so each MFMA waits only for its own load. The
+// W_r values for the tables are loaded before the X rows and split while those are in flight.
+constexpr int kRouteMfmaTokensPerWG = 64;
+constexpr int kRouteMfmaRing = 16;
+constexpr size_t route_mfma_lds_bytes(int dm) { return (size_t)dm / 8 * 24 * 16; }
+
+template <int NKS>
+__global__ __launch_bounds__(256) void k_route_logits_mfma(const uint16_t *__restrict__ X, int T,
+                                                           const float *__restrict__ Wr,
+                                                           const float *__restrict__ bias, int K,
+                                                           int32_t *__restrict__ ids, float *__restrict__ prob,
+                                                           int32_t *__restrict__ wg_counts, int nwg) {
+    constexpr int DM = NKS * 32, NOCT = DM / 8, NIT = NOCT * 8 / 256, R = kRouteMfmaRing;
+    static_assert(NKS % 16 == 0 && NKS >= R && NIT >= 1, "shape");
+    extern __shared__ uint4 rt_dyn[];
+    __shared__ int hist[ROM_MAX_TOP_K * 8];
+    uint4 *tmain = rt_dyn, *tlow = rt_dyn + NOCT * 16;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid < K * 8) hist[tid] = 0;
+
+    // table items q = tid + 256 it: expert e = q & 7 of octet o = q >> 3 (8 consecutive lanes read one
+    // 32-byte W_r row)
+    float wv[NIT][8];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int q = tid + 256 * it, e = q & 7, o = q >> 3;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wv[it][j] = Wr[(size_t)(8 * o + j) * 8 + e];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the W_r loads go out ahead of the X rows
+
+    const int r16 = lane & 15, g = lane >> 4;
+    const int tok0 = blockIdx.x * kRouteMfmaTokensPerWG + wave * 16;
+    const uint16_t *xp = X + (size_t)min(tok0 + r16, T - 1) * DM + 8 * g;  // + 32 s for step s
+    uint4 ring[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) ring[u] = *reinterpret_cast<const uint4 *>(xp + 32 * u);
+    __builtin_amdgcn_sched_barrier(0);  // the X rows are in flight before the first wait for W_r
+
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int q = tid + 256 * it, e = q & 7, o = q >> 3;
+        uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            float rm[2], rl[2];
+            uint16_t bh[2], bm[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const float w = wv[it][2 * h + b];
+                bh[b] = f32_to_bf16(w);
+                rm[b] = w - bf16_to_f32(bh[b]);
+                bm[b] = f32_to_bf16(rm[b]);
+                rl[b] = rm[b] - bf16_to_f32(bm[b]);
+            }
+            hi[h] = uint32_t(bh[0]) | (uint32_t(bh[1]) << 16);
+            mid[h] = uint32_t(bm[0]) | (uint32_t(bm[1]) << 16);
+            lo[h] = pack_bf16x2(rl[0], rl[1]);
+        }
+        tmain[o * 16 + e] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        tmain[o * 16 + 8 + e] = make_uint4(mid[0], mid[1], mid[2], mid[3]);
+        tlow[o * 8 + e] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+    // the tables and the histogram's zeros are in LDS at lgkmcnt(0); the X rows stay in flight
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+    barrier_no_fence();
+
+    f32x4 am = {0.0f, 0.0f, 0.0f, 0.0f}, al = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+        const uint4 xw = ring[s % R];
+        const uint4 wm = tmain[s * 64 + lane];
+        uint4 wl = tlow[s * 32 + g * 8 + (r16 & 7)];
+        if (r16 >= 8) wl = make_uint4(0u, 0u, 0u, 0u);
+        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wm), __builtin_bit_cast(bf16x8, xw),
+                                                     am, 0, 0, 0);
+        al = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wl), __builtin_bit_cast(bf16x8, xw),
+                                                     al, 0, 0, 0);
+        if (s + R < NKS) ring[s % R] = *reinterpret_cast<const uint4 *>(xp + 32 * (s + R));
+    }
+
+    // lanes 0..31: hi + lo (the low table's rows 8..15 are zero, so lanes 32..63 keep the mids exactly)
+    float v[4], lg[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[i] = am[i] + al[i];
+        v[i] += __shfl_xor(v[i], 32);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float other = __shfl_xor(v[i], 16);
+        lg[i] = (g & 1) ? other : v[i];
+        lg[4 + i] = (g & 1) ? v[i] : other;
+    }
+    const int t = tok0 + lane;
+    if (lane < 16 && t < T) {
+        int best[2];
+        float p[2];
+        select_topk<8>(lg, bias, 8, K, best, p);
+#pragma unroll
+        for (int k = 0; k < ROM_MAX_TOP_K; ++k) {
+            if (k < K) {
+                ids[(size_t)k * T + t] = best[k];
+                prob[(size_t)k * T + t] = p[k];
+                atomicAdd(&hist[k * 8 + best[k]], 1);
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < K * 8) wg_counts[(size_t)tid * nwg + blockIdx.x] = hist[tid];
+}
+
 // Multi-workgroup path, kernel 2: per-expert totals and bases, then the stable scatter of 256 tokens
 // per workgroup (= sub logits workgroups).
 template <typename TX>
@@ -403,19 +540,47 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t *__restrict
     perm += (size_t)blockIdx.y * T;
     inv_perm += (size_t)blockIdx.y * T;
     const int first = wg * sub;  // logits workgroups before this one contribute to the base
-    for (int e = wave; e < E; e += 4) {
-        int before = 0, total = 0;
-#pragma unroll 8
-        for (int w = lane; w < nwg; w += 64) {
-            const int c = wg_counts[(size_t)e * nwg + w];
-            total += c;
-            before += (w < first) ? c : 0;
-        }
+    const int t = wg * kScatterTokensPerWG + tid;
+    const int te = t < T ? ids[t] : -1;  // this thread's token's expert, in flight with the partial histograms
+    // wave w sums the partial histograms of experts w, w + 4, ..., two experts at a time with all of their
+    // loads (4 per 256 logits workgroups each) in flight before the first add
+    for (int e0 = wave; e0 < E; e0 += 8) {
+        const int e1 = e0 + 4;
+        int b0 = 0, t0 = 0, b1 = 0, t1 = 0;
+        auto chunk = [&](int w0) {
+            // unconditional loads from clamped (in-bounds) indices, the surplus zeroed afterwards: straight-line
+            // code, so no branch join makes the compiler wait between them
+            int c0[4], c1[4];
+            const size_t r0 = (size_t)e0 * nwg, r1 = (size_t)min(e1, E - 1) * nwg;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int w = min(w0 + 64 * u + lane, nwg - 1);
+                c0[u] = wg_counts[r0 + w];
+                c1[u] = wg_counts[r1 + w];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int w = w0 + 64 * u + lane;
+                const int v0 = w < nwg ? c0[u] : 0, v1 = (w < nwg && e1 < E) ? c1[u] : 0;
+                t0 += v0;
+                t1 += v1;
+                b0 += w < first ? v0 : 0;
+                b1 += w < first ? v1 : 0;
+            }
+        };
+        chunk(0);  // outside the loop, so that no loop-head wait holds these loads back
+        for (int w0 = 256; w0 < nwg; w0 += 256) chunk(w0);
         for (int m = 32; m >= 1; m >>= 1) {
-            before += __shfl_xor(before, m);
-            total += __shfl_xor(total, m);
+            b0 += __shfl_xor(b0, m);
+            t0 += __shfl_xor(t0, m);
+            b1 += __shfl_xor(b1, m);
+            t1 += __shfl_xor(t1, m);
         }
-        if (lane == 0) { s_before[e] = before; s_total[e] = total; }
+        if (lane == 0) {
+            s_before[e0] = b0;
+            s_total[e0] = t0;
+            if (e1 < E) { s_before[e1] = b1; s_total[e1] = t1; }
+        }
     }
     __syncthreads();
     if (tid == 0) {
@@ -428,12 +593,10 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t *__restrict
         if (wg == 0) offsets[E] = run;
     }
     __syncthreads();
-    const int t = wg * kScatterTokensPerWG + tid;
-    const int e = t < T ? ids[t] : -1;
-    const int rank = wg_stable_rank(e, E, s_wcnt);
+    const int rank = wg_stable_rank(te, E, s_wcnt);
     int pos = -1;
-    if (e >= 0) {
-        pos = s_base[e] + rank;
+    if (te >= 0) {
+        pos = s_base[te] + rank;
         perm[pos] = t;
         inv_perm[t] = pos;
     }
@@ -525,6 +688,36 @@ __global__ __launch_bounds__(256) void k_route_small(const TX *__restrict__ X, i
 
 // ---------------------------------------------------------------------------------------------
 
+template <int NKS>
+static hipError_t launch_route_mfma_n(const uint16_t *X, int T, const float *Wr, const float *bias,
+                                      const rom_routing &r, int32_t *wg_counts, int nwg, hipStream_t s) {
+    const size_t smem = route_mfma_lds_bytes(NKS * 32);
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_route_logits_mfma<NKS>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (err != hipSuccess) return err;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((k_route_logits_mfma<NKS>), dim3(nwg), dim3(256), smem, s, X, T, Wr, bias, r.top_k,
+                       r.expert_id, r.prob, wg_counts, nwg);
+    return hipGetLastError();
+}
+
+// d_model values with a matrix-core router kernel (bf16 X, E = 8, wide path)
+inline bool route_mfma_dm(int dm) { return dm == 512 || dm == 1024 || dm == 1536 || dm == 2048; }
+
+static hipError_t launch_route_mfma(const uint16_t *X, int T, int dm, const float *Wr, const float *bias,
+                                    const rom_routing &r, int32_t *wg_counts, int nwg, hipStream_t s) {
+    switch (dm) {
+        case 512: return launch_route_mfma_n<16>(X, T, Wr, bias, r, wg_counts, nwg, s);
+        case 1024: return launch_route_mfma_n<32>(X, T, Wr, bias, r, wg_counts, nwg, s);
+        case 1536: return launch_route_mfma_n<48>(X, T, Wr, bias, r, wg_counts, nwg, s);
+        case 2048: return launch_route_mfma_n<64>(X, T, Wr, bias, r, wg_counts, nwg, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <typename TX, int EG, int EMAX>
 static hipError_t launch_route_t(const TX *X, int T, int dm, const float *Wr, const float *bias, int E,
                                  const rom_routing &r, TX *Xp, int32_t *wg_counts, hipStream_t s) {
@@ -551,15 +744,23 @@ static hipError_t launch_route_t(const TX *X, int T, int dm, const float *Wr, co
                            use_lds, r.expert_id, r.prob, r.counts, r.offsets, r.perm, r.inv_perm, Xp);
         return hipGetLastError();
     }
-    const int tpw = wide ? 32 : 8;
+    // bf16 rows, 8 experts and a d_model with a matrix-core kernel: 64 tokens per workgroup
+    const bool mfma = std::is_same<TX, uint16_t>::value && wide && E == 8 && route_mfma_dm(dm);
+    const int tpw = mfma ? kRouteMfmaTokensPerWG : wide ? 32 : 8;
     const int nwg = (T + tpw - 1) / tpw;
-    if (wide)
-        hipLaunchKernelGGL((k_route_logits<TX, EG, EMAX, 1>), dim3(nwg), dim3(256), smem, s, X, T, dm, Wr, bias, E,
-                           r.top_k, use_lds, r.expert_id, r.prob, wg_counts, nwg);
-    else
-        hipLaunchKernelGGL((k_route_logits<TX, EG, EMAX, 4>), dim3(nwg), dim3(256), smem, s, X, T, dm, Wr, bias, E,
-                           r.top_k, use_lds, r.expert_id, r.prob, wg_counts, nwg);
-    hipError_t err = hipGetLastError();
+    hipError_t err = hipSuccess;
+    if constexpr (std::is_same<TX, uint16_t>::value) {
+        if (mfma) err = launch_route_mfma(X, T, dm, Wr, bias, r, wg_counts, nwg, s);
+    }
+    if (!mfma) {
+        if (wide)
+            hipLaunchKernelGGL((k_route_logits<TX, EG, EMAX, 1>), dim3(nwg), dim3(256), smem, s, X, T, dm, Wr, bias,
+                               E, r.top_k, use_lds, r.expert_id, r.prob, wg_counts, nwg);
+        else
+            hipLaunchKernelGGL((k_route_logits<TX, EG, EMAX, 4>), dim3(nwg), dim3(256), smem, s, X, T, dm, Wr, bias,
+                               E, r.top_k, use_lds, r.expert_id, r.prob, wg_counts, nwg);
+        err = hipGetLastError();
+    }
     if (err != hipSuccess) return err;
     const int nsc = (T + kScatterTokensPerWG - 1) / kScatterTokensPerWG;
     hipLaunchKernelGGL((k_route_scatter<TX>), dim3(nsc, r.top_k), dim3(256), 0, s, r.expert_id, T, E, wg_counts, nwg,

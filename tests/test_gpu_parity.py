@@ -105,6 +105,10 @@ SMALL = [
     workloads.custom_workload("bf16_T9_split_route", T=9, d_model=512, d_inner=128, E=4, seed=114),
     workloads.custom_workload("bf16_wide_route_E64", T=16400, d_model=128, d_inner=128, E=64, seed=115),
     workloads.custom_workload("bf16_wide_route_E3", T=16421, d_model=192, d_inner=128, E=3, seed=116),
+    # wide router on the matrix cores (bf16, 8 experts): a ragged last workgroup, d_model 512 (no ring
+    # refills) and 1536 (ring refilled)
+    workloads.custom_workload("bf16_wide_mfma_dm512", T=16400, d_model=512, d_inner=128, E=8, seed=118),
+    workloads.custom_workload("bf16_wide_mfma_dm1536", T=16390, d_model=1536, d_inner=128, E=8, seed=119),
     # wide router with W_r in LDS and fp32 rows: 144 chunks per row, so every lane has a second chunk in
     # flight at the barrier and some refill a third time
     workloads.custom_workload("f32_wide_route_dm1152", T=16400, d_model=1152, d_inner=128, E=8, dtype="f32", seed=117),
@@ -149,9 +153,15 @@ def test_empty_experts(rom, oracle):
     assert gr["counts"][0] == gr["counts"][2] == gr["counts"][7] == 0
 
 
-def test_tied_logits_lowest_index_and_exact_prob(rom, oracle):
+TIES = [
+    workloads.custom_workload("ties", T=500, d_model=128, d_inner=128, E=8, seed=122),
+    workloads.custom_workload("ties_wide_mfma", T=16400, d_model=512, d_inner=128, E=8, seed=160),
+]
+
+
+@pytest.mark.parametrize("w", TIES, ids=[w.name for w in TIES])
+def test_tied_logits_lowest_index_and_exact_prob(rom, oracle, w):
     """W_router = 0: every logit ties; both sides pick expert 0 and p = 1/E exactly."""
-    w = workloads.custom_workload("ties", T=500, d_model=128, d_inner=128, E=8, seed=122)
     inp = workloads.make_inputs(w)
     inp["W_router"] = np.zeros_like(inp["W_router"])
     g = _run_chain(rom, w, inp, isolated=False)
@@ -259,6 +269,7 @@ TOP2 = [
     workloads.custom_workload("top2_T40_decode", T=40, d_model=256, d_inner=320, E=4, seed=206),
     workloads.custom_workload("top2_T64_decode", T=64, d_model=512, d_inner=256, E=8, seed=207),
     workloads.custom_workload("top2_wide_route", T=16400, d_model=128, d_inner=128, E=8, seed=208),
+    workloads.custom_workload("top2_wide_mfma_dm1024", T=16400, d_model=1024, d_inner=128, E=8, seed=211),
     # 256-row early-barrier tiles (their padding rules out 320 rows here) with the fp32 accumulate epilogue
     workloads.custom_workload("top2_T4096_tiles256", T=4096, d_model=512, d_inner=512, E=8, seed=210),
 ]
