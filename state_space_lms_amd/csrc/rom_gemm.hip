@@ -632,13 +632,32 @@ __global__ __launch_bounds__(64 * NW) void k_grouped_gemv_bf16(GemmArgs p) {
     }
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 template <bool OUT>
 static hipError_t launch_gemv(const GemmArgs &a0, int nB, hipStream_t s) {
     GemmArgs a = a0;
     a.n_tiles = nB * a.N0 / 16;
     a.n_tiles_per_b = a.N0 / 16;
     const int active = a.T < a.E ? a.T : a.E;
-    hipLaunchKernelGGL((k_grouped_gemv_bf16<8, OUT>), dim3((unsigned)a.n_tiles * active), dim3(512), 0, s, a);
+    const long nwg = (long)a.n_tiles * active;
+    // At most one workgroup per compute unit (the out-projection of a single token): 16 waves, so that each
+    // wave streams half as many K-steps and a compute unit keeps twice the loads in flight.
+    if (nwg <= device_cus())
+        hipLaunchKernelGGL((k_grouped_gemv_bf16<16, OUT>), dim3((unsigned)nwg), dim3(1024), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_grouped_gemv_bf16<8, OUT>), dim3((unsigned)nwg), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 
@@ -719,18 +738,6 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs p) {
 
 // ---------------------------------------------------------------------------------------------
 
-// Compute units of the current device (cached per device).
-static int device_cus() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
 
 // XCD-aware grouping of M-tiles (0 = off); ROM_GROUP_M overrides it for tuning sweeps.
 static int group_m_choice() {
