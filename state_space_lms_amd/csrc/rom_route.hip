@@ -121,10 +121,10 @@ __device__ __forceinline__ void xrows_issue(XRows<TX> &xr, const TX *__restrict_
 // bits 3..5. On return every lane of the wave with (lane & 7) == j holds this wave's partial logits of
 // token tok0 + j in out[0..EG); with LPT > 64 the caller still sums the waves. Must be called by every
 // lane of the wave (it shuffles). wl != nullptr: W_r is read from the LDS copy made by
-// stage_router_weight.
+// stage_router_weight. Rows q >= nrows (tokens past T) get no FMAs; their zero sums are discarded.
 template <typename TX, int LPT, int EG>
 __device__ __forceinline__ void logits_group8(XRows<TX> &xr, int dm, const float *__restrict__ Wr, const float4 *wl,
-                                              int E, int e0, int jl, float out[EG]) {
+                                              int E, int e0, int jl, int nrows, float out[EG]) {
     float acc[8][EG];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
@@ -163,12 +163,14 @@ __device__ __forceinline__ void logits_group8(XRows<TX> &xr, int dm, const float
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            float xf[8];
-            buf[q].unpack(xf);
+            if (q < nrows) {  // uniform; rows past T repeat row T - 1 and are discarded
+                float xf[8];
+                buf[q].unpack(xf);
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk)
+                for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-                for (int x = 0; x < EG; ++x) acc[q][x] = fmaf(xf[kk], w[kk][x], acc[q][x]);
+                    for (int x = 0; x < EG; ++x) acc[q][x] = fmaf(xf[kk], w[kk][x], acc[q][x]);
+            }
         }
     };
     // chunks c (in a) and c + LPT (in b); each buffer is refilled two strides ahead as soon as it is used
@@ -226,7 +228,7 @@ __device__ __forceinline__ void logits_token(XRows<TX> &xr, const TX *X, int T, 
         if (g * EG < E) {  // uniform
             if (g > 0) xrows_issue<TX, LPT>(xr, X, T, dm, tok0, jl);
             float o[EG];
-            logits_group8<TX, LPT, EG>(xr, dm, Wr, wl, E, g * EG, jl, o);
+            logits_group8<TX, LPT, EG>(xr, dm, Wr, wl, E, g * EG, jl, min(8, T - tok0), o);
 #pragma unroll
             for (int x = 0; x < EG; ++x) lg[g * EG + x] = (g * EG + x < E) ? o[x] : -INFINITY;
         } else {
@@ -724,7 +726,8 @@ static hipError_t launch_route_t(const TX *X, int T, int dm, const float *Wr, co
     const size_t wbytes = (size_t)dm * E * sizeof(float);
     // enough 32-token workgroups to fill the chip: one wave per 8 tokens; otherwise 8 tokens per
     // workgroup with the waves splitting d_model. W_r is staged in LDS only on the wide path: with 8
-    // tokens per workgroup each W_r value serves too few tokens to repay the staging round trip.
+    // tokens per workgroup each W_r value serves too few tokens to repay the staging round trip, and for
+    // T <= 8 one compute unit copying all of W_r was slower (decode_T1 7.7 -> 8.0 us) than reading it.
     const bool wide = (T + 31) / 32 >= 512;
     const int use_lds = wide && (E % 4 == 0) && (((E >> 2) & ((E >> 2) - 1)) == 0) && wbytes <= (size_t)kRouteLdsW;
     const size_t smem = use_lds ? wbytes : 0;
