@@ -534,23 +534,25 @@ __global__ __launch_bounds__(256) void k_gate_permute(const uint16_t *__restrict
 
 // ---------------------------------------------------------------------------------------------
 // Decode path (T <= 64): the cost is streaming each active expert's weights from HBM once; the MFMA
-// work is tiny. A workgroup owns 16 weight rows of one expert and every token routed to it (at most
-// 64, i.e. NB blocks of 16), and its NW waves split K. The weight fragment of a 16x16x32 MFMA comes
-// straight from global memory (lane l: row l%16, 8 elements at k + 8*(l/16)), the token fragments
+// work is tiny. A workgroup owns RB blocks of 16 weight rows of one expert and every token routed to it
+// (at most 64, i.e. NB blocks of 16), and its NW waves split K. The weight fragment of a 16x16x32 MFMA
+// comes straight from global memory (lane l: row l%16, 8 elements at k + 8*(l/16)), the token fragments
 // likewise through perm (for the out-projection, from the gated rows k_gate_permute wrote in token
 // order: the gate is evaluated once per token, not once per workgroup and padding column); each wave
-// keeps U K-steps of loads in flight. Partial sums of the waves are added in wave order through LDS
-// (deterministic), then scaled (out-projection) and stored.
-// Grid: (weight rows / 16) x min(E, T): the second index is the rank among experts that received tokens;
-// each workgroup runs the variant sized for its expert's token-block count.
-template <int NW, int NB, int U, bool OUT>
+// keeps U K-steps of loads in flight. Every workgroup reads all of its expert's token rows, so with more
+// tokens (RB = 2 from 32 tokens on) a workgroup takes 32 weight rows and the token rows are read half as
+// often. Partial sums of the waves are added in wave order through LDS (deterministic), then scaled
+// (out-projection) and stored.
+// Grid: (weight rows / (16 RB)) x min(E, T): the second index is the rank among experts that received
+// tokens; each workgroup runs the variant sized for its expert's token-block count.
+template <int NW, int RB, int NB, int U, bool OUT>
 __device__ __forceinline__ void gemv_block(const GemmArgs &p, int e, int o0, int ne, int rb,
-                                           float (*s_red)[4][16][16]) {
+                                           float (*s_red)[RB * 4][16][16]) {
     constexpr int NT = 64 * NW;
     __shared__ int s_tok[64];
     __shared__ float s_prob[64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nglob = rb * 16;
+    const int nglob = rb * 16 * RB;  // N0 is a multiple of 64, so the RB blocks lie in one output
     const int which = nglob / p.N0, n0 = nglob % p.N0;
     const int K = p.K;
     const uint16_t *W = static_cast<const uint16_t *>(which ? p.B1 : p.B0) + ((size_t)e * p.N0 + n0) * K;
@@ -564,22 +566,27 @@ __device__ __forceinline__ void gemv_block(const GemmArgs &p, int e, int o0, int
     __syncthreads();
 
     const int r = lane & 15, g = lane >> 4;
-    const uint16_t *wp = W + (size_t)r * K + g * 8;
+    const uint16_t *wp[RB];
+#pragma unroll
+    for (int j = 0; j < RB; ++j) wp[j] = W + (size_t)(j * 16 + r) * K + g * 8;
     const uint16_t *xp[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) xp[b] = static_cast<const uint16_t *>(p.A0) + (size_t)s_tok[b * 16 + r] * K + g * 8;
-    f32x4 acc[NB];
+    f32x4 acc[RB][NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < RB; ++j)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[j][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     // U K-steps of loads in flight per wave (indices clamped, so every load is in bounds), then their MFMAs
     const int nsteps = K / 32;
     for (int s0 = wave; s0 < nsteps; s0 += NW * U) {
-        bf16x8 wf[U], xf[U][NB];
+        bf16x8 wf[U][RB], xf[U][NB];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int k0 = min(s0 + u * NW, nsteps - 1) * 32;
-            wf[u] = *reinterpret_cast<const bf16x8 *>(wp + k0);
+#pragma unroll
+            for (int j = 0; j < RB; ++j) wf[u][j] = *reinterpret_cast<const bf16x8 *>(wp[j] + k0);
 #pragma unroll
             for (int b = 0; b < NB; ++b) xf[u][b] = *reinterpret_cast<const bf16x8 *>(xp[b] + k0);
         }
@@ -587,33 +594,38 @@ __device__ __forceinline__ void gemv_block(const GemmArgs &p, int e, int o0, int
         for (int u = 0; u < U; ++u) {
             if (s0 + u * NW < nsteps) {  // uniform
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], xf[u][b], acc[b], 0, 0, 0);
+                for (int j = 0; j < RB; ++j)
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        acc[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u][j], xf[u][b], acc[j][b], 0, 0, 0);
             }
         }
     }
-    // accumulator register i of lane l: weight row 4*(l/16) + i, token column l%16
+    // accumulator register i of lane l: weight row 4*(l/16) + i (of block j), token column l%16
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+    for (int j = 0; j < RB; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s_red[wave][b][4 * g + i][r] = acc[b][i];
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_red[wave][j * NB + b][4 * g + i][r] = acc[j][b][i];
     __syncthreads();
-    for (int idx = tid; idx < NB * 256; idx += NT) {
-        const int b = idx >> 8, n = (idx >> 4) & 15, m = idx & 15;
+    for (int idx = tid; idx < RB * NB * 256; idx += NT) {
+        const int jb = idx >> 8, n = (idx >> 4) & 15, m = idx & 15;
+        const int j = jb / NB, b = jb - j * NB;
         const int col = b * 16 + m;
         if (col < ne) {
             float v = 0.0f;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) v += s_red[w][b][n][m];
-            uint16_t *dst = C + (size_t)s_tok[col] * p.N0 + n0 + n;
+            for (int w = 0; w < NW; ++w) v += s_red[w][jb][n][m];
+            uint16_t *dst = C + (size_t)s_tok[col] * p.N0 + n0 + j * 16 + n;
             *dst = f32_to_bf16(p.accumulate ? fmaf(v, s_prob[col], bf16_to_f32(*dst)) : v * s_prob[col]);
         }
     }
 }
 
-template <int NW, bool OUT>
+template <int NW, int RB, bool OUT>
 __global__ __launch_bounds__(64 * NW) void k_grouped_gemv_bf16(GemmArgs p) {
-    __shared__ float s_red[NW][4][16][16];
+    __shared__ float s_red[NW][RB * 4][16][16];
     const int rb = blockIdx.x % p.n_tiles, rank = blockIdx.x / p.n_tiles;
     int e = -1, o0 = 0, ne = 0;
     for (int i = 0, j = 0; i < p.E; ++i) {
@@ -625,10 +637,10 @@ __global__ __launch_bounds__(64 * NW) void k_grouped_gemv_bf16(GemmArgs p) {
     }
     if (e < 0) return;
     switch ((ne + 15) >> 4) {  // token blocks of this expert (1..4), uniform per workgroup
-        case 1: gemv_block<NW, 1, 8, OUT>(p, e, o0, ne, rb, s_red); break;
-        case 2: gemv_block<NW, 2, 4, OUT>(p, e, o0, ne, rb, s_red); break;
-        case 3: gemv_block<NW, 3, 4, OUT>(p, e, o0, ne, rb, s_red); break;
-        default: gemv_block<NW, 4, 4, OUT>(p, e, o0, ne, rb, s_red); break;
+        case 1: gemv_block<NW, RB, 1, 8, OUT>(p, e, o0, ne, rb, s_red); break;
+        case 2: gemv_block<NW, RB, 2, 4, OUT>(p, e, o0, ne, rb, s_red); break;
+        case 3: gemv_block<NW, RB, 3, 4, OUT>(p, e, o0, ne, rb, s_red); break;
+        default: gemv_block<NW, RB, 4, 4, OUT>(p, e, o0, ne, rb, s_red); break;
     }
 }
 
@@ -648,16 +660,20 @@ static int device_cus() {
 template <bool OUT>
 static hipError_t launch_gemv(const GemmArgs &a0, int nB, hipStream_t s) {
     GemmArgs a = a0;
-    a.n_tiles = nB * a.N0 / 16;
-    a.n_tiles_per_b = a.N0 / 16;
     const int active = a.T < a.E ? a.T : a.E;
+    // From 32 tokens on, 32 weight rows per workgroup (every workgroup reads all of its expert's token rows)
+    const int rbk = a.T >= 32 ? 2 : 1;
+    a.n_tiles = nB * a.N0 / (16 * rbk);
+    a.n_tiles_per_b = a.N0 / (16 * rbk);
     const long nwg = (long)a.n_tiles * active;
     // At most one workgroup per compute unit (the out-projection of a single token): 16 waves, so that each
     // wave streams half as many K-steps and a compute unit keeps twice the loads in flight.
-    if (nwg <= device_cus())
-        hipLaunchKernelGGL((k_grouped_gemv_bf16<16, OUT>), dim3((unsigned)nwg), dim3(1024), 0, s, a);
+    if (rbk == 2)
+        hipLaunchKernelGGL((k_grouped_gemv_bf16<8, 2, OUT>), dim3((unsigned)nwg), dim3(512), 0, s, a);
+    else if (nwg <= device_cus())
+        hipLaunchKernelGGL((k_grouped_gemv_bf16<16, 1, OUT>), dim3((unsigned)nwg), dim3(1024), 0, s, a);
     else
-        hipLaunchKernelGGL((k_grouped_gemv_bf16<8, OUT>), dim3((unsigned)nwg), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((k_grouped_gemv_bf16<8, 1, OUT>), dim3((unsigned)nwg), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 
