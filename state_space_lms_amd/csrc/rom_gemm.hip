@@ -415,8 +415,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
         constexpr int SWM = (CPR4 < 32 ? CPR4 : 32) - 1;             // chunk swizzle mask (stays in the row)
         float *ct = reinterpret_cast<float *>(smem);
         auto prow_of = [&](int wmr, int ii, int r) { return (ii * WGM + wmr) * 32 + r; };  // LDS row
+        constexpr int CPR = BN / 8;  // 8-column units per row
+        constexpr int UNITS = IPP * PROWS * CPR;
+        constexpr int UPT = UNITS % NT == 0 ? UNITS / NT : 0;  // units per thread, when they divide evenly
 #pragma unroll
         for (int q = 0; q < NPASS; ++q) {
+            // the pass's stored values are loaded first, all at once, so that their latency overlaps the LDS
+            // pass below instead of one round trip per unit (rows clamped into the tile: every load is in
+            // bounds, and only the stored rows are used)
+            uint4 old[UPT > 0 ? UPT : 1];
+            if constexpr (UPT > 0) {
+#pragma unroll
+                for (int k = 0; k < UPT; ++k) {
+                    const int u = tid + k * NT;
+                    const int lr = u / CPR, c = u % CPR;
+                    const int ii = lr / PROWS, wmr = (lr / 32) % WGM, i = q * IPP + ii;
+                    const int row = min(wmr * WM + i * 32 + (lr & 31), BM - 1);
+                    old[k] = *reinterpret_cast<const uint4 *>(C + (size_t)s_tok[row] * p.N0 + n0 + c * 8);
+                }
+            }
             __syncthreads();
 #pragma unroll
             for (int ii = 0; ii < IPP; ++ii) {
@@ -439,23 +456,32 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
                 }
             }
             __syncthreads();
-            constexpr int CPR = BN / 8;  // 8-column units per row
-            const int units = IPP * PROWS * CPR;
-            for (int u = tid; u < units; u += NT) {
+            // unit u: LDS row lr = u / CPR (tile row wmr * WM + i * 32 + lr % 32), 8 columns from 8 (u % CPR)
+            auto add_store = [&](int u, const uint4 &ov) {
                 const int lr = u / CPR, c = u % CPR;
                 const int ii = lr / PROWS, wmr = (lr / 32) % WGM, i = q * IPP + ii;
                 const int row = wmr * WM + i * 32 + (lr & 31);  // tile row
                 if (i < FM && row < rows) {
                     uint4 *dst = reinterpret_cast<uint4 *>(C + (size_t)s_tok[row] * p.N0 + n0 + c * 8);
-                    const uint4 old = *dst;
                     const float4 a = *reinterpret_cast<const float4 *>(ct + lr * BN + (((2 * c) ^ (lr & SWM)) << 2));
                     const float4 b = *reinterpret_cast<const float4 *>(ct + lr * BN + (((2 * c + 1) ^ (lr & SWM)) << 2));
                     uint4 pk;
-                    pk.x = pack_bf16x2(__uint_as_float(old.x << 16) + a.x, __uint_as_float(old.x & 0xFFFF0000u) + a.y);
-                    pk.y = pack_bf16x2(__uint_as_float(old.y << 16) + a.z, __uint_as_float(old.y & 0xFFFF0000u) + a.w);
-                    pk.z = pack_bf16x2(__uint_as_float(old.z << 16) + b.x, __uint_as_float(old.z & 0xFFFF0000u) + b.y);
-                    pk.w = pack_bf16x2(__uint_as_float(old.w << 16) + b.z, __uint_as_float(old.w & 0xFFFF0000u) + b.w);
+                    pk.x = pack_bf16x2(__uint_as_float(ov.x << 16) + a.x, __uint_as_float(ov.x & 0xFFFF0000u) + a.y);
+                    pk.y = pack_bf16x2(__uint_as_float(ov.y << 16) + a.z, __uint_as_float(ov.y & 0xFFFF0000u) + a.w);
+                    pk.z = pack_bf16x2(__uint_as_float(ov.z << 16) + b.x, __uint_as_float(ov.z & 0xFFFF0000u) + b.y);
+                    pk.w = pack_bf16x2(__uint_as_float(ov.w << 16) + b.z, __uint_as_float(ov.w & 0xFFFF0000u) + b.w);
                     *dst = pk;
+                }
+            };
+            if constexpr (UPT > 0) {
+#pragma unroll
+                for (int k = 0; k < UPT; ++k) add_store(tid + k * NT, old[k]);
+            } else {
+                for (int u = tid; u < UNITS; u += NT) {
+                    const int lr = u / CPR, c = u % CPR;
+                    const int ii = lr / PROWS, wmr = (lr / 32) % WGM, i = q * IPP + ii;
+                    const int row = min(wmr * WM + i * 32 + (lr & 31), BM - 1);
+                    add_store(u, *reinterpret_cast<const uint4 *>(C + (size_t)s_tok[row] * p.N0 + n0 + c * 8));
                 }
             }
         }
