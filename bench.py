@@ -10,13 +10,20 @@ For the Swimba workloads (swimba_decode_T*) one step is rom_route + rom_in_proj_
 Switch Mamba layer (Swimba project page, extended abstract): expert in-projections whose outputs are weighted
 by the router probability.
 
-Default workload: the Samba-421M-like block, T = 4 x 4096 tokens, d_model 1024, d_inner 2048, 8 experts,
-bf16 data. Prints ONE JSON line: whole-step tokens/s, the roofline of the dominant kernel (the
-in-projection grouped GEMM, timed live with HIP events on the stream it runs on), and the CPU oracle
-timed on a bounded sample of the same workload on the host cores.
+Default workload: the largest single-GPU block, skewed routing without a balance loss: T = 65536 tokens
+(16 x 4096), d_model 2048, d_inner 4096, 8 experts whose loads are 60/10/10/5/5/5/3/2 % (a router bias
+realises them), bf16 data. Prints ONE JSON line: whole-step tokens/s, the roofline of the dominant kernel
+(the in-projection grouped GEMM, timed live with HIP events on the stream it runs on), per-call medians
+with p10/p90, and the CPU oracle timed on a bounded sample of the same workload on the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--cold] [--backward]
-                    [--with-conv1d] [--event-every N]
+Decode workloads (T <= 64) run with cold caches by default (a 1 GiB read evicts L2 and the MALL before
+every step) and report the whole step (router + both projections) against HBM bandwidth as their roofline.
+
+Before the W warm-up steps the GPU runs steps for --ramp-seconds of wall time, so that its clocks have left
+their idle state whatever W is (the time is reported as clock_ramp_s).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--cold | --warm]
+                    [--backward] [--with-conv1d] [--event-every N] [--ramp-seconds S]
 """
 from __future__ import annotations
 
@@ -114,13 +121,15 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed steps first: the GPU needs some tens of milliseconds of work to leave its idle "
-                         "clocks (the first ~50 Samba-size steps run ~40%% slower)")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed steps after the clock ramp")
+    ap.add_argument("--ramp-seconds", type=float, default=1.0,
+                    help="run untimed steps for this much wall time before the warm-up steps: the GPU needs some "
+                         "tens of milliseconds of work to leave its idle clocks (the first ~50 Samba-size steps "
+                         "run ~40%% slower), whatever --warmup is")
     ap.add_argument("--event-every", type=int, default=5,
                     help="bracket the in-projection with HIP events on every n-th timed step (events cost a few "
                          "microseconds of GPU time each, which matters at decode sizes)")
-    ap.add_argument("--workload", default="samba421m")
+    ap.add_argument("--workload", default="skewed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--with-conv1d", action="store_true",
@@ -130,8 +139,9 @@ def main() -> int:
                     help="add the backward of both projections (out_proj_backward, then in_proj_backward on its dz) to "
                          "the step: a forward + backward pass of the routed projections (prefill RoM workloads)")
     ap.add_argument("--cold", action="store_true",
-                    help="read a 1 GiB buffer before every step, so weights and inputs come from HBM (decode); the "
-                         "step is then timed with GPU events around it")
+                    help="read a 1 GiB buffer before every step, so weights and inputs come from HBM; the step is "
+                         "then timed with GPU events around it (the default for decode workloads, T <= 64)")
+    ap.add_argument("--warm", action="store_true", help="decode workloads: keep caches warm between steps")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the routed projections of a token need no data "
@@ -186,9 +196,13 @@ def main() -> int:
         cin = workloads.make_conv_inputs(1, 1, w.d_inner, CONV_WIDTH, w.dtype, seed=w.seed)
         Wcv, bcv = up(cin["weight"], w.dtype), up(cin["bias"], w.dtype)
         xc = torch.empty((w.T, w.d_inner), dtype=X.dtype, device=dev)
+    decode = w.T <= 64
+    cold = (args.cold or decode) and not args.warm
     # cold runs stream this buffer through the caches before each step; reading (not writing) it leaves no
     # dirty lines whose write-back would be charged to the step
-    flush = torch.zeros((1 << 30) // 4, dtype=torch.int32, device=dev) if args.cold else None
+    flush = torch.zeros((1 << 30) // 4, dtype=torch.int32, device=dev) if cold else None
+    # the materialised permute (X_perm[pos] = X[perm[pos]], top-1) is timed as its own call after the step
+    xperm = rom.Routing(w.T, w.E, dev, top_k=1) if w.top_k == 1 else None
 
     # plain copy of known size: the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters
     cp_src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
@@ -230,6 +244,17 @@ def main() -> int:
         if ev is not None:
             ev[-1].record(stream)
 
+    # clock ramp: steps for a fixed wall time (synchronised every few steps), then the warm-up steps
+    t_ramp0 = time.perf_counter()
+    n_ramp = 0
+    while time.perf_counter() - t_ramp0 < args.ramp_seconds:
+        for _ in range(4):
+            if flush is not None:
+                flush.sum()
+            step()
+            n_ramp += 1
+        torch.cuda.synchronize()
+    ramp_s = time.perf_counter() - t_ramp0
     for _ in range(args.warmup):
         if flush is not None:
             flush.sum()
@@ -238,6 +263,20 @@ def main() -> int:
 
     new_ev = lambda n: [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     events = [new_ev(len(phases) + 1) for _ in range(args.steps)]
+    perm_ev = [new_ev(2) for _ in range(args.steps)] if xperm is not None else None
+
+    def breakdown_pass():
+        """Per-phase events on every step (untimed), then the route call with the materialised permute."""
+        for k in range(args.steps):
+            if flush is not None:
+                flush.sum()
+            step(ev=events[k])
+            if perm_ev is not None:
+                perm_ev[k][0].record(stream)
+                rom.route(X, Wr, bias, top_k=1, permute=True, routing=xperm, stream=stream)
+                perm_ev[k][1].record(stream)
+        torch.cuda.synchronize()
+
     if flush is None:
         # warm: wall clock over K back-to-back steps; inside them the in-projection is bracketed by events
         # (the roofline's launch time) on every n-th step, so the timed region carries few markers
@@ -251,20 +290,16 @@ def main() -> int:
         elapsed = time.perf_counter() - t0
         t_in_timed = np.array([e[0].elapsed_time(e[1]) for e in ins.values()]) * 1e-3
         # per-phase breakdown from a second, untimed pass of the same K steps
-        for k in range(args.steps):
-            step(ev=events[k])
-        torch.cuda.synchronize()
+        breakdown_pass()
     else:
         # cold cache: the eviction runs between steps and stays outside the timed sum, which adds up the
         # GPU time of each step (event before the router to event after the last phase)
-        for k in range(args.steps):
-            flush.sum()
-            step(ev=events[k])
-        torch.cuda.synchronize()
+        breakdown_pass()
         elapsed = sum(e[0].elapsed_time(e[-1]) for e in events) * 1e-3
         t_in_timed = None
 
     t_ph = {ph: np.array([e[i].elapsed_time(e[i + 1]) for e in events]) * 1e-3 for i, ph in enumerate(phases)}
+    t_step = np.array([e[0].elapsed_time(e[-1]) for e in events]) * 1e-3
     t_route, t_in = t_ph["route"], (t_in_timed if t_in_timed is not None else t_ph["in"])
     t_out = t_ph.get("out", np.zeros(1))
     # the in-projection's output width: Conv + Gate (2 * d_inner) for RoM, d_out for Swimba
@@ -278,31 +313,48 @@ def main() -> int:
     # algorithmic bytes: every operand and result moved once, only the experts that received tokens
     bytes_in = es * (w.T * w.d_model + used * n_in * w.d_model + w.T * n_in)
     bytes_out = 0 if swimba else es * (2 * w.T * w.d_inner + used * w.d_model * w.d_inner + w.T * w.d_model) + 4 * w.T * 2
-    bytes_route = es * w.T * w.d_model + 4 * w.d_model * w.E + 4 * w.T * 4
+    # router: X once, W_r once, ids and probabilities out, perm and inv_perm out (per choice)
+    bytes_route = es * w.T * w.d_model + 4 * w.d_model * w.E + 4 * w.T * 4 * w.top_k
+    bytes_permute = 2 * es * w.T * w.d_model  # X rows read once and written once in slot order
     bytes_conv = es * (2 * w.T * w.d_inner + (CONV_WIDTH + 1) * w.d_inner)
     ms_per_step = elapsed / args.steps * 1e3
     mean_in, mean_out, mean_route = float(t_in.mean()), float(t_out.mean()), float(t_route.mean())
+    step_bytes = bytes_route + bytes_in + bytes_out
 
-    decode = w.T <= 64
     if decode:
-        achieved = (bytes_in / mean_in) / 1e9
+        # the whole step (router included) against HBM: the used experts' weights dominate its bytes
+        mean_step = float(t_step.mean())
+        achieved = step_bytes / mean_step / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4)}
     else:
         achieved = fl_in / mean_in / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4)}
-    roof["traffic"] = measured_traffic(w.name)
+    roof["traffic"] = None if decode else measured_traffic(w.name)
     entry = "rom_in_proj_weighted" if swimba else "rom_in_proj"
-    if w.dtype != "bf16":
-        roof["kernel"] = f"k_grouped_gemm_f32 ({entry})"
+    if decode:
+        roof["kernel"] = ("whole step: rom_route + " + entry + ("" if swimba else " + rom_out_proj") +
+                          ", cold caches")
+        roof["algorithmic"] = {"bytes_per_step": step_bytes}
+        roof["step_us"] = round(float(t_step.mean()) * 1e6, 2)
     else:
-        roof["kernel"] = ("k_grouped_gemv_bf16" if decode else "k_grouped_gemm_bf16") + f" ({entry})"
-    roof["algorithmic"] = ({"bytes_per_launch": bytes_in} if decode else {"flops_per_launch": fl_in})
-    roof["launch_us"] = round(mean_in * 1e6, 2)
+        roof["kernel"] = ("k_grouped_gemm_f32" if w.dtype != "bf16" else "k_grouped_gemm_bf16") + f" ({entry})"
+        roof["algorithmic"] = {"flops_per_launch": fl_in}
+        roof["launch_us"] = round(mean_in * 1e6, 2)
+
+    def pct(a):
+        a = np.asarray(a) * 1e6
+        return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+                "p90": round(float(np.percentile(a, 90)), 2), "mean": round(float(a.mean()), 2)}
+
+    names = {"route": "rom_route", "in": entry, "conv": "rom_conv1d", "out": "rom_out_proj",
+             "obwd": "rom_out_proj_backward", "ibwd": "rom_in_proj_backward"}
+    per_call = {names[ph]: pct(t_ph[ph]) for ph in phases}
+    per_call["step"] = pct(t_step)
 
     config = {"workload": w.name, "T": w.T, "d_model": w.d_model, "d_inner": w.d_inner, "E": w.E,
-              "top_k": w.top_k, "router": "fp32", "cache": "cold" if args.cold else "warm",
+              "top_k": w.top_k, "router": "fp32", "cache": "cold" if cold else "warm",
               "expert_loads": counts[0].tolist() if w.top_k == 1 else counts.tolist()}
     if swimba:
         config["d_out"] = w.dout
@@ -315,6 +367,8 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_ramp_s": round(ramp_s, 2),
+        "clock_ramp_steps": n_ramp,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -333,11 +387,22 @@ def main() -> int:
             "route_gbs": round(bytes_route / mean_route / 1e9, 1),
             "in_proj_gbs": round(bytes_in / mean_in / 1e9, 1),
             "out_proj_gbs": round(bytes_out / mean_out / 1e9, 1) if mean_out > 0 else 0.0,
-            "step_hbm_frac": round((bytes_route + bytes_in + bytes_out) / (mean_route + mean_in + mean_out)
-                                   / 1e9 / PEAK_HBM_GBS, 4),
+            "step_hbm_frac": round(step_bytes / (mean_route + mean_in + mean_out) / 1e9 / PEAK_HBM_GBS, 4),
+            "in_proj_hbm_frac": round(bytes_in / mean_in / 1e9 / PEAK_HBM_GBS, 4),
+            "per_call_us": per_call,
         },
         "cpu_baseline": None,
     }
+    if perm_ev is not None:
+        t_rp = np.array([e[0].elapsed_time(e[1]) for e in perm_ev]) * 1e-3
+        # the permute runs inside the router's scatter kernel: its cost is the router call's extra time
+        t_perm = max(float(np.median(t_rp)) - float(np.median(t_route)), 1e-9)
+        result["breakdown"]["permute"] = {
+            "route_with_permute_us": pct(t_rp),
+            "permute_us": round(t_perm * 1e6, 2),
+            "permute_bytes": bytes_permute,
+            "permute_gbs": round(bytes_permute / t_perm / 1e9, 1),
+        }
     if bwd:
         for ph, key, mult in (("obwd", "out_proj_backward", 4), ("ibwd", "in_proj_backward", 8)):
             tm = float(t_ph[ph].mean())

@@ -14,8 +14,8 @@
  *
  * Conventions for every entry point
  *  - Pointers named in a signature are DEVICE pointers unless marked "host". The caller owns every
- *    buffer; the library allocates nothing and keeps no state apart from a per-device property
- *    cache. Tensors are dense, row-major, and 16-byte aligned.
+ *    buffer; the library allocates nothing and keeps no state apart from per-device caches (device
+ *    properties, kernel attributes), each filled once per device, thread-safely. Tensors are dense, row-major, and 16-byte aligned.
  *  - Calls enqueue kernels on `stream` (a hipStream_t; NULL is the null stream) and return without
  *    synchronising. The projections read what rom_route wrote: run them on the same stream, or
  *    order them after it. No count is ever read back to the host.
@@ -23,7 +23,7 @@
  *    except for ROM_ERR_HIP, which reports a failed launch. rom_last_error() gives details.
  *  - T == 0 is a valid no-op (ROM_OK, nothing enqueued, no buffer touched).
  *  - Supported range: 1 <= E <= ROM_MAX_EXPERTS, 1 <= top_k <= min(E, ROM_MAX_TOP_K), d_model and
- *    d_inner multiples of 64, T <= ROM_MAX_TOKENS. dtype is the storage type of X, the expert stacks, z, h and all outputs;
+ *    d_inner multiples of 64 and at most ROM_MAX_DIM, T <= ROM_MAX_TOKENS. dtype is the storage type of X, the expert stacks, z, h and all outputs;
  *    the router weight and bias are always fp32. bf16 data is accumulated in fp32 on MFMA; fp32
  *    data is computed in fp32 throughout.
  *  - Expert matrices are stored transposed relative to the page's x_t W notation, as [out][in]
@@ -40,13 +40,14 @@
 extern "C" {
 #endif
 
-#define ROM_ABI_VERSION 6
+#define ROM_ABI_VERSION 7
 #ifndef ROM_API
 #define ROM_API __attribute__((visibility("default")))
 #endif
 #define ROM_MAX_EXPERTS 64
 #define ROM_MAX_TOP_K 2
 #define ROM_MAX_TOKENS (1 << 24)
+#define ROM_MAX_DIM 65536     /* largest d_model, d_inner, d_out or channel count */
 #define ROM_MAX_CONV_WIDTH 8
 
 typedef enum {

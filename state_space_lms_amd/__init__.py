@@ -27,7 +27,7 @@ __all__ = ["route", "in_proj", "in_proj_weighted", "out_proj", "conv1d", "out_pr
            "route_workspace_bytes", "out_proj_workspace_bytes"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "librom.so")
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 ROM_OK, ROM_ERR_INVALID_ARGUMENT, ROM_ERR_UNSUPPORTED, ROM_ERR_WORKSPACE_TOO_SMALL, ROM_ERR_HIP = range(5)
 ROM_DTYPE_F32, ROM_DTYPE_BF16 = 0, 1
@@ -121,6 +121,27 @@ def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+def _want(t: torch.Tensor, shape, dtype, name: str) -> torch.Tensor:
+    """Shape and dtype of a tensor the library reads or writes in full: the C ABI receives only a pointer, so a
+    wrong-sized tensor would be read or written out of bounds. Checked before the device and layout checks."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t
+
+
+def _matrix(t: torch.Tensor, name: str):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    return t.shape
+
+
+def _same_device(routing: "Routing", t: torch.Tensor):
+    if torch.device(routing.device) != t.device:
+        raise ValueError(f"the routing buffers are on {routing.device}, the data on {t.device}")
+
+
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else (t.data_ptr() or None)
 
@@ -161,19 +182,22 @@ class Routing:
 def route(X: torch.Tensor, W_router: torch.Tensor, bias: Optional[torch.Tensor] = None, top_k: int = 1,
           permute: bool = False, routing: Optional[Routing] = None, stream=None) -> Routing:
     """rom_route: fp32 router, top-1 or top-2, probabilities, histogram, stable counting sort (and the permute)."""
-    _dev(X, "X")
-    _dev(W_router, "W_router")
+    T, dm = _matrix(X, "X")
+    _dtype_code(X)
     if W_router.dtype != torch.float32:
         raise TypeError("W_router must be fp32")
-    T, dm = X.shape
+    if W_router.dim() != 2 or W_router.shape[0] != dm:
+        raise ValueError(f"W_router must be [d_model = {dm}][E], got shape {tuple(W_router.shape)}")
     E = W_router.shape[1]
     if bias is not None:
+        _want(bias, (E,), torch.float32, "bias")
         _dev(bias, "bias")
-        if bias.dtype != torch.float32 or bias.shape != (E,):
-            raise ValueError("bias must be fp32 of shape [E]")
+    _dev(X, "X")
+    _dev(W_router, "W_router")
     r = routing if routing is not None else Routing(T, E, X.device, top_k)
     if (r.T, r.E, r.top_k) != (T, E, top_k):
         raise ValueError("routing buffers were sized for another T, E or top_k")
+    _same_device(r, X)
     if permute:
         if r.x_perm is None or r.x_perm.dtype != X.dtype or r.x_perm.shape != X.shape:
             r.x_perm = torch.empty_like(X)
@@ -189,14 +213,22 @@ def in_proj(X: torch.Tensor, routing: Routing, W_conv: torch.Tensor, W_gate: tor
             stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """rom_in_proj: x = sum over the token's experts of W_conv[e] X, z likewise with W_gate (token order, no
     probability scale)."""
-    for t, n in ((X, "X"), (W_conv, "W_conv"), (W_gate, "W_gate")):
-        _dev(t, n)
-    T, dm = X.shape
+    T, dm = _matrix(X, "X")
+    _dtype_code(X)
+    if W_conv.dim() != 3:
+        raise ValueError("W_conv must be [E][d_inner][d_model]")
     E, di, dm2 = W_conv.shape
     if dm2 != dm or W_gate.shape != W_conv.shape or W_conv.dtype != X.dtype or W_gate.dtype != X.dtype:
         raise ValueError("W_conv/W_gate must be [E][d_inner][d_model] in X's dtype")
     if E != routing.E:
         raise ValueError("expert count differs from the routing's")
+    if x_out is not None:
+        _want(x_out, (T, di), X.dtype, "x_out")
+    if z_out is not None:
+        _want(z_out, (T, di), X.dtype, "z_out")
+    for t, n in ((X, "X"), (W_conv, "W_conv"), (W_gate, "W_gate")):
+        _dev(t, n)
+    _same_device(routing, X)
     x_out = torch.empty((T, di), dtype=X.dtype, device=X.device) if x_out is None else _dev(x_out, "x_out")
     z_out = torch.empty((T, di), dtype=X.dtype, device=X.device) if z_out is None else _dev(z_out, "z_out")
     status = lib().rom_in_proj(_ptr(X), ctypes.byref(routing.struct), _dtype_code(X), T, dm, di, _ptr(W_conv),
@@ -208,14 +240,20 @@ def in_proj(X: torch.Tensor, routing: Routing, W_conv: torch.Tensor, W_gate: tor
 def in_proj_weighted(X: torch.Tensor, routing: Routing, W_in: torch.Tensor, y_out: Optional[torch.Tensor] = None,
                      stream=None) -> torch.Tensor:
     """rom_in_proj_weighted (Swimba): y = sum over the token's experts of p_t,e * W_in[e] X (token order)."""
-    _dev(X, "X")
-    _dev(W_in, "W_in")
-    T, dm = X.shape
+    T, dm = _matrix(X, "X")
+    _dtype_code(X)
+    if W_in.dim() != 3:
+        raise ValueError("W_in must be [E][d_out][d_model]")
     E, dout, dm2 = W_in.shape
     if dm2 != dm or W_in.dtype != X.dtype:
         raise ValueError("W_in must be [E][d_out][d_model] in X's dtype")
     if E != routing.E:
         raise ValueError("expert count differs from the routing's")
+    if y_out is not None:
+        _want(y_out, (T, dout), X.dtype, "y_out")
+    _dev(X, "X")
+    _dev(W_in, "W_in")
+    _same_device(routing, X)
     y_out = torch.empty((T, dout), dtype=X.dtype, device=X.device) if y_out is None else _dev(y_out, "y_out")
     status = lib().rom_in_proj_weighted(_ptr(X), ctypes.byref(routing.struct), _dtype_code(X), T, dm, dout,
                                         _ptr(W_in), _ptr(y_out), _stream(X.device, stream))
@@ -227,17 +265,20 @@ def conv1d(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] =
            activation: bool = True, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """rom_conv1d: the shared short causal depthwise convolution of each of n_seq sequences of x [T][C]
     (T = n_seq * seq_len, token order), weight [C][width], optional bias [C], optional SiLU."""
-    _dev(x, "x")
-    _dev(weight, "weight")
-    T, C = x.shape
+    T, C = _matrix(x, "x")
+    _dtype_code(x)
     if n_seq <= 0 or T % n_seq != 0:
         raise ValueError("T must be a multiple of n_seq")
     if weight.dim() != 2 or weight.shape[0] != C or weight.dtype != x.dtype:
         raise ValueError("weight must be [C][width] in x's dtype")
     if bias is not None:
+        _want(bias, (C,), x.dtype, "bias")
+    if y is not None:
+        _want(y, (T, C), x.dtype, "y")
+    _dev(x, "x")
+    _dev(weight, "weight")
+    if bias is not None:
         _dev(bias, "bias")
-        if bias.shape != (C,) or bias.dtype != x.dtype:
-            raise ValueError("bias must be [C] in x's dtype")
     y = torch.empty_like(x) if y is None else _dev(y, "y")
     status = lib().rom_conv1d(_ptr(x), _dtype_code(x), n_seq, T // n_seq, C, _ptr(weight), _ptr(bias),
                               weight.shape[1], ROM_ACT_SILU if activation else ROM_ACT_NONE, _ptr(y),
@@ -261,12 +302,17 @@ def out_proj_backward(d_out: torch.Tensor, z: torch.Tensor, h: torch.Tensor, rou
                       stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """rom_out_proj_backward: (dz, dh, dW_out) for the upstream gradient d_out, router probabilities held fixed.
     dW_out is fp32."""
-    for t, n in ((d_out, "d_out"), (z, "z"), (h, "h"), (W_out, "W_out")):
-        _dev(t, n)
-    T, di = z.shape
+    T, di = _matrix(z, "z")
+    if W_out.dim() != 3:
+        raise ValueError("W_out must be [E][d_model][d_inner]")
     E, dm, di2 = W_out.shape
     if di2 != di or h.shape != z.shape or d_out.shape != (T, dm) or E != routing.E:
         raise ValueError("shapes: d_out [T][d_model], z, h [T][d_inner], W_out [E][d_model][d_inner]")
+    if not (d_out.dtype == z.dtype == h.dtype == W_out.dtype):
+        raise ValueError("d_out, z, h and W_out must share one dtype")
+    for t, n in ((d_out, "d_out"), (z, "z"), (h, "h"), (W_out, "W_out")):
+        _dev(t, n)
+    _same_device(routing, z)
     dz, dh = torch.empty_like(z), torch.empty_like(z)
     dW = torch.empty((E, dm, di), dtype=torch.float32, device=z.device)
     ws = _bwd_workspace(routing, T, dm, di, z.device)
@@ -280,12 +326,17 @@ def out_proj_backward(d_out: torch.Tensor, z: torch.Tensor, h: torch.Tensor, rou
 def in_proj_backward(X: torch.Tensor, dx: torch.Tensor, dz: torch.Tensor, routing: "Routing", W_conv: torch.Tensor,
                      W_gate: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """rom_in_proj_backward: (dX, dW_conv, dW_gate) for the upstream gradients dx, dz; weight gradients are fp32."""
-    for t, n in ((X, "X"), (dx, "dx"), (dz, "dz"), (W_conv, "W_conv"), (W_gate, "W_gate")):
-        _dev(t, n)
-    T, dm = X.shape
+    T, dm = _matrix(X, "X")
+    if W_conv.dim() != 3:
+        raise ValueError("W_conv must be [E][d_inner][d_model]")
     E, di, dm2 = W_conv.shape
     if dm2 != dm or W_gate.shape != W_conv.shape or dx.shape != (T, di) or dz.shape != (T, di) or E != routing.E:
         raise ValueError("shapes: X [T][d_model], dx, dz [T][d_inner], W_conv, W_gate [E][d_inner][d_model]")
+    if not (X.dtype == dx.dtype == dz.dtype == W_conv.dtype == W_gate.dtype):
+        raise ValueError("X, dx, dz, W_conv and W_gate must share one dtype")
+    for t, n in ((X, "X"), (dx, "dx"), (dz, "dz"), (W_conv, "W_conv"), (W_gate, "W_gate")):
+        _dev(t, n)
+    _same_device(routing, X)
     dX = torch.empty_like(X)
     dWc = torch.empty((E, di, dm), dtype=torch.float32, device=X.device)
     dWg = torch.empty_like(dWc)
@@ -306,15 +357,23 @@ def out_proj(z: torch.Tensor, h: torch.Tensor, routing: Routing, W_out: torch.Te
              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
              stream=None) -> torch.Tensor:
     """rom_out_proj: out = sum over the token's experts of p_t,e * W_out[e] (SiLU(z) * h) (token order)."""
-    for t, n in ((z, "z"), (h, "h"), (W_out, "W_out")):
-        _dev(t, n)
-    T, di = z.shape
+    T, di = _matrix(z, "z")
+    _dtype_code(z)
+    if W_out.dim() != 3:
+        raise ValueError("W_out must be [E][d_model][d_inner]")
     E, dm, di2 = W_out.shape
     if di2 != di or h.shape != z.shape or h.dtype != z.dtype or W_out.dtype != z.dtype:
         raise ValueError("W_out must be [E][d_model][d_inner]; z, h [T][d_inner]; one dtype")
     if E != routing.E:
         raise ValueError("expert count differs from the routing's")
+    if out is not None:
+        _want(out, (T, dm), z.dtype, "out")
+    for t, n in ((z, "z"), (h, "h"), (W_out, "W_out")):
+        _dev(t, n)
     out = torch.empty((T, dm), dtype=z.dtype, device=z.device) if out is None else _dev(out, "out")
+    _same_device(routing, z)
+    if workspace is not None:
+        _dev(workspace, "workspace")
     need = out_proj_workspace_bytes(T, di, z.dtype)
     if workspace is None and need > 0:
         if routing.out_workspace is None or routing.out_workspace.numel() < need:

@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "rom.h"
 #include "rom_internal.h"
 
@@ -44,6 +46,7 @@ rom_status check_dims(int32_t T, int32_t d, const char *dname) {
     if (T > ROM_MAX_TOKENS) return fail(ROM_ERR_UNSUPPORTED, "T = %d exceeds ROM_MAX_TOKENS", T);
     if (d <= 0) return fail(ROM_ERR_INVALID_ARGUMENT, "%s = %d must be positive", dname, d);
     if (d % 64 != 0) return fail(ROM_ERR_UNSUPPORTED, "%s = %d is not a multiple of 64", dname, d);
+    if (d > ROM_MAX_DIM) return fail(ROM_ERR_UNSUPPORTED, "%s = %d exceeds ROM_MAX_DIM (%d)", dname, d, ROM_MAX_DIM);
     return ROM_OK;
 }
 
@@ -100,25 +103,23 @@ int rom_abi_version(void) { return ROM_ABI_VERSION; }
 
 size_t rom_route_workspace_bytes(int32_t T, int32_t E) {
     if (T <= 0 || E <= 0) return 0;
-    const size_t b = (size_t)ROM_MAX_TOP_K * E * (size_t)rom::route_workgroups(T) * sizeof(int32_t);
+    const size_t b = rom::route_workspace_words(T, E) * sizeof(int32_t);
     return (b + 255) & ~(size_t)255;
 }
 
-rom_status rom_route(const void *X, rom_dtype x_dtype, int32_t T, int32_t d_model, const float *W_router,
-                     const float *bias, int32_t E, int32_t top_k, rom_routing *routing, void *X_perm,
-                     void *workspace, size_t workspace_bytes, void *stream) {
-    g_last_error[0] = '\0';
+}  // extern "C"
+
+namespace {
+
+// Argument validation of rom_route (workspace checks excluded).
+rom_status check_route_args(const void *X, rom_dtype x_dtype, int32_t T, int32_t d_model, const float *W_router,
+                            const float *bias, int32_t E, int32_t top_k, rom_routing *routing, void *X_perm) {
     rom_status s;
     if ((s = check_dtype(x_dtype)) != ROM_OK) return s;
     if ((s = check_dims(T, d_model, "d_model")) != ROM_OK) return s;
     if ((s = check_experts(E, top_k)) != ROM_OK) return s;
     if (routing == nullptr) return fail(ROM_ERR_INVALID_ARGUMENT, "routing is NULL");
-    if (T == 0) {
-        routing->T = 0;
-        routing->E = E;
-        routing->top_k = top_k;
-        return ROM_OK;
-    }
+    if (T == 0) return ROM_OK;
     ROM_CHECK_PTR(X, 16);
     ROM_CHECK_PTR(W_router, 16);
     if (bias != nullptr && !aligned(bias, 4)) return fail(ROM_ERR_INVALID_ARGUMENT, "bias is not 4-byte aligned");
@@ -134,6 +135,38 @@ rom_status rom_route(const void *X, rom_dtype x_dtype, int32_t T, int32_t d_mode
         const size_t xb = (size_t)T * d_model * elem_size(x_dtype);
         if (overlap(X, xb, X_perm, xb)) return fail(ROM_ERR_INVALID_ARGUMENT, "X_perm overlaps X");
     }
+    return ROM_OK;
+}
+
+rom_status route_enqueue(const void *X, rom_dtype x_dtype, int32_t T, int32_t d_model, const float *W_router,
+                         const float *bias, int32_t E, int32_t top_k, rom_routing *routing, void *X_perm,
+                         int32_t *workspace, void *stream, const char *what) {
+    routing->T = T;
+    routing->E = E;
+    routing->top_k = top_k;
+    routing->reserved = 0;
+    hipError_t err = rom::launch_route(X, x_dtype, T, d_model, W_router, bias, E, *routing, X_perm, workspace,
+                                       static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return hip_fail(err, what);
+    return ROM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rom_status rom_route(const void *X, rom_dtype x_dtype, int32_t T, int32_t d_model, const float *W_router,
+                     const float *bias, int32_t E, int32_t top_k, rom_routing *routing, void *X_perm,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+    g_last_error[0] = '\0';
+    rom_status s = check_route_args(X, x_dtype, T, d_model, W_router, bias, E, top_k, routing, X_perm);
+    if (s != ROM_OK) return s;
+    if (T == 0) {
+        routing->T = 0;
+        routing->E = E;
+        routing->top_k = top_k;
+        return ROM_OK;
+    }
     const size_t need = rom_route_workspace_bytes(T, E);
     if (T > rom::kRouteSmallT) {
         if (workspace == nullptr) return fail(ROM_ERR_WORKSPACE_TOO_SMALL, "workspace is NULL (%zu bytes needed)", need);
@@ -141,14 +174,8 @@ rom_status rom_route(const void *X, rom_dtype x_dtype, int32_t T, int32_t d_mode
     }
     if (workspace_bytes < need && T > rom::kRouteSmallT)
         return fail(ROM_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
-    routing->T = T;
-    routing->E = E;
-    routing->top_k = top_k;
-    routing->reserved = 0;
-    hipError_t err = rom::launch_route(X, x_dtype, T, d_model, W_router, bias, E, *routing, X_perm,
-                                       static_cast<int32_t *>(workspace), static_cast<hipStream_t>(stream));
-    if (err != hipSuccess) return hip_fail(err, "rom_route launch");
-    return ROM_OK;
+    return route_enqueue(X, x_dtype, T, d_model, W_router, bias, E, top_k, routing, X_perm,
+                         static_cast<int32_t *>(workspace), stream, "rom_route launch");
 }
 
 rom_status rom_in_proj(const void *X, const rom_routing *routing, rom_dtype dtype, int32_t T, int32_t d_model,

@@ -297,13 +297,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_wgrad_gemm_bf16(WgradArgs p)
 template <int BM, int BN, int WGM, int WGN>
 hipError_t launch_wgrad_t(const WgradArgs &a, hipStream_t s) {
     const size_t smem = (size_t)2 * (BM + BN) * 64 * 2;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_wgrad_gemm_bf16<BM, BN, WGM, WGN>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (err != hipSuccess) return err;
-        attr_set = true;
-    }
+    static LdsAttrOnce attr;
+    hipError_t err =
+        set_lds_limit_once(attr, reinterpret_cast<const void *>(&k_wgrad_gemm_bf16<BM, BN, WGM, WGN>), smem);
+    if (err != hipSuccess) return err;
     const unsigned grid = (unsigned)(a.E * (a.M / BM) * (a.N / BN));
     hipLaunchKernelGGL((k_wgrad_gemm_bf16<BM, BN, WGM, WGN>), dim3(grid), dim3(64 * WGM * WGN), smem, s, a);
     return hipGetLastError();

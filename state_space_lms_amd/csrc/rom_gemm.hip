@@ -160,6 +160,126 @@ constexpr size_t gemm_lds_bytes(int BM, int BN, int BK, int NSTAGE, int WGM) {
     return (size_t)(NSTAGE * (BM + BN) * BK > crows * BN ? NSTAGE * (BM + BN) * BK : crows * BN) * 2;
 }
 
+// Epilogue of the bf16 grouped GEMMs: the accumulators of wave (wm, wn) (FM x FN blocks of 32 x 32 in the
+// C^T layout) go back to their tokens' rows of C, columns [n0, n0 + BN), scaled by p_t for the out-projection;
+// with p.accumulate they are added to the values already stored (one rounding of the sum). The LDS bytes of
+// the pipeline stages are reused; the caller has no copies in flight.
+template <int BM, int BN, int BK, int NSTAGE, int WGM, int WGN, bool OUT>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs &p, f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32], int wm,
+                                              int wn, int rows, int n0, uint16_t *C, const int *s_tok,
+                                              const float *s_prob, uint16_t *smem) {
+    constexpr int NT = 64 * WGM * WGN;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
+    constexpr int FM = WM / 32, FN = WN / 32;
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
+    // epilogue; rows go back to their tokens, scaled by p_t for the out-projection
+    if (p.accumulate) {
+        // C += result (one rounding of the sum), through LDS in fp32: pass q takes block rows
+        // [q*IPP, q*IPP + IPP) of every wave, i.e. rows wm*WM + i*32 + (0..31) of the tile. Register r of block
+        // (i, j) holds column 8*(r/4) + 4*half + r%4 of row lane%32; it is written as 4-float chunks
+        // (16-byte chunk index XOR-swizzled by the pass row), then every thread adds 8 consecutive columns to
+        // the stored bf16 values of a token row with 16-byte loads and stores.
+        constexpr int CPR4 = BN / 4;                                  // 16-byte fp32 chunks per row
+        constexpr int PROWS = WGM * 32;                               // pass rows per block row
+        constexpr int IPP = (int)(gemm_lds_bytes(BM, BN, BK, NSTAGE, WGM) / ((size_t)PROWS * BN * 4));
+        static_assert(IPP >= 1, "fp32 accumulate pass");
+        constexpr int NPASS = (FM + IPP - 1) / IPP;
+        constexpr int SWM = (CPR4 < 32 ? CPR4 : 32) - 1;             // chunk swizzle mask (stays in the row)
+        float *ct = reinterpret_cast<float *>(smem);
+        auto prow_of = [&](int wmr, int ii, int r) { return (ii * WGM + wmr) * 32 + r; };  // LDS row
+        constexpr int CPR = BN / 8;  // 8-column units per row
+        constexpr int UNITS = IPP * PROWS * CPR;
+        constexpr int UPT = UNITS % NT == 0 ? UNITS / NT : 0;  // units per thread, when they divide evenly
+#pragma unroll
+        for (int q = 0; q < NPASS; ++q) {
+            // the pass's stored values are loaded first, all at once, so that their latency overlaps the LDS
+            // pass below instead of one round trip per unit (rows clamped into the tile: every load is in
+            // bounds, and only the stored rows are used)
+            uint4 old[UPT > 0 ? UPT : 1];
+            if constexpr (UPT > 0) {
+#pragma unroll
+                for (int k = 0; k < UPT; ++k) {
+                    const int u = tid + k * NT;
+                    const int lr = u / CPR, c = u % CPR;
+                    const int ii = lr / PROWS, wmr = (lr / 32) % WGM, i = q * IPP + ii;
+                    const int row = min(wmr * WM + i * 32 + (lr & 31), BM - 1);
+                    old[k] = *reinterpret_cast<const uint4 *>(C + (size_t)s_tok[row] * p.N0 + n0 + c * 8);
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int ii = 0; ii < IPP; ++ii) {
+                const int i = q * IPP + ii;
+                if (i < FM) {
+                    const int lr = prow_of(wm, ii, lane & 31);
+                    const float sc = OUT ? s_prob[wm * WM + i * 32 + (lane & 31)] : 1.0f;
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const int ch = (wn * WN + j * 32 + 8 * g + 4 * half) >> 2;
+                            float4 v;
+                            v.x = acc[i][j][4 * g] * sc;
+                            v.y = acc[i][j][4 * g + 1] * sc;
+                            v.z = acc[i][j][4 * g + 2] * sc;
+                            v.w = acc[i][j][4 * g + 3] * sc;
+                            *reinterpret_cast<float4 *>(ct + lr * BN + ((ch ^ (lr & SWM)) << 2)) = v;
+                        }
+                }
+            }
+            __syncthreads();
+            // unit u: LDS row lr = u / CPR (tile row wmr * WM + i * 32 + lr % 32), 8 columns from 8 (u % CPR)
+            auto add_store = [&](int u, const uint4 &ov) {
+                const int lr = u / CPR, c = u % CPR;
+                const int ii = lr / PROWS, wmr = (lr / 32) % WGM, i = q * IPP + ii;
+                const int row = wmr * WM + i * 32 + (lr & 31);  // tile row
+                if (i < FM && row < rows) {
+                    uint4 *dst = reinterpret_cast<uint4 *>(C + (size_t)s_tok[row] * p.N0 + n0 + c * 8);
+                    const float4 a = *reinterpret_cast<const float4 *>(ct + lr * BN + (((2 * c) ^ (lr & SWM)) << 2));
+                    const float4 b = *reinterpret_cast<const float4 *>(ct + lr * BN + (((2 * c + 1) ^ (lr & SWM)) << 2));
+                    uint4 pk;
+                    pk.x = pack_bf16x2(__uint_as_float(ov.x << 16) + a.x, __uint_as_float(ov.x & 0xFFFF0000u) + a.y);
+                    pk.y = pack_bf16x2(__uint_as_float(ov.y << 16) + a.z, __uint_as_float(ov.y & 0xFFFF0000u) + a.w);
+                    pk.z = pack_bf16x2(__uint_as_float(ov.z << 16) + b.x, __uint_as_float(ov.z & 0xFFFF0000u) + b.y);
+                    pk.w = pack_bf16x2(__uint_as_float(ov.w << 16) + b.z, __uint_as_float(ov.w & 0xFFFF0000u) + b.w);
+                    *dst = pk;
+                }
+            };
+            if constexpr (UPT > 0) {
+#pragma unroll
+                for (int k = 0; k < UPT; ++k) add_store(tid + k * NT, old[k]);
+            } else {
+                for (int u = tid; u < UNITS; u += NT) {
+                    const int lr = u / CPR, c = u % CPR;
+                    const int ii = lr / PROWS, wmr = (lr / 32) % WGM, i = q * IPP + ii;
+                    const int row = min(wmr * WM + i * 32 + (lr & 31), BM - 1);
+                    add_store(u, *reinterpret_cast<const uint4 *>(C + (size_t)s_tok[row] * p.N0 + n0 + c * 8));
+                }
+            }
+        }
+        return;
+    }
+    // through LDS (no copies are in flight after the last step), in one pass or one band of waves at a time
+    float sc[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) sc[i] = OUT ? s_prob[wm * WM + i * 32 + (lane & 31)] : 1.0f;
+    constexpr int PASSES = ctile_passes(BM, BN, WGM);
+    if constexpr (PASSES == 1) {
+        __syncthreads();
+        acc_to_ctile<FM, FN, BN>(acc, smem, wm * WM, wn * WN, lane, sc);
+        __syncthreads();
+        ctile_to_global<BN, NT>(smem, BM, rows, s_tok, C, p.N0, n0, tid);
+    } else {
+#pragma unroll
+        for (int q = 0; q < PASSES; ++q) {
+            __syncthreads();
+            if (wm == q) acc_to_ctile<FM, FN, BN>(acc, smem, 0, wn * WN, lane, sc);
+            __syncthreads();
+            ctile_to_global<BN, NT>(smem, WM, rows - q * WM, s_tok + q * WM, C, p.N0, n0, tid);
+        }
+    }
+}
+
 template <int BM, int BN, int BK, int NSTAGE, int WGM, int WGN, bool OUT, int SCHED, bool KSPLIT>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p) {
     constexpr int NW = WGM * WGN;
@@ -400,112 +520,169 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
     }
     }
 
-    // epilogue; rows go back to their tokens, scaled by p_t for the out-projection
-    if (p.accumulate) {
-        // C += result (one rounding of the sum), through LDS in fp32: pass q takes block rows
-        // [q*IPP, q*IPP + IPP) of every wave, i.e. rows wm*WM + i*32 + (0..31) of the tile. Register r of block
-        // (i, j) holds column 8*(r/4) + 4*half + r%4 of row lane%32; it is written as 4-float chunks
-        // (16-byte chunk index XOR-swizzled by the pass row), then every thread adds 8 consecutive columns to
-        // the stored bf16 values of a token row with 16-byte loads and stores.
-        constexpr int CPR4 = BN / 4;                                  // 16-byte fp32 chunks per row
-        constexpr int PROWS = WGM * 32;                               // pass rows per block row
-        constexpr int IPP = (int)(gemm_lds_bytes(BM, BN, BK, NSTAGE, WGM) / ((size_t)PROWS * BN * 4));
-        static_assert(IPP >= 1, "fp32 accumulate pass");
-        constexpr int NPASS = (FM + IPP - 1) / IPP;
-        constexpr int SWM = (CPR4 < 32 ? CPR4 : 32) - 1;             // chunk swizzle mask (stays in the row)
-        float *ct = reinterpret_cast<float *>(smem);
-        auto prow_of = [&](int wmr, int ii, int r) { return (ii * WGM + wmr) * 32 + r; };  // LDS row
-        constexpr int CPR = BN / 8;  // 8-column units per row
-        constexpr int UNITS = IPP * PROWS * CPR;
-        constexpr int UPT = UNITS % NT == 0 ? UNITS / NT : 0;  // units per thread, when they divide evenly
-#pragma unroll
-        for (int q = 0; q < NPASS; ++q) {
-            // the pass's stored values are loaded first, all at once, so that their latency overlaps the LDS
-            // pass below instead of one round trip per unit (rows clamped into the tile: every load is in
-            // bounds, and only the stored rows are used)
-            uint4 old[UPT > 0 ? UPT : 1];
-            if constexpr (UPT > 0) {
-#pragma unroll
-                for (int k = 0; k < UPT; ++k) {
-                    const int u = tid + k * NT;
-                    const int lr = u / CPR, c = u % CPR;
-                    const int ii = lr / PROWS, wmr = (lr / 32) % WGM, i = q * IPP + ii;
-                    const int row = min(wmr * WM + i * 32 + (lr & 31), BM - 1);
-                    old[k] = *reinterpret_cast<const uint4 *>(C + (size_t)s_tok[row] * p.N0 + n0 + c * 8);
-                }
-            }
-            __syncthreads();
-#pragma unroll
-            for (int ii = 0; ii < IPP; ++ii) {
-                const int i = q * IPP + ii;
-                if (i < FM) {
-                    const int lr = prow_of(wm, ii, lane & 31);
-                    const float sc = OUT ? s_prob[wm * WM + i * 32 + (lane & 31)] : 1.0f;
-#pragma unroll
-                    for (int j = 0; j < FN; ++j)
-#pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            const int ch = (wn * WN + j * 32 + 8 * g + 4 * half) >> 2;
-                            float4 v;
-                            v.x = acc[i][j][4 * g] * sc;
-                            v.y = acc[i][j][4 * g + 1] * sc;
-                            v.z = acc[i][j][4 * g + 2] * sc;
-                            v.w = acc[i][j][4 * g + 3] * sc;
-                            *reinterpret_cast<float4 *>(ct + lr * BN + ((ch ^ (lr & SWM)) << 2)) = v;
-                        }
-                }
-            }
-            __syncthreads();
-            // unit u: LDS row lr = u / CPR (tile row wmr * WM + i * 32 + lr % 32), 8 columns from 8 (u % CPR)
-            auto add_store = [&](int u, const uint4 &ov) {
-                const int lr = u / CPR, c = u % CPR;
-                const int ii = lr / PROWS, wmr = (lr / 32) % WGM, i = q * IPP + ii;
-                const int row = wmr * WM + i * 32 + (lr & 31);  // tile row
-                if (i < FM && row < rows) {
-                    uint4 *dst = reinterpret_cast<uint4 *>(C + (size_t)s_tok[row] * p.N0 + n0 + c * 8);
-                    const float4 a = *reinterpret_cast<const float4 *>(ct + lr * BN + (((2 * c) ^ (lr & SWM)) << 2));
-                    const float4 b = *reinterpret_cast<const float4 *>(ct + lr * BN + (((2 * c + 1) ^ (lr & SWM)) << 2));
-                    uint4 pk;
-                    pk.x = pack_bf16x2(__uint_as_float(ov.x << 16) + a.x, __uint_as_float(ov.x & 0xFFFF0000u) + a.y);
-                    pk.y = pack_bf16x2(__uint_as_float(ov.y << 16) + a.z, __uint_as_float(ov.y & 0xFFFF0000u) + a.w);
-                    pk.z = pack_bf16x2(__uint_as_float(ov.z << 16) + b.x, __uint_as_float(ov.z & 0xFFFF0000u) + b.y);
-                    pk.w = pack_bf16x2(__uint_as_float(ov.w << 16) + b.z, __uint_as_float(ov.w & 0xFFFF0000u) + b.w);
-                    *dst = pk;
-                }
-            };
-            if constexpr (UPT > 0) {
-#pragma unroll
-                for (int k = 0; k < UPT; ++k) add_store(tid + k * NT, old[k]);
-            } else {
-                for (int u = tid; u < UNITS; u += NT) {
-                    const int lr = u / CPR, c = u % CPR;
-                    const int ii = lr / PROWS, wmr = (lr / 32) % WGM, i = q * IPP + ii;
-                    const int row = min(wmr * WM + i * 32 + (lr & 31), BM - 1);
-                    add_store(u, *reinterpret_cast<const uint4 *>(C + (size_t)s_tok[row] * p.N0 + n0 + c * 8));
-                }
-            }
-        }
-        return;
+    gemm_epilogue<BM, BN, BK, NSTAGE, WGM, WGN, OUT>(p, acc, wm, wn, rows, n0, C, s_tok, s_prob, smem);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Ping-pong bf16 grouped GEMM: 256 x 256 tiles, K step 64, two LDS stages, 8 waves in two groups of four.
+// The waves of a workgroup are spread over the SIMDs in order, so waves w and w + 4 share a SIMD: group 0
+// (waves 0-3) and group 1 (waves 4-7) hold one wave on every SIMD. The groups take turns, two phases per K
+// step separated by barriers: in one phase a group issues the 32 MFMAs of a K step from fragments it already
+// holds in registers (at raised priority), while the other group reads its fragments of a step from LDS; so a
+// SIMD's matrix core is fed by one wave while the other waits for LDS. Wave (g, q) owns the 128 x 64 block
+// (wm, wn) = (q / 2, 2 g + q % 2) of the tile, laid out as in k_grouped_gemm_bf16's 8-wave 256 x 256 tile,
+// whose epilogue it shares.
+//
+// Timeline, phase 2k and 2k + 1 of K step k (stage k % 2 holds step k):
+//   phase 2k:     group 0: MFMAs of step k            group 1: reads step k's fragments
+//                 every wave: its copies of step k + 1 have landed (vmcnt 0)           -- barrier
+//   phase 2k + 1: every wave issues its copies of step k + 2 into stage k % 2 (step k's reads are done)
+//                 group 0: reads step k + 1's fragments    group 1: MFMAs of step k    -- barrier
+// so the copies of a step are in flight for two phases. The prologue copies steps 0 and 1 and gives group 0
+// the fragments of step 0.
+template <bool OUT>
+__global__ __launch_bounds__(512) void k_grouped_gemm_pp(GemmArgs p) {
+    constexpr int BM = 256, BN = 256, BK = 64, NSTAGE = 2, WGM = 2, WGN = 4, NW = 8, NT = 512;
+    constexpr int KCH = BK / 8, RG = 64 / KCH;
+    constexpr int A_DMA = BM / RG / NW, B_DMA = BN / RG / NW, PER_STEP = A_DMA + B_DMA;
+    constexpr int STAGE = (BM + BN) * BK;
+    constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32, NKK = BK / 16;
+    static_assert(PER_STEP < 16, "vmcnt");
+
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    __shared__ int s_tok[BM];
+    __shared__ int s_arow[BM];
+    __shared__ float s_prob[OUT ? BM : 1];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int mt, nt, e, slot0, rows;
+    if (!tile_of_block(p, mt, nt)) return;
+    if (!locate_mtile<BM>(p.offsets, p.E, mt, e, slot0, rows)) return;
+    const int which = nt / p.n_tiles_per_b;
+    const int n0 = (nt % p.n_tiles_per_b) * BN;
+    const int K = p.K;
+    const uint16_t *Bsrc = static_cast<const uint16_t *>(which ? p.B1 : p.B0) + ((size_t)e * p.N0 + n0) * K;
+    uint16_t *C = static_cast<uint16_t *>(which ? p.C1 : p.C0);
+
+    // rows past the group's end repeat its last row (in-bounds, finite data); they are never stored
+    for (int i = tid; i < BM; i += NT) {
+        const int slot = slot0 + min(i, rows - 1);
+        const int tok = p.perm[slot];
+        s_tok[i] = tok;
+        s_arow[i] = (OUT && !p.a_by_token) ? slot : tok;
+        if (OUT) s_prob[i] = p.prob[tok];
     }
-    // through LDS (no copies are in flight after the last step), in one pass or one band of waves at a time
-    float sc[FM];
+    __syncthreads();
+
+    // copy sources, as in k_grouped_gemm_bf16: lane i fills row g*RG + i/KCH, physical chunk i%KCH
+    const int dr = lane / KCH, dpc = lane % KCH;
+    const uint16_t *a_dma[A_DMA];
+    const uint16_t *b_dma[B_DMA];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) sc[i] = OUT ? s_prob[wm * WM + i * 32 + (lane & 31)] : 1.0f;
-    constexpr int PASSES = ctile_passes(BM, BN, WGM);
-    if constexpr (PASSES == 1) {
-        __syncthreads();
-        acc_to_ctile<FM, FN, BN>(acc, smem, wm * WM, wn * WN, lane, sc);
-        __syncthreads();
-        ctile_to_global<BN, NT>(smem, BM, rows, s_tok, C, p.N0, n0, tid);
+    for (int j = 0; j < A_DMA; ++j) {
+        const int row = (wave * A_DMA + j) * RG + dr;
+        a_dma[j] = static_cast<const uint16_t *>(p.A0) + (size_t)s_arow[row] * K + (dpc ^ lds_swz<KCH>(row)) * 8;
+    }
+#pragma unroll
+    for (int j = 0; j < B_DMA; ++j) {
+        const int row = (wave * B_DMA + j) * RG + dr;
+        b_dma[j] = Bsrc + (size_t)row * K + (dpc ^ lds_swz<KCH>(row)) * 8;
+    }
+    auto issue_copies = [&](int kt, int stage) {
+        uint16_t *as = smem + stage * STAGE;
+        uint16_t *bs = as + BM * BK;
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int j = 0; j < A_DMA; ++j) dma16_to_lds(a_dma[j] + k0, as + (wave * A_DMA + j) * RG * BK);
+#pragma unroll
+        for (int j = 0; j < B_DMA; ++j) dma16_to_lds(b_dma[j] + k0, bs + (wave * B_DMA + j) * RG * BK);
+    };
+
+    const int g = wave >> 2, q = wave & 3;
+    const int wm = q >> 1, wn = 2 * g + (q & 1);
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int half = lane >> 5;
+    const int a_frag0 = (wm * WM + (lane & 31)) * BK;
+    const int b_frag0 = BM * BK + (wn * WN + (lane & 31)) * BK;
+    const int swz = lds_swz<KCH>(lane & 31);
+    bf16x8 af[NKK][FM], bfr[NKK][FN];
+    auto load_step = [&](int stg) {
+        const uint16_t *st = smem + stg * STAGE;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const int co = ((kk * 2 + half) ^ swz) * 8;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) af[kk][i] = *reinterpret_cast<const bf16x8 *>(st + a_frag0 + i * 32 * BK + co);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bfr[kk][j] = *reinterpret_cast<const bf16x8 *>(st + b_frag0 + j * 32 * BK + co);
+        }
+    };
+    auto mfma_step = [&]() {
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk][j], af[kk][i], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
+    };
+    auto barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    const int nk = K / BK;
+    issue_copies(0, 0);
+    if (nk > 1) {
+        issue_copies(1, 1);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(PER_STEP));  // step 0 has landed
     } else {
-#pragma unroll
-        for (int q = 0; q < PASSES; ++q) {
-            __syncthreads();
-            if (wm == q) acc_to_ctile<FM, FN, BN>(acc, smem, 0, wn * WN, lane, sc);
-            __syncthreads();
-            ctile_to_global<BN, NT>(smem, WM, rows - q * WM, s_tok + q * WM, C, p.N0, n0, tid);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    }
+    barrier();
+    // each group runs its own copy of the loop (the same barriers, two per K step), so that the compiler
+    // keeps one set of fragment registers per wave
+    if (g == 0) {
+        load_step(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+        barrier();
+        for (int k = 0; k < nk; ++k) {
+            const int st = k & 1;
+            mfma_step();                                      // phase 2k: step k
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // the copies of step k + 1 have landed
+            barrier();
+            if (k + 2 < nk) issue_copies(k + 2, st);          // phase 2k + 1
+            // past the last step this reads a stage that is never used again (in bounds)
+            load_step(st ^ 1);
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+            barrier();
+        }
+    } else {
+        barrier();
+        for (int k = 0; k < nk; ++k) {
+            const int st = k & 1;
+            load_step(st);                                    // phase 2k: step k's fragments
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // and the copies of step k + 1 have landed
+            barrier();
+            if (k + 2 < nk) issue_copies(k + 2, st);          // phase 2k + 1
+            mfma_step();
+            barrier();
         }
     }
+    gemm_epilogue<BM, BN, BK, NSTAGE, WGM, WGN, OUT>(p, acc, wm, wn, rows, n0, C, s_tok, s_prob, smem);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -670,19 +847,6 @@ __global__ __launch_bounds__(64 * NW) void k_grouped_gemv_bf16(GemmArgs p) {
     }
 }
 
-// Compute units of the current device (cached per device).
-static int device_cus() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
 template <bool OUT>
 static hipError_t launch_gemv(const GemmArgs &a0, int nB, hipStream_t s) {
     GemmArgs a = a0;
@@ -782,14 +946,15 @@ __global__ __launch_bounds__(256) void k_grouped_gemm_f32(GemmArgs p) {
 
 
 // XCD-aware grouping of M-tiles (0 = off); ROM_GROUP_M overrides it for tuning sweeps.
+static int env_int(const char *name, int dflt, int lo, int hi) {
+    const char *v = getenv(name);
+    const int c = v ? atoi(v) : dflt;
+    return (c < lo || c > hi) ? dflt : c;
+}
+// read once per process (thread-safe static initialisation)
 static int group_m_choice() {
-    static int cached = -2;
-    if (cached == -2) {
-        const char *v = getenv("ROM_GROUP_M");
-        cached = v ? atoi(v) : 0;
-        if (cached < 0 || cached > 64) cached = 0;
-    }
-    return cached;
+    static const int v = env_int("ROM_GROUP_M", 0, 0, 64);
+    return v;
 }
 
 template <int BM, int BN, int BK, int NSTAGE, int WGM, int WGN, bool OUT, int SCHED, bool KSPLIT>
@@ -810,16 +975,29 @@ static hipError_t launch_bf16(const GemmArgs &a0, int nB, hipStream_t s) {
         grid = (unsigned)a.m_tiles * a.n_tiles;
     }
     const size_t smem = gemm_lds_bytes(BM, BN, BK, NSTAGE, WGM);
-    static bool attr_set = false;  // per process; the attribute is per function
-    if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&k_grouped_gemm_bf16<BM, BN, BK, NSTAGE, WGM, WGN, OUT, SCHED, KSPLIT>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (err != hipSuccess) return err;
-        attr_set = true;
-    }
+    static LdsAttrOnce attr;
+    hipError_t err = set_lds_limit_once(
+        attr, reinterpret_cast<const void *>(&k_grouped_gemm_bf16<BM, BN, BK, NSTAGE, WGM, WGN, OUT, SCHED, KSPLIT>),
+        smem);
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL((k_grouped_gemm_bf16<BM, BN, BK, NSTAGE, WGM, WGN, OUT, SCHED, KSPLIT>), dim3(grid), dim3(64 * WGM * WGN),
                        smem, s, a);
+    return hipGetLastError();
+}
+
+template <bool OUT>
+static hipError_t launch_pp(const GemmArgs &a0, int nB, hipStream_t s) {
+    GemmArgs a = a0;
+    a.n_tiles_per_b = a.N0 / 256;
+    a.n_tiles = nB * a.n_tiles_per_b;
+    a.m_tiles = (a.T + a.E * 255) / 256;
+    a.group_m = 0;
+    const unsigned grid = (unsigned)a.m_tiles * a.n_tiles;
+    const size_t smem = gemm_lds_bytes(256, 256, 64, 2, 2);
+    static LdsAttrOnce attr;
+    hipError_t err = set_lds_limit_once(attr, reinterpret_cast<const void *>(&k_grouped_gemm_pp<OUT>), smem);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((k_grouped_gemm_pp<OUT>), dim3(grid), dim3(512), smem, s, a);
     return hipGetLastError();
 }
 
@@ -836,19 +1014,15 @@ constexpr TileCfg kTiles[] = {
     {320, 256, 64, 2, 2, 4, 1},  // 7: 8 waves (160x64 each), BK 64, 2 stages (144 KiB), C tile in 2 passes
     {256, 256, 64, 2, 2, 4, 2},  // 8: as 0, barrier ahead of each step's last MFMAs
     {320, 256, 64, 2, 2, 4, 2},  // 9: as 7, barrier ahead of each step's last MFMAs
+    {256, 256, 64, 2, 2, 4, 3},  // 10: ping-pong (k_grouped_gemm_pp): 8 waves in two alternating groups
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 // Optional override of the tile choice (tuning sweeps): ROM_TILE_IN / ROM_TILE_OUT = index above.
 static int tile_override(bool out) {
-    static int cached[2] = {-2, -2};
-    int &c = cached[out ? 1 : 0];
-    if (c == -2) {
-        const char *v = getenv(out ? "ROM_TILE_OUT" : "ROM_TILE_IN");
-        c = v ? atoi(v) : -1;
-        if (c < 0 || c >= kNumTiles) c = -1;
-    }
-    return c;
+    static const int in_v = env_int("ROM_TILE_IN", -1, 0, kNumTiles - 1);
+    static const int out_v = env_int("ROM_TILE_OUT", -1, 0, kNumTiles - 1);
+    return out ? out_v : in_v;
 }
 
 
@@ -886,6 +1060,9 @@ static hipError_t launch_bf16_auto(const GemmArgs &a, int nB, hipStream_t s) {
         case 7: return launch_bf16<320, 256, 64, 2, 2, 4, OUT, 1, KSPLIT>(a, nB, s);
         case 8: return launch_bf16<256, 256, 64, 2, 2, 4, OUT, 2, KSPLIT>(a, nB, s);
         case 9: return launch_bf16<320, 256, 64, 2, 2, 4, OUT, 2, KSPLIT>(a, nB, s);
+        case 10:
+            if constexpr (!KSPLIT) return launch_pp<OUT>(a, nB, s);
+            return launch_bf16<256, 256, 64, 2, 2, 4, OUT, 2, KSPLIT>(a, nB, s);
         default: return launch_bf16<128, 64, 64, 4, 2, 2, OUT, 0, KSPLIT>(a, nB, s);
     }
 }

@@ -5,9 +5,45 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "rom.h"
 
 namespace rom {
+
+// ---- per-device caches (the library's only state). Each entry is filled once per device, thread-safely.
+constexpr int kMaxDevices = 64;
+
+// A kernel's dynamic-LDS limit, raised once per device on first use (the attribute belongs to the kernel
+// as loaded on the current device). One instance per kernel instantiation (a function-local static).
+struct LdsAttrOnce {
+    std::once_flag flag[kMaxDevices];
+    hipError_t err[kMaxDevices] = {};
+};
+inline hipError_t set_lds_limit_once(LdsAttrOnce &o, const void *fn, size_t bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(o.flag[dev], [&] {
+        o.err[dev] = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    });
+    return o.err[dev];
+}
+
+// Compute units of the current device (cached per device; 256 if the query fails).
+inline int device_cus() {
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 // Fewest tokens per workgroup of the router-logits kernel (8; 32 when T is large), tokens per
 // workgroup of the scatter kernel.
@@ -21,6 +57,20 @@ constexpr int kDecodeMaxT = 64;
 
 // Upper bound of router-logits workgroups for T tokens (sizes the per-workgroup histogram workspace).
 inline int route_workgroups(int T) { return (T + kRouteMinTokensPerWG - 1) / kRouteMinTokensPerWG; }
+inline int scatter_workgroups(int T) { return (T + kScatterTokensPerWG - 1) / kScatterTokensPerWG; }
+
+// Router workspace (int32 words): the partial histograms [K][E][logits workgroups] (sized for the smallest
+// tokens-per-workgroup), then the scatter bases [K][E][scatter workgroups] and the totals [K][E] that the
+// prefix-scan kernel writes when the scatter would otherwise re-read too many partial histograms.
+inline size_t route_workspace_words(int T, int E) {
+    return (size_t)ROM_MAX_TOP_K * E * ((size_t)route_workgroups(T) + scatter_workgroups(T) + 1);
+}
+inline size_t route_bases_offset(int T, int E) { return (size_t)ROM_MAX_TOP_K * E * route_workgroups(T); }
+
+// With more than this many (scatter workgroup, logits workgroup, expert) triples, a prefix-scan kernel turns
+// the partial histograms into per-scatter-workgroup bases once, instead of every scatter workgroup summing all
+// partial histograms before its own (whose cost grows with T squared).
+constexpr long kScatterPrescanMin = 1L << 22;
 
 // Each returns hipSuccess or the launch error. Arguments are already validated.
 hipError_t launch_route(const void *X, rom_dtype dt, int T, int dm, const float *Wr, const float *bias, int E,

@@ -523,15 +523,14 @@ __global__ __launch_bounds__(256) void k_route_logits_mfma(const uint16_t *__res
 
 // Multi-workgroup path, kernel 2: per-expert totals and bases, then the stable scatter of 256 tokens
 // per workgroup (= sub logits workgroups).
-template <typename TX>
+// With `bases` (written by k_route_scan), each workgroup reads its own per-expert bases and the totals instead.
 __global__ __launch_bounds__(256) void k_route_scatter(const int32_t *__restrict__ ids, int T, int E,
                                                        const int32_t *__restrict__ wg_counts, int nwg, int sub,
+                                                       const int32_t *__restrict__ bases, int nsc,
                                                        int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-                                                       int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm,
-                                                       const TX *__restrict__ X, TX *__restrict__ Xp, int dm) {
+                                                       int32_t *__restrict__ perm, int32_t *__restrict__ inv_perm) {
     __shared__ int s_before[ROM_MAX_EXPERTS], s_total[ROM_MAX_EXPERTS], s_base[ROM_MAX_EXPERTS];
     __shared__ int s_wcnt[4][ROM_MAX_EXPERTS];
-    __shared__ int s_pos[kScatterTokensPerWG];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wg = blockIdx.x;
     // choice k = blockIdx.y: the k-th stacked top-1 routing
@@ -544,9 +543,18 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t *__restrict
     const int first = wg * sub;  // logits workgroups before this one contribute to the base
     const int t = wg * kScatterTokensPerWG + tid;
     const int te = t < T ? ids[t] : -1;  // this thread's token's expert, in flight with the partial histograms
+    if (bases != nullptr) {
+        // [K][E][nsc] bases before this workgroup, then the [K][E] totals
+        const int32_t *bk = bases + (size_t)blockIdx.y * E * nsc;
+        const int32_t *tk = bases + (size_t)gridDim.y * E * nsc + (size_t)blockIdx.y * E;
+        if (tid < E) {
+            s_before[tid] = bk[(size_t)tid * nsc + wg];
+            s_total[tid] = tk[tid];
+        }
+    }
     // wave w sums the partial histograms of experts w, w + 4, ..., two experts at a time with all of their
     // loads (4 per 256 logits workgroups each) in flight before the first add
-    for (int e0 = wave; e0 < E; e0 += 8) {
+    for (int e0 = bases != nullptr ? E : wave; e0 < E; e0 += 8) {
         const int e1 = e0 + 4;
         int b0 = 0, t0 = 0, b1 = 0, t1 = 0;
         auto chunk = [&](int w0) {
@@ -596,18 +604,77 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t *__restrict
     }
     __syncthreads();
     const int rank = wg_stable_rank(te, E, s_wcnt);
-    int pos = -1;
     if (te >= 0) {
-        pos = s_base[te] + rank;
+        const int pos = s_base[te] + rank;
         perm[pos] = t;
         inv_perm[t] = pos;
     }
-    if (Xp) {
-        s_pos[tid] = pos;
-        __syncthreads();
-        permute_rows<TX>(X, Xp, dm, wg * kScatterTokensPerWG, min(kScatterTokensPerWG, T - wg * kScatterTokensPerWG),
-                         s_pos);
+}
+
+// The materialised permute (top-1): X_perm[inv_perm[t]] = X[t], a streaming copy over the whole chip. A
+// workgroup owns perm_rows_per_wg(cpr) consecutive source rows (about 2048 16-byte chunks; cpr chunks per row)
+// and its threads stride over their chunks with kPermChunks loads in flight each, issued before the stores:
+// source rows are read in token order, destination rows are written whole. The row of chunk unit u is
+// umulhi(u, magic) with magic = floor(2^32 / cpr) + 1, exact for u < max(2048, cpr) and cpr < 2^16.
+constexpr int kPermChunks = 8;
+inline int perm_rows_per_wg(int cpr) { return cpr >= 2048 ? 1 : 2048 / cpr; }
+template <typename TX>
+__global__ __launch_bounds__(256) void k_permute_rows(const TX *__restrict__ X, const int32_t *__restrict__ inv_perm,
+                                                      int T, int cpr, int rows_per_wg, uint32_t magic,
+                                                      TX *__restrict__ Xp) {
+    const int r0 = blockIdx.x * rows_per_wg;
+    const int n = min(rows_per_wg, T - r0) * cpr;  // chunk units of this workgroup
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(X) + (size_t)r0 * cpr;
+    for (int ub = threadIdx.x; ub < n; ub += kPermChunks * 256) {
+        u32x4 v[kPermChunks];
+#pragma unroll
+        for (int j = 0; j < kPermChunks; ++j) v[j] = src[min(ub + j * 256, n - 1)];  // clamped: in bounds
+#pragma unroll
+        for (int j = 0; j < kPermChunks; ++j) {
+            const int u = ub + j * 256;
+            if (u < n) {
+                const int rr = (int)__umulhi((uint32_t)u, magic), c = u - rr * cpr;
+                __builtin_nontemporal_store(v[j], reinterpret_cast<u32x4 *>(Xp) + (size_t)inv_perm[r0 + rr] * cpr + c);
+            }
+        }
     }
+}
+
+// Prefix scan of the partial histograms (large T): workgroup (e, k) reads the nwg partial counts of expert e
+// in choice k once and writes, for every scatter workgroup s (= logits workgroups [s * sub, s * sub + sub)),
+// the tokens of expert e in the logits workgroups before s, and the expert's total. Groups of 256 scatter
+// workgroups are scanned in turn (a wave-level inclusive scan, then the four waves' sums through LDS), with
+// a running carry.
+__global__ __launch_bounds__(256) void k_route_scan(const int32_t *__restrict__ wg_counts, int nwg, int sub,
+                                                    int nsc, int32_t *__restrict__ bases) {
+    __shared__ int s_wsum[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = gridDim.x, e = blockIdx.x, k = blockIdx.y;
+    const int32_t *v = wg_counts + ((size_t)k * E + e) * nwg;
+    int32_t *out = bases + ((size_t)k * E + e) * nsc;
+    int carry = 0;
+    for (int c0 = 0; c0 < nsc; c0 += 256) {
+        const int s = c0 + tid;
+        int g = 0;
+        if (s < nsc) {
+            const int w1 = min(nwg, (s + 1) * sub);
+            for (int w = s * sub; w < w1; ++w) g += v[w];
+        }
+        int incl = g;  // inclusive scan within the wave
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int up = __shfl_up(incl, d);
+            if (lane >= d) incl += up;
+        }
+        if (lane == 63) s_wsum[wave] = incl;
+        __syncthreads();
+        int before = carry;
+        for (int w = 0; w < wave; ++w) before += s_wsum[w];
+        if (s < nsc) out[s] = before + incl - g;
+        carry += s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+        __syncthreads();
+    }
+    if (tid == 0) bases[(size_t)gridDim.y * E * nsc + (size_t)k * E + e] = carry;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -694,13 +761,9 @@ template <int NKS>
 static hipError_t launch_route_mfma_n(const uint16_t *X, int T, const float *Wr, const float *bias,
                                       const rom_routing &r, int32_t *wg_counts, int nwg, hipStream_t s) {
     const size_t smem = route_mfma_lds_bytes(NKS * 32);
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_route_logits_mfma<NKS>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (err != hipSuccess) return err;
-        attr_set = true;
-    }
+    static LdsAttrOnce attr;
+    hipError_t err = set_lds_limit_once(attr, reinterpret_cast<const void *>(&k_route_logits_mfma<NKS>), smem);
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL((k_route_logits_mfma<NKS>), dim3(nwg), dim3(256), smem, s, X, T, Wr, bias, r.top_k,
                        r.expert_id, r.prob, wg_counts, nwg);
     return hipGetLastError();
@@ -731,16 +794,13 @@ static hipError_t launch_route_t(const TX *X, int T, int dm, const float *Wr, co
     const bool wide = (T + 31) / 32 >= 512;
     const int use_lds = wide && (E % 4 == 0) && (((E >> 2) & ((E >> 2) - 1)) == 0) && wbytes <= (size_t)kRouteLdsW;
     const size_t smem = use_lds ? wbytes : 0;
-    static bool attr_set = false;
-    if (!attr_set) {
-        const void *fns[3] = {reinterpret_cast<const void *>(&k_route_logits<TX, EG, EMAX, 1>),
-                              reinterpret_cast<const void *>(&k_route_logits<TX, EG, EMAX, 4>),
-                              reinterpret_cast<const void *>(&k_route_small<TX, EG, EMAX>)};
-        for (const void *f : fns) {
-            hipError_t err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kRouteLdsW);
-            if (err != hipSuccess) return err;
-        }
-        attr_set = true;
+    static LdsAttrOnce attr[3];
+    const void *fns[3] = {reinterpret_cast<const void *>(&k_route_logits<TX, EG, EMAX, 1>),
+                          reinterpret_cast<const void *>(&k_route_logits<TX, EG, EMAX, 4>),
+                          reinterpret_cast<const void *>(&k_route_small<TX, EG, EMAX>)};
+    for (int f = 0; f < 3; ++f) {
+        hipError_t err = set_lds_limit_once(attr[f], fns[f], kRouteLdsW);
+        if (err != hipSuccess) return err;
     }
     if (T <= kRouteSmallT) {
         hipLaunchKernelGGL((k_route_small<TX, EG, EMAX>), dim3(1), dim3(256), smem, s, X, T, dm, Wr, bias, E, r.top_k,
@@ -765,9 +825,22 @@ static hipError_t launch_route_t(const TX *X, int T, int dm, const float *Wr, co
         err = hipGetLastError();
     }
     if (err != hipSuccess) return err;
-    const int nsc = (T + kScatterTokensPerWG - 1) / kScatterTokensPerWG;
-    hipLaunchKernelGGL((k_route_scatter<TX>), dim3(nsc, r.top_k), dim3(256), 0, s, r.expert_id, T, E, wg_counts, nwg,
-                       kScatterTokensPerWG / tpw, r.counts, r.offsets, r.perm, r.inv_perm, X, Xp, dm);
+    const int nsc = scatter_workgroups(T), sub = kScatterTokensPerWG / tpw;
+    int32_t *bases = nullptr;
+    if ((long)nsc * nwg * E > kScatterPrescanMin) {
+        bases = wg_counts + route_bases_offset(T, E);
+        hipLaunchKernelGGL(k_route_scan, dim3(E, r.top_k), dim3(256), 0, s, wg_counts, nwg, sub, nsc, bases);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(k_route_scatter, dim3(nsc, r.top_k), dim3(256), 0, s, r.expert_id, T, E, wg_counts, nwg,
+                       sub, bases, nsc, r.counts, r.offsets, r.perm, r.inv_perm);
+    err = hipGetLastError();
+    if (err != hipSuccess || Xp == nullptr) return err;
+    const int cpr = dm * (int)sizeof(TX) / 16, rpw = perm_rows_per_wg(cpr);
+    const uint32_t magic = (uint32_t)((1ull << 32) / (uint64_t)cpr + 1);
+    hipLaunchKernelGGL((k_permute_rows<TX>), dim3((unsigned)((T + rpw - 1) / rpw)), dim3(256), 0, s, X, r.inv_perm, T,
+                       cpr, rpw, magic, Xp);
     return hipGetLastError();
 }
 

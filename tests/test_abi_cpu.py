@@ -70,6 +70,7 @@ def _route(L, X=A, dt=BF16, T=512, dm=128, Wr=A, bias=None, E=8, k=1, r="default
     (dict(T=-1), INVALID), (dict(E=0), INVALID), (dict(E=65), UNSUPPORTED), (dict(k=3), UNSUPPORTED),
     (dict(k=2, E=1), INVALID), (dict(k=2, Xp=A + (1 << 24)), UNSUPPORTED),  # the permute is top-1 only
     (dict(k=0), INVALID), (dict(k=9), INVALID), (dict(dm=0), INVALID), (dict(dm=96), UNSUPPORTED),
+    (dict(dm=65536 + 64), UNSUPPORTED),
     (dict(dt=7), INVALID), (dict(X=None), INVALID), (dict(X=A + 8), INVALID), (dict(Wr=None), INVALID),
     (dict(r=None), INVALID), (dict(bias=A + 2), INVALID), (dict(ws=None), WS_SMALL), (dict(wsb=16), WS_SMALL),
     (dict(Xp=A + 4096), INVALID),  # overlaps X
@@ -232,3 +233,47 @@ def test_binding_has_no_cpu_path(L):
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         rom.lib(os.path.join(tmp_path, "librom.so"))
+
+
+# ---- the Python binding checks shapes and dtypes of everything the library reads or writes in full before it
+# checks devices (the C ABI receives only pointers): CPU tensors of the wrong shape raise a shape error here
+
+def _cpu(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", ["router_rows", "router_1d", "bias", "x_out", "z_out_dtype", "y_out", "out",
+                                  "conv_y", "conv_bias", "out_dtype"])
+def test_binding_rejects_wrong_shapes_before_any_device_call(L, case):
+    import torch
+    T, dm, di, E = 40, 128, 64, 4
+    X = _cpu(T, dm)
+    Wr = torch.zeros((dm, E), dtype=torch.float32)
+    r = rom.Routing(T, E, "cpu")
+    Wc = _cpu(E, di, dm)
+    Wo = _cpu(E, dm, di)
+    z = _cpu(T, di)
+    with pytest.raises(ValueError) as ei:
+        if case == "router_rows":
+            rom.route(X, torch.zeros((dm + 64, E), dtype=torch.float32))
+        elif case == "router_1d":
+            rom.route(X, torch.zeros((dm * E,), dtype=torch.float32))
+        elif case == "bias":
+            rom.route(X, Wr, torch.zeros((E + 1,), dtype=torch.float32))
+        elif case == "x_out":
+            rom.in_proj(X, r, Wc, Wc, x_out=_cpu(T, di + 64))
+        elif case == "z_out_dtype":
+            rom.in_proj(X, r, Wc, Wc, z_out=_cpu(T, di, dtype=torch.float32))
+        elif case == "y_out":
+            rom.in_proj_weighted(X, r, Wc, y_out=_cpu(T - 1, di))
+        elif case == "out":
+            rom.out_proj(z, z, r, Wo, out=_cpu(T, dm - 64))
+        elif case == "out_dtype":
+            rom.out_proj(z, z, r, Wo, out=_cpu(T, dm, dtype=torch.float32))
+        elif case == "conv_y":
+            rom.conv1d(z, _cpu(di, 4), y=_cpu(T, di + 64))
+        elif case == "conv_bias":
+            rom.conv1d(z, _cpu(di, 4), _cpu(di + 1))
+    msg = str(ei.value)
+    assert "ROCm device" not in msg, msg  # the shape check came first

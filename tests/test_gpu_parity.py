@@ -52,32 +52,48 @@ def _rows(t, rows):
     return parity.to_host(t.index_select(0, idx))
 
 
+def _prob_rtol(inp, o_route):
+    """Per-token fp32 bound on the router probability's relative error (both sides compute in fp32)."""
+    return parity.router_prob_rtol(inp["X"], inp["W_router"], inp.get("bias"), o_route["logits"])
+
+
+def _fwd_tiles(w, top_k=1):
+    """Row tiles of the in-projection (Conv + Gate stacks) and out-projection GEMMs the library launches."""
+    return [parity.gemm_row_tiles(w.T, w.d_inner, 2, w.E, w.dtype), parity.gemm_row_tiles(w.T, w.d_model, 1, w.E, w.dtype)]
+
+
+def _choice_sorts(orc, ids, E):
+    """The oracle's grouping of every routing choice (column k of ids [T][K])."""
+    return [orc.sort(np.ascontiguousarray(ids[:, k:k + 1]), E) for k in range(ids.shape[1])]
+
+
 def check_workload(rom, orc, w, inp=None, rows=None, label=""):
     """Full comparison of one workload; rows=None compares every token."""
     inp = inp if inp is not None else workloads.make_inputs(w)
     tol = parity.TOL[w.dtype]
     print(f"[parity] {label or w.name}: T={w.T} d_model={w.d_model} d_inner={w.d_inner} E={w.E} {w.dtype}",
           flush=True)
+    parity.begin(label or w.name)
     g = _run_chain(rom, w, inp)
     gr = _route_host(g["r"])
-    o_route = orc.route(inp["X"], inp["W_router"], inp.get("bias"))
+    o_route = orc.route(inp["X"], inp["W_router"], inp.get("bias"), want_logits=True)
     o_sort = orc.sort(o_route["ids"], w.E)
-    rep = parity.check_route(gr, o_route, o_sort, w.T, w.E, tol)
+    rep = parity.check_route(gr, o_route, o_sort, w.T, w.E, _prob_rtol(inp, o_route))
     if rows is None:
         rows = np.arange(w.T)
     ids_o = o_route["ids"][:, 0]
     agree = gr["expert_id"][rows] == ids_o[rows]
     rows = rows[agree]
     x_o, z_o = orc.in_proj(inp["X"][rows], o_route["ids"][rows], inp["W_conv"], inp["W_gate"])
-    ex = parity.norm_max_err(_rows(g["x"], rows), x_o)
-    ez = parity.norm_max_err(_rows(g["z"], rows), z_o)
+    ex = parity.norm_max_err(_rows(g["x"], rows), x_o, "x")
+    ez = parity.norm_max_err(_rows(g["z"], rows), z_o, "z")
     out_o = orc.out_proj(z_o, inp["h"][rows], o_route["ids"][rows], o_route["prob"][rows], inp["W_out"])
-    eo = parity.norm_max_err(_rows(g["out"], rows), out_o)
+    eo = parity.norm_max_err(_rows(g["out"], rows), out_o, "out")
     ei = 0.0
     if g["out_iso"] is not None:
         out_i = orc.out_proj(inp["z"][rows].astype(np.float64), inp["h"][rows], o_route["ids"][rows],
                              o_route["prob"][rows], inp["W_out"])
-        ei = parity.norm_max_err(_rows(g["out_iso"], rows), out_i)
+        ei = parity.norm_max_err(_rows(g["out_iso"], rows), out_i, "out_isolated")
     print(f"[parity]   excluded(gap<1e-4)={rep.n_excluded} id-mismatch={rep.n_id_mismatch_excluded} "
           f"prob={rep.prob_err:.2e} x={ex:.2e} z={ez:.2e} out={eo:.2e} out_isolated={ei:.2e} rows={len(rows)}",
           flush=True)
@@ -112,6 +128,14 @@ SMALL = [
     # wide router with W_r in LDS and fp32 rows: 144 chunks per row, so every lane has a second chunk in
     # flight at the barrier and some refill a third time
     workloads.custom_workload("f32_wide_route_dm1152", T=16400, d_model=1152, d_inner=128, E=8, dtype="f32", seed=117),
+    # 320-row tiles with 160-row epilogue passes (the tile of every full-size workload), every token: few experts
+    # keep the padding of 320-row tiles within 5% of 256-row ones at T = 4096; a ragged last tile
+    workloads.custom_workload("bf16_tiles320_T4096_E2", T=4096, d_model=256, d_inner=256, E=2, seed=130),
+    workloads.custom_workload("bf16_tiles320_T4100_E3", T=4100, d_model=512, d_inner=256, E=3, seed=131),
+    # many router workgroups: the scatter reads per-workgroup bases from the prefix-scan kernel (8-token router
+    # workgroups with 64 experts; 32-token workgroups at 300K tokens) instead of summing the partial histograms
+    workloads.custom_workload("bf16_E64_T12000_prescan", T=12000, d_model=128, d_inner=64, E=64, seed=132),
+    workloads.custom_workload("bf16_T300000_prescan", T=300000, d_model=64, d_inner=64, E=8, seed=133),
     workloads.custom_workload("f32_E5", T=333, d_model=128, d_inner=192, E=5, dtype="f32", seed=111),
     workloads.custom_workload("f32_T1000_E8", T=1000, d_model=64, d_inner=128, E=8, dtype="f32", seed=112),
 ]
@@ -119,6 +143,8 @@ SMALL = [
 
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
 def test_small_shapes(rom, oracle, w):
+    if "tiles320" in w.name:
+        assert all(t[0] == 320 for t in _fwd_tiles(w)), "the case no longer selects 320-row tiles"
     check_workload(rom, oracle, w)
 
 
@@ -221,7 +247,7 @@ def test_full_workload(rom, oracle, name):
                                 if w.T <= 64 else {"X", "W_router", "W_conv", "W_gate", "W_out", "h"})
     o_route = oracle.route(inp["X"], inp["W_router"], inp.get("bias"))
     o_sort = oracle.sort(o_route["ids"], w.E)
-    rows = parity.sample_rows(o_sort, w.T) if w.T > 64 else None
+    rows = parity.sample_rows(o_sort, w.T, tiles=_fwd_tiles(w)) if w.T > 64 else None
     _, gr, _, _ = check_workload(rom, oracle, w, inp, rows=rows)
     if w.skew is not None:
         frac = gr["counts"] / w.T
@@ -237,22 +263,23 @@ def check_workload_top2(rom, orc, w, inp=None, rows=None, label=""):
     tol = parity.TOL[w.dtype]
     print(f"[parity top2] {label or w.name}: T={w.T} d_model={w.d_model} d_inner={w.d_inner} E={w.E} {w.dtype}",
           flush=True)
+    parity.begin((label or w.name) + " top-2")
     g = _run_chain(rom, w, inp, top_k=K)
     gr = _route_host(g["r"], squeeze=False)
     o_route = orc.route(inp["X"], inp["W_router"], inp.get("bias"), top_k=K, want_logits=True)
-    agree = parity.check_route_topk(gr, o_route, w.T, w.E, K, tol)
+    agree = parity.check_route_topk(gr, o_route, w.T, w.E, K, _prob_rtol(inp, o_route))
     rows = np.arange(w.T) if rows is None else rows
     rows = rows[agree[rows]]
     ids_o, prob_o = o_route["ids"][rows], o_route["prob"][rows]
     x_o, z_o = orc.in_proj(inp["X"][rows], ids_o, inp["W_conv"], inp["W_gate"])
-    ex = parity.norm_max_err(_rows(g["x"], rows), x_o)
-    ez = parity.norm_max_err(_rows(g["z"], rows), z_o)
+    ex = parity.norm_max_err(_rows(g["x"], rows), x_o, "x")
+    ez = parity.norm_max_err(_rows(g["z"], rows), z_o, "z")
     out_o = orc.out_proj(z_o, inp["h"][rows], ids_o, prob_o, inp["W_out"])
-    eo = parity.norm_max_err(_rows(g["out"], rows), out_o)
+    eo = parity.norm_max_err(_rows(g["out"], rows), out_o, "out")
     ei = 0.0
     if g["out_iso"] is not None:
         out_i = orc.out_proj(inp["z"][rows].astype(np.float64), inp["h"][rows], ids_o, prob_o, inp["W_out"])
-        ei = parity.norm_max_err(_rows(g["out_iso"], rows), out_i)
+        ei = parity.norm_max_err(_rows(g["out_iso"], rows), out_i, "out_isolated")
     print(f"[parity top2]   set-mismatch={int((~agree).sum())} x={ex:.2e} z={ez:.2e} out={eo:.2e} "
           f"out_isolated={ei:.2e} rows={len(rows)}", flush=True)
     for name, err in (("x", ex), ("z", ez), ("out", eo), ("out_isolated", ei)):
@@ -272,6 +299,9 @@ TOP2 = [
     workloads.custom_workload("top2_wide_mfma_dm1024", T=16400, d_model=1024, d_inner=128, E=8, seed=211),
     # 256-row early-barrier tiles (their padding rules out 320 rows here) with the fp32 accumulate epilogue
     workloads.custom_workload("top2_T4096_tiles256", T=4096, d_model=512, d_inner=512, E=8, seed=210),
+    # 320-row tiles (two 160-row passes of the fp32 accumulate epilogue for the second choice), every token
+    workloads.custom_workload("top2_tiles320_T4096_E2", T=4096, d_model=256, d_inner=256, E=2, seed=212),
+    workloads.custom_workload("top2_tiles320_T4100_E3", T=4100, d_model=512, d_inner=256, E=3, seed=213),
 ]
 
 
@@ -320,7 +350,7 @@ def test_top2_full_samba_shape(rom, oracle):
     w = workloads.get_workload("samba421m")
     inp = workloads.make_inputs(w, which={"X", "W_router", "W_conv", "W_gate", "W_out", "h"})
     o_route = oracle.route(inp["X"], inp["W_router"], top_k=2)
-    rows = parity.sample_rows(oracle.sort(o_route["ids"][:, :1].copy(), w.E), w.T)
+    rows = parity.sample_rows(_choice_sorts(oracle, o_route["ids"], w.E), w.T, tiles=_fwd_tiles(w))
     check_workload_top2(rom, oracle, w, inp, rows=rows, label="samba421m top-2")
 
 
@@ -337,16 +367,17 @@ def check_weighted(rom, orc, w, top_k=1, inp=None, rows=None, label=""):
     Wr = parity.to_device(inp["W_router"], "f32")
     W = parity.to_device(inp["W_in"], w.dtype)
     bias = parity.to_device(inp["bias"], "f32") if inp.get("bias") is not None else None
+    parity.begin((label or w.name) + " weighted")
     r = rom.route(X, Wr, bias, top_k=top_k)
     y = rom.in_proj_weighted(X, r, W)
     torch.cuda.synchronize()
     gr = _route_host(r, squeeze=False)
     o_route = orc.route(inp["X"], inp["W_router"], inp.get("bias"), top_k=top_k, want_logits=True)
-    agree = parity.check_route_topk(gr, o_route, w.T, w.E, top_k, tol)
+    agree = parity.check_route_topk(gr, o_route, w.T, w.E, top_k, _prob_rtol(inp, o_route))
     rows = np.arange(w.T) if rows is None else rows
     rows = rows[agree[rows]]
     y_o = orc.in_proj_weighted(inp["X"][rows], o_route["ids"][rows], o_route["prob"][rows], inp["W_in"])
-    ey = parity.norm_max_err(_rows(y, rows), y_o)
+    ey = parity.norm_max_err(_rows(y, rows), y_o, "y")
     print(f"[parity weighted]   set-mismatch={int((~agree).sum())} y={ey:.2e} rows={len(rows)}", flush=True)
     assert ey <= tol, f"y: normalised max error {ey:.3g} > {tol}"
     return gr
@@ -363,6 +394,8 @@ WEIGHTED = [
     (workloads.custom_workload("w_T5", T=5, d_model=512, d_inner=128, E=4, seed=308), 1),
     (workloads.custom_workload("w_T40", T=40, d_model=256, d_inner=160, E=4, seed=309), 1),
     (workloads.custom_workload("w_T64_top2", T=64, d_model=512, d_inner=256, E=4, seed=310), 2),
+    (workloads.custom_workload("w_tiles320_T4096_E2", T=4096, d_model=256, d_inner=128, E=2, seed=311), 1),
+    (workloads.custom_workload("w_tiles320_top2_T4100_E3", T=4100, d_model=256, d_inner=256, E=3, seed=313), 2),
 ]
 
 
@@ -388,7 +421,8 @@ def test_weighted_in_proj_prefill_shape(rom, oracle):
     w = workloads.custom_workload("w_prefill", T=16384, d_model=1024, d_inner=2048, E=4, seed=312)
     inp = workloads.make_inputs(w, which={"X", "W_router", "W_in"})
     o_route = oracle.route(inp["X"], inp["W_router"])
-    rows = parity.sample_rows(oracle.sort(o_route["ids"], w.E), w.T)
+    rows = parity.sample_rows(oracle.sort(o_route["ids"], w.E), w.T,
+                              tiles=[parity.gemm_row_tiles(w.T, w.dout, 1, w.E, w.dtype)])
     check_weighted(rom, oracle, w, inp=inp, rows=rows)
 
 
@@ -422,7 +456,8 @@ def test_conv1d(rom, oracle, case):
     y = rom.conv1d(x, W, b, n_seq=ns, activation=act)
     torch.cuda.synchronize()
     ref = oracle.conv1d(inp["x"], inp["weight"], inp["bias"], activation=act).reshape(ns * L, C)
-    err = parity.norm_max_err(parity.to_host(y), ref)
+    parity.begin(f"conv1d ns{ns} L{L} C{C} w{w} {dt}")
+    err = parity.norm_max_err(parity.to_host(y), ref, "y")
     print(f"[parity conv1d]   y={err:.2e}", flush=True)
     assert err <= parity.TOL[dt], f"conv1d: normalised max error {err:.3g}"
 
@@ -449,13 +484,14 @@ def check_backward(rom, orc, w, top_k=1, inp=None, rows=None, n_entries=None, la
     g, dx, dzu = d(gr_in["d_out"]), d(gr_in["dx"]), d(gr_in["dz"])
     Wr = parity.to_device(inp["W_router"], "f32")
     bias = parity.to_device(inp["bias"], "f32") if inp.get("bias") is not None else None
+    parity.begin((label or w.name) + f" backward top-{top_k}")
     r = rom.route(X, Wr, bias, top_k=top_k)
     dz, dh, dWo = rom.out_proj_backward(g, z, h, r, Wo)
     dX, dWc, dWg = rom.in_proj_backward(X, dx, dzu, r, Wc, Wg)
     torch.cuda.synchronize()
     gr = _route_host(r, squeeze=False)
     o_route = orc.route(inp["X"], inp["W_router"], inp.get("bias"), top_k=top_k, want_logits=True)
-    agree = parity.check_route_topk(gr, o_route, w.T, w.E, top_k, tol)
+    agree = parity.check_route_topk(gr, o_route, w.T, w.E, top_k, _prob_rtol(inp, o_route))
     ids_o, prob_o = o_route["ids"], o_route["prob"]
     # weight gradients sum over all tokens: compare only experts untouched by a token whose expert set differs
     bad = set(np.unique(ids_o[~agree]).tolist()) | set(np.unique(gr["expert_id"][:, ~agree]).tolist())
@@ -466,15 +502,16 @@ def check_backward(rom, orc, w, top_k=1, inp=None, rows=None, n_entries=None, la
     dz_o, dh_o = orc.out_proj_dgrad(gr_in["d_out"][rows], zf[rows], inp["h"][rows], ids_o[rows], prob_o[rows],
                                     inp["W_out"])
     dX_o = orc.in_proj_dgrad(gr_in["dx"][rows], gr_in["dz"][rows], ids_o[rows], inp["W_conv"], inp["W_gate"])
-    errs = {"dz": parity.norm_max_err(_rows(dz, rows), dz_o), "dh": parity.norm_max_err(_rows(dh, rows), dh_o),
-            "dX": parity.norm_max_err(_rows(dX, rows), dX_o)}
+    errs = {"dz": parity.norm_max_err(_rows(dz, rows), dz_o, "dz"),
+            "dh": parity.norm_max_err(_rows(dh, rows), dh_o, "dh"),
+            "dX": parity.norm_max_err(_rows(dX, rows), dX_o, "dX")}
     keep_e = np.array([e for e in range(w.E) if e not in bad], dtype=np.int64)
     if full:
         dWo_o = orc.out_proj_wgrad(gr_in["d_out"], zf, inp["h"], ids_o, prob_o, w.E)
         dWc_o, dWg_o = orc.in_proj_wgrad(inp["X"], gr_in["dx"], gr_in["dz"], ids_o, w.E)
-        errs["dW_out"] = parity.norm_max_err(parity.to_host(dWo)[keep_e], dWo_o[keep_e])
-        errs["dW_conv"] = parity.norm_max_err(parity.to_host(dWc)[keep_e], dWc_o[keep_e])
-        errs["dW_gate"] = parity.norm_max_err(parity.to_host(dWg)[keep_e], dWg_o[keep_e])
+        errs["dW_out"] = parity.norm_max_err(parity.to_host(dWo)[keep_e], dWo_o[keep_e], "dW_out")
+        errs["dW_conv"] = parity.norm_max_err(parity.to_host(dWc)[keep_e], dWc_o[keep_e], "dW_conv")
+        errs["dW_gate"] = parity.norm_max_err(parity.to_host(dWg)[keep_e], dWg_o[keep_e], "dW_gate")
         # an expert that received no token has an exactly zero gradient
         used = np.unique(ids_o)
         for e in range(w.E):
@@ -509,6 +546,8 @@ BWD = [
     (workloads.custom_workload("bwd_top2_T64", T=64, d_model=256, d_inner=256, E=4, seed=506), 2),
     (workloads.custom_workload("bwd_top2_E16", T=2000, d_model=320, d_inner=192, E=16, seed=507), 2),
     (workloads.custom_workload("bwd_T4096_tiles256", T=4096, d_model=512, d_inner=512, E=8, seed=508), 1),
+    (workloads.custom_workload("bwd_T4096_tiles320", T=4096, d_model=256, d_inner=256, E=2, seed=510), 1),
+    (workloads.custom_workload("bwd_top2_T4100_tiles320", T=4100, d_model=512, d_inner=256, E=3, seed=511), 2),
 ]
 
 
@@ -530,5 +569,7 @@ def test_backward_full_samba_shape(rom, oracle, top_k):
     w = workloads.get_workload("samba421m")
     inp = workloads.make_inputs(w)
     o_route = oracle.route(inp["X"], inp["W_router"], top_k=top_k)
-    rows = parity.sample_rows(oracle.sort(o_route["ids"][:, :1].copy(), w.E), w.T, n_random=96)
+    # data-gradient GEMMs: d(gated rows) over d_inner columns, dX over d_model columns
+    tiles = [parity.gemm_row_tiles(w.T, w.d_inner, 1, w.E, w.dtype), parity.gemm_row_tiles(w.T, w.d_model, 1, w.E, w.dtype)]
+    rows = parity.sample_rows(_choice_sorts(oracle, o_route["ids"], w.E), w.T, tiles=tiles, n_random=96)
     check_backward(rom, oracle, w, top_k=top_k, inp=inp, rows=rows, n_entries=600, label=f"samba421m top-{top_k}")
