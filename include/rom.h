@@ -15,7 +15,8 @@
  * Conventions for every entry point
  *  - Pointers named in a signature are DEVICE pointers unless marked "host". The caller owns every
  *    buffer; the library allocates nothing and keeps no state apart from per-device caches (device
- *    properties, kernel attributes), each filled once per device, thread-safely. Tensors are dense, row-major, and 16-byte aligned.
+ *    properties, kernel attributes, the scratch address of rom_route_noalloc), each filled once per device,
+ *    thread-safely. Tensors are dense, row-major, and 16-byte aligned.
  *  - Calls enqueue kernels on `stream` (a hipStream_t; NULL is the null stream) and return without
  *    synchronising. The projections read what rom_route wrote: run them on the same stream, or
  *    order them after it. No count is ever read back to the host.
@@ -40,7 +41,7 @@
 extern "C" {
 #endif
 
-#define ROM_ABI_VERSION 7
+#define ROM_ABI_VERSION 8
 #ifndef ROM_API
 #define ROM_API __attribute__((visibility("default")))
 #endif
@@ -49,6 +50,7 @@ extern "C" {
 #define ROM_MAX_TOKENS (1 << 24)
 #define ROM_MAX_DIM 65536     /* largest d_model, d_inner, d_out or channel count */
 #define ROM_MAX_CONV_WIDTH 8
+#define ROM_NOALLOC_SCRATCH_BYTES (4u << 20)  /* static router scratch of rom_route_noalloc, per device */
 
 typedef enum {
     ROM_OK = 0,
@@ -110,6 +112,21 @@ ROM_API rom_status rom_route(const void *X, rom_dtype x_dtype, int32_t T, int32_
                      const float *W_router, const float *bias, int32_t E, int32_t top_k,
                      rom_routing *routing, void *X_perm, void *workspace, size_t workspace_bytes,
                      void *stream);
+
+/*
+ * rom_route for callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same arguments, kernels and results (bit for bit) as rom_route,
+ * without the workspace: the router's partial histograms live in a static device array of
+ * ROM_NOALLOC_SCRATCH_BYTES that the library owns (each GPU the library runs on holds its own copy until the
+ * process ends). The call allocates nothing. It returns ROM_ERR_UNSUPPORTED when
+ * rom_route_workspace_bytes(T, E) exceeds ROM_NOALLOC_SCRATCH_BYTES (e.g. E = 8 beyond about 500K tokens).
+ * Every call on one GPU shares that GPU's array and nothing in it needs to start at zero: calls that overlap
+ * in time on one GPU (on different streams, or from host threads without ordering between them) race on it
+ * and give undefined results, so order them (one stream, or events).
+ */
+ROM_API rom_status rom_route_noalloc(const void *X, rom_dtype x_dtype, int32_t T, int32_t d_model,
+                             const float *W_router, const float *bias, int32_t E, int32_t top_k,
+                             rom_routing *routing, void *X_perm, void *stream);
 
 /*
  * In-projection experts (Knowl 1, H_t and the argument of SiLU in G_t): for every token t,

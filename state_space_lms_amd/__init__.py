@@ -22,17 +22,17 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["route", "in_proj", "in_proj_weighted", "out_proj", "conv1d", "out_proj_backward", "in_proj_backward",
+__all__ = ["route", "route_noalloc", "in_proj", "in_proj_weighted", "out_proj", "conv1d", "out_proj_backward", "in_proj_backward",
            "backward_workspace_bytes", "Routing", "RomError", "lib", "LIB_PATH", "ABI_VERSION",
            "route_workspace_bytes", "out_proj_workspace_bytes"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "librom.so")
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 ROM_OK, ROM_ERR_INVALID_ARGUMENT, ROM_ERR_UNSUPPORTED, ROM_ERR_WORKSPACE_TOO_SMALL, ROM_ERR_HIP = range(5)
 ROM_DTYPE_F32, ROM_DTYPE_BF16 = 0, 1
 ROM_ACT_NONE, ROM_ACT_SILU = 0, 1
-ABI_SYMBOLS = ("rom_abi_version", "rom_route_workspace_bytes", "rom_route", "rom_in_proj", "rom_in_proj_weighted", "rom_conv1d",
+ABI_SYMBOLS = ("rom_abi_version", "rom_route_workspace_bytes", "rom_route", "rom_route_noalloc", "rom_in_proj", "rom_in_proj_weighted", "rom_conv1d",
                "rom_backward_workspace_bytes", "rom_out_proj_backward", "rom_in_proj_backward",
                "rom_out_proj_workspace_bytes", "rom_out_proj", "rom_status_string", "rom_last_error")
 
@@ -68,6 +68,9 @@ def lib(path: str = LIB_PATH) -> ctypes.CDLL:
     L.rom_route.argtypes = [_vp, ctypes.c_int, _i32, _i32, _vp, _vp, _i32, _i32, ctypes.POINTER(RoutingStruct),
                             _vp, _vp, _sz, _vp]
     L.rom_route.restype = ctypes.c_int
+    L.rom_route_noalloc.argtypes = [_vp, ctypes.c_int, _i32, _i32, _vp, _vp, _i32, _i32,
+                                    ctypes.POINTER(RoutingStruct), _vp, _vp]
+    L.rom_route_noalloc.restype = ctypes.c_int
     L.rom_in_proj.argtypes = [_vp, ctypes.POINTER(RoutingStruct), ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                               _vp]
     L.rom_in_proj.restype = ctypes.c_int
@@ -206,6 +209,35 @@ def route(X: torch.Tensor, W_router: torch.Tensor, bias: Optional[torch.Tensor] 
                              r.workspace.numel(), _stream(X.device, stream))
     _check(status, "rom_route")
     return r
+
+
+def route_noalloc(X: torch.Tensor, W_router: torch.Tensor, routing: Routing, bias: Optional[torch.Tensor] = None,
+                  permute: bool = False, stream=None) -> Routing:
+    """rom_route_noalloc: rom_route with the library's static scratch instead of a workspace (for callers
+    that cannot allocate). The routing buffers (and X_perm, with permute) must already exist: this call
+    allocates nothing."""
+    T, dm = _matrix(X, "X")
+    _dtype_code(X)
+    if W_router.dtype != torch.float32 or W_router.dim() != 2 or W_router.shape[0] != dm:
+        raise ValueError(f"W_router must be fp32 [d_model = {dm}][E], got {W_router.dtype} {tuple(W_router.shape)}")
+    E = W_router.shape[1]
+    if (routing.T, routing.E) != (T, E):
+        raise ValueError("routing buffers were sized for another T or E")
+    if bias is not None:
+        _want(bias, (E,), torch.float32, "bias")
+        _dev(bias, "bias")
+    if permute:
+        if routing.x_perm is None:
+            raise ValueError("permute needs routing.x_perm allocated beforehand")
+        _want(routing.x_perm, (T, dm), X.dtype, "routing.x_perm")
+    _dev(X, "X")
+    _dev(W_router, "W_router")
+    _same_device(routing, X)
+    status = lib().rom_route_noalloc(_ptr(X), _dtype_code(X), T, dm, _ptr(W_router), _ptr(bias), E, routing.top_k,
+                                     ctypes.byref(routing.struct), _ptr(routing.x_perm) if permute else None,
+                                     _stream(X.device, stream))
+    _check(status, "rom_route_noalloc")
+    return routing
 
 
 def in_proj(X: torch.Tensor, routing: Routing, W_conv: torch.Tensor, W_gate: torch.Tensor,

@@ -111,7 +111,7 @@ size_t rom_route_workspace_bytes(int32_t T, int32_t E) {
 
 namespace {
 
-// Argument validation of rom_route (workspace checks excluded).
+// Validation shared by rom_route and rom_route_noalloc (workspace checks excluded).
 rom_status check_route_args(const void *X, rom_dtype x_dtype, int32_t T, int32_t d_model, const float *W_router,
                             const float *bias, int32_t E, int32_t top_k, rom_routing *routing, void *X_perm) {
     rom_status s;
@@ -153,7 +153,61 @@ rom_status route_enqueue(const void *X, rom_dtype x_dtype, int32_t T, int32_t d_
 
 }  // namespace
 
+// ---- the scratch of rom_route_noalloc: a library-owned static device array (each device that loads the
+// library holds its own copy until the process ends). Host code never uses the array's name as an address:
+// its device address is taken once per device with hipGetSymbolAddress, with that device current.
+static __device__ __align__(256) int32_t scratch[ROM_NOALLOC_SCRATCH_BYTES / sizeof(int32_t)];
+
+namespace {
+
+std::once_flag g_scratch_once[rom::kMaxDevices];
+int32_t *g_scratch_ptr[rom::kMaxDevices];
+hipError_t g_scratch_err[rom::kMaxDevices];
+
+// Device address of the current device's scratch array.
+hipError_t scratch_address(int32_t **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= rom::kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [&] {
+        void *p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = static_cast<int32_t *>(p);
+    });
+    if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+    if (g_scratch_ptr[dev] == nullptr) return hipErrorInvalidSymbol;
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
 extern "C" {
+
+rom_status rom_route_noalloc(const void *X, rom_dtype x_dtype, int32_t T, int32_t d_model, const float *W_router,
+                             const float *bias, int32_t E, int32_t top_k, rom_routing *routing, void *X_perm,
+                             void *stream) {
+    g_last_error[0] = '\0';
+    rom_status s = check_route_args(X, x_dtype, T, d_model, W_router, bias, E, top_k, routing, X_perm);
+    if (s != ROM_OK) return s;
+    if (T == 0) {
+        routing->T = 0;
+        routing->E = E;
+        routing->top_k = top_k;
+        return ROM_OK;
+    }
+    const size_t need = rom_route_workspace_bytes(T, E);
+    if (need > ROM_NOALLOC_SCRATCH_BYTES)
+        return fail(ROM_ERR_UNSUPPORTED, "T = %d, E = %d need %zu bytes of router scratch; the static scratch of "
+                    "rom_route_noalloc holds %zu (use rom_route with a workspace)", T, E, need,
+                    (size_t)ROM_NOALLOC_SCRATCH_BYTES);
+    int32_t *ws = nullptr;
+    hipError_t err = scratch_address(&ws);
+    if (err != hipSuccess) return hip_fail(err, "rom_route_noalloc scratch address");
+    return route_enqueue(X, x_dtype, T, d_model, W_router, bias, E, top_k, routing, X_perm, ws, stream,
+                         "rom_route_noalloc launch");
+}
 
 rom_status rom_route(const void *X, rom_dtype x_dtype, int32_t T, int32_t d_model, const float *W_router,
                      const float *bias, int32_t E, int32_t top_k, rom_routing *routing, void *X_perm,
