@@ -293,13 +293,22 @@ def main() -> int:
         breakdown_pass()
     else:
         # cold cache: the eviction runs between steps and stays outside the timed sum, which adds up the
-        # GPU time of each step (event before the router to event after the last phase)
-        breakdown_pass()
-        elapsed = sum(e[0].elapsed_time(e[-1]) for e in events) * 1e-3
+        # GPU time of each step between two events (none inside the step); the per-phase breakdown comes
+        # from a second pass with an event between phases
+        bounds = [new_ev(2) for _ in range(args.steps)]
+        for k in range(args.steps):
+            flush.sum()
+            bounds[k][0].record(stream)
+            step()
+            bounds[k][1].record(stream)
+        torch.cuda.synchronize()
+        t_step_timed = np.array([b[0].elapsed_time(b[1]) for b in bounds]) * 1e-3
+        elapsed = float(t_step_timed.sum())
         t_in_timed = None
+        breakdown_pass()
 
     t_ph = {ph: np.array([e[i].elapsed_time(e[i + 1]) for e in events]) * 1e-3 for i, ph in enumerate(phases)}
-    t_step = np.array([e[0].elapsed_time(e[-1]) for e in events]) * 1e-3
+    t_step = t_step_timed if flush is not None else np.array([e[0].elapsed_time(e[-1]) for e in events]) * 1e-3
     t_route, t_in = t_ph["route"], (t_in_timed if t_in_timed is not None else t_ph["in"])
     t_out = t_ph.get("out", np.zeros(1))
     # the in-projection's output width: Conv + Gate (2 * d_inner) for RoM, d_out for Swimba

@@ -781,13 +781,20 @@ __device__ __forceinline__ void gemv_block(const GemmArgs &p, int e, int o0, int
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[j][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    // U K-steps of loads in flight per wave (indices clamped, so every load is in bounds), then their MFMAs
+    // U K-steps of loads in flight per wave (indices clamped, so every load is in bounds), then their MFMAs.
+    // With 8 waves each wave streams a contiguous K range (U consecutive steps: 32 U contiguous elements of
+    // each row per batch); with 16 waves the steps are interleaved (the 16 waves' loads of one batch cover
+    // 16 consecutive steps), which measured faster for the one-workgroup-per-CU launch.
+    constexpr bool CONTIG = NW == 8;
     const int nsteps = K / 32;
-    for (int s0 = wave; s0 < nsteps; s0 += NW * U) {
+    const int spw = CONTIG ? (nsteps + NW - 1) / NW : 0;
+    const int sbeg = CONTIG ? wave * spw : wave, send = CONTIG ? min(nsteps, sbeg + spw) : nsteps;
+    constexpr int SU = CONTIG ? 1 : NW;  // step stride within a batch
+    for (int s0 = sbeg; s0 < send; s0 += SU * U) {
         bf16x8 wf[U][RB], xf[U][NB];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int k0 = min(s0 + u * NW, nsteps - 1) * 32;
+            const int k0 = min(s0 + u * SU, send - 1) * 32;
 #pragma unroll
             for (int j = 0; j < RB; ++j) wf[u][j] = *reinterpret_cast<const bf16x8 *>(wp[j] + k0);
 #pragma unroll
@@ -795,7 +802,7 @@ __device__ __forceinline__ void gemv_block(const GemmArgs &p, int e, int o0, int
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (s0 + u * NW < nsteps) {  // uniform
+            if (s0 + u * SU < send) {  // uniform
 #pragma unroll
                 for (int j = 0; j < RB; ++j)
 #pragma unroll
@@ -826,7 +833,9 @@ __device__ __forceinline__ void gemv_block(const GemmArgs &p, int e, int o0, int
     }
 }
 
-template <int NW, int RB, bool OUT>
+// NBMAX: the most token blocks any expert can hold (T <= 16 NBMAX), so that small T instantiates only the
+// small variants and keeps fewer registers.
+template <int NW, int RB, int NBMAX, bool OUT>
 __global__ __launch_bounds__(64 * NW) void k_grouped_gemv_bf16(GemmArgs p) {
     __shared__ float s_red[NW][RB * 4][16][16];
     const int rb = blockIdx.x % p.n_tiles, rank = blockIdx.x / p.n_tiles;
@@ -839,12 +848,11 @@ __global__ __launch_bounds__(64 * NW) void k_grouped_gemv_bf16(GemmArgs p) {
         }
     }
     if (e < 0) return;
-    switch ((ne + 15) >> 4) {  // token blocks of this expert (1..4), uniform per workgroup
-        case 1: gemv_block<NW, RB, 1, 8, OUT>(p, e, o0, ne, rb, s_red); break;
-        case 2: gemv_block<NW, RB, 2, 4, OUT>(p, e, o0, ne, rb, s_red); break;
-        case 3: gemv_block<NW, RB, 3, 4, OUT>(p, e, o0, ne, rb, s_red); break;
-        default: gemv_block<NW, RB, 4, 4, OUT>(p, e, o0, ne, rb, s_red); break;
-    }
+    const int nb = (ne + 15) >> 4;  // token blocks of this expert (1..NBMAX), uniform per workgroup
+    if (NBMAX == 1 || nb == 1) gemv_block<NW, RB, 1, 8, OUT>(p, e, o0, ne, rb, s_red);
+    else if (NBMAX == 2 || nb == 2) gemv_block<NW, RB, 2, 4, OUT>(p, e, o0, ne, rb, s_red);
+    else if (nb == 3) gemv_block<NW, RB, 3, 4, OUT>(p, e, o0, ne, rb, s_red);
+    else gemv_block<NW, RB, 4, 4, OUT>(p, e, o0, ne, rb, s_red);
 }
 
 template <bool OUT>
@@ -858,12 +866,17 @@ static hipError_t launch_gemv(const GemmArgs &a0, int nB, hipStream_t s) {
     const long nwg = (long)a.n_tiles * active;
     // At most one workgroup per compute unit (the out-projection of a single token): 16 waves, so that each
     // wave streams half as many K-steps and a compute unit keeps twice the loads in flight.
-    if (rbk == 2)
-        hipLaunchKernelGGL((k_grouped_gemv_bf16<8, 2, OUT>), dim3((unsigned)nwg), dim3(512), 0, s, a);
-    else if (nwg <= device_cus())
-        hipLaunchKernelGGL((k_grouped_gemv_bf16<16, 1, OUT>), dim3((unsigned)nwg), dim3(1024), 0, s, a);
-    else
-        hipLaunchKernelGGL((k_grouped_gemv_bf16<8, 1, OUT>), dim3((unsigned)nwg), dim3(512), 0, s, a);
+    const dim3 grid((unsigned)nwg);
+    if (rbk == 2) {
+        if (a.T <= 32) hipLaunchKernelGGL((k_grouped_gemv_bf16<8, 2, 2, OUT>), grid, dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((k_grouped_gemv_bf16<8, 2, 4, OUT>), grid, dim3(512), 0, s, a);
+    } else if (nwg <= device_cus()) {
+        if (a.T <= 16) hipLaunchKernelGGL((k_grouped_gemv_bf16<16, 1, 1, OUT>), grid, dim3(1024), 0, s, a);
+        else hipLaunchKernelGGL((k_grouped_gemv_bf16<16, 1, 2, OUT>), grid, dim3(1024), 0, s, a);
+    } else {
+        if (a.T <= 16) hipLaunchKernelGGL((k_grouped_gemv_bf16<8, 1, 1, OUT>), grid, dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((k_grouped_gemv_bf16<8, 1, 2, OUT>), grid, dim3(512), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -262,15 +262,20 @@ __device__ __forceinline__ int wg_logits(XRows<TX> &xr, const TX *X, int T, int 
         logits_token<TX, 64, EG, EMAX>(xr, X, T, dm, Wr, wl, E, tok0, jl, lg);
         return tok0;
     }
-    logits_token<TX, 256, EG, EMAX>(xr, X, T, dm, Wr, wl, E, tok0, jl, lg);
+    logits_token<TX, 64 * WPG, EG, EMAX>(xr, X, T, dm, Wr, wl, E, tok0, jl, lg);
     if (lane < 8) {
 #pragma unroll
         for (int e = 0; e < EMAX; ++e) s_red[wave][lane][e] = lg[e];
     }
     __syncthreads();
-    if (lane < 8) {
+    if (lane < 8) {  // the waves' partial sums, added in wave order
 #pragma unroll
-        for (int e = 0; e < EMAX; ++e) lg[e] = ((s_red[0][lane][e] + s_red[1][lane][e]) + s_red[2][lane][e]) + s_red[3][lane][e];
+        for (int e = 0; e < EMAX; ++e) {
+            float v = s_red[0][lane][e];
+#pragma unroll
+            for (int w = 1; w < WPG; ++w) v += s_red[w][lane][e];
+            lg[e] = v;
+        }
     }
     return tok_base;
 }
@@ -678,33 +683,30 @@ __global__ __launch_bounds__(256) void k_route_scan(const int32_t *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------------------------
-// Small-T path (T <= 8): the whole routing in one workgroup and one launch; the four waves split
-// d_model.
-template <typename TX, int EG, int EMAX>
-__global__ __launch_bounds__(256) void k_route_small(const TX *__restrict__ X, int T, int dm,
-                                                     const float *__restrict__ Wr, const float *__restrict__ bias,
-                                                     int E, int K, int use_lds, int32_t *__restrict__ ids,
-                                                     float *__restrict__ prob, int32_t *__restrict__ counts,
-                                                     int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
-                                                     int32_t *__restrict__ inv_perm, TX *__restrict__ Xp) {
-    extern __shared__ float4 wl_dyn[];
+// Small-T path (T <= 8): the whole routing in one workgroup and one launch. Its WPG waves split d_model
+// (64 WPG lanes, each with at most one or two 8-element chunks), so that every X and W_r load goes out at
+// once, in one round trip; W_r is read from L2/HBM directly (each of its values serves at most 8 tokens).
+// The grouping of at most 8 tokens is counted directly: slot = (tokens of lower experts) + (earlier tokens
+// of the same expert).
+template <typename TX, int EG, int EMAX, int WPG>
+__global__ __launch_bounds__(64 * WPG) void k_route_small(const TX *__restrict__ X, int T, int dm,
+                                                          const float *__restrict__ Wr, const float *__restrict__ bias,
+                                                          int E, int K, int32_t *__restrict__ ids,
+                                                          float *__restrict__ prob, int32_t *__restrict__ counts,
+                                                          int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
+                                                          int32_t *__restrict__ inv_perm, TX *__restrict__ Xp) {
     __shared__ int s_ids[ROM_MAX_TOP_K * kRouteSmallT];
-    __shared__ int s_base[ROM_MAX_EXPERTS];
-    __shared__ int s_wcnt[4][ROM_MAX_EXPERTS];
     __shared__ int s_pos[kRouteSmallT];
-    __shared__ float s_red[4][8][EMAX];
+    __shared__ float s_red[WPG][8][EMAX];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (use_lds) stage_router_weight(Wr, dm, E, wl_dyn);
     XRows<TX> xr;
     {
         int g0, jl;
-        wg_token_group<4>(0, g0, jl);
-        xrows_issue<TX, 256>(xr, X, T, dm, g0, jl);
+        wg_token_group<WPG>(0, g0, jl);
+        xrows_issue<TX, 64 * WPG>(xr, X, T, dm, g0, jl);
     }
-    if (use_lds) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // the W_r copies (and the X rows) have landed
-    __syncthreads();
     float lg[EMAX];
-    wg_logits<TX, EG, EMAX, 4>(xr, X, T, dm, Wr, use_lds ? wl_dyn : nullptr, E, 0, lg, s_red);
+    wg_logits<TX, EG, EMAX, WPG>(xr, X, T, dm, Wr, nullptr, E, 0, lg, s_red);
     if (wave == 0 && lane < T) {
         int best[2];
         float p[2];
@@ -719,39 +721,30 @@ __global__ __launch_bounds__(256) void k_route_small(const TX *__restrict__ X, i
         }
     }
     __syncthreads();
-    for (int k = 0; k < K; ++k) {  // the K stacked top-1 routings, one after the other
-        if (tid < E) {
-            int c = 0;
-            for (int t = 0; t < T; ++t) c += (s_ids[k * kRouteSmallT + t] == tid);
-            s_wcnt[0][tid] = c;  // borrowed as the histogram until the scan below
-        }
-        __syncthreads();
-        if (tid == 0) {
-            int run = 0;
-            for (int e = 0; e < E; ++e) {
-                const int c = s_wcnt[0][e];
-                s_base[e] = run;
-                counts[k * E + e] = c;
-                offsets[k * (E + 1) + e] = run;
-                run += c;
-            }
-            offsets[k * (E + 1) + E] = run;
-        }
-        __syncthreads();
-        const int e = tid < T ? s_ids[k * kRouteSmallT + tid] : -1;
-        const int rank = wg_stable_rank(e, E, s_wcnt);
-        int pos = -1;
-        if (e >= 0) {
-            pos = s_base[e] + rank;
+    for (int k = 0; k < K; ++k) {  // the K stacked top-1 routings
+        const int *sid = s_ids + k * kRouteSmallT;
+        if (tid < T) {
+            const int e = sid[tid];
+            int pos = 0;
+            for (int t = 0; t < T; ++t) pos += (sid[t] < e) || (sid[t] == e && t < tid);
             perm[k * T + pos] = tid;
             inv_perm[k * T + tid] = pos;
+            s_pos[tid] = pos;
         }
-        if (Xp) {  // top-1 only
-            if (tid < kRouteSmallT) s_pos[tid] = pos;
+        if (tid < E) {
+            int c = 0, below = 0;
+            for (int t = 0; t < T; ++t) {
+                c += sid[t] == tid;
+                below += sid[t] < tid;
+            }
+            counts[k * E + tid] = c;
+            offsets[k * (E + 1) + tid] = below;
+            if (tid == E - 1) offsets[k * (E + 1) + E] = T;
+        }
+        if (Xp && k == 0) {  // top-1 only
             __syncthreads();
-            permute_rows<TX>(X, Xp, dm, 0, T, s_pos);
+            if (wave < 4) permute_rows<TX>(X, Xp, dm, 0, T, s_pos);
         }
-        __syncthreads();
     }
 }
 
@@ -794,18 +787,20 @@ static hipError_t launch_route_t(const TX *X, int T, int dm, const float *Wr, co
     const bool wide = (T + 31) / 32 >= 512;
     const int use_lds = wide && (E % 4 == 0) && (((E >> 2) & ((E >> 2) - 1)) == 0) && wbytes <= (size_t)kRouteLdsW;
     const size_t smem = use_lds ? wbytes : 0;
-    static LdsAttrOnce attr[3];
-    const void *fns[3] = {reinterpret_cast<const void *>(&k_route_logits<TX, EG, EMAX, 1>),
-                          reinterpret_cast<const void *>(&k_route_logits<TX, EG, EMAX, 4>),
-                          reinterpret_cast<const void *>(&k_route_small<TX, EG, EMAX>)};
-    for (int f = 0; f < 3; ++f) {
+    if (T <= kRouteSmallT) {
+        // 8 waves (one chunk per lane at d_model 4096) when the chunks and logits (bf16 rows, up to 8 experts)
+        // fit the registers of 2 waves per SIMD, else 4
+        constexpr int WPG = (EMAX <= 8 && sizeof(TX) == 2) ? 8 : 4;
+        hipLaunchKernelGGL((k_route_small<TX, EG, EMAX, WPG>), dim3(1), dim3(64 * WPG), 0, s, X, T, dm, Wr, bias, E,
+                           r.top_k, r.expert_id, r.prob, r.counts, r.offsets, r.perm, r.inv_perm, Xp);
+        return hipGetLastError();
+    }
+    static LdsAttrOnce attr[2];
+    const void *fns[2] = {reinterpret_cast<const void *>(&k_route_logits<TX, EG, EMAX, 1>),
+                          reinterpret_cast<const void *>(&k_route_logits<TX, EG, EMAX, 4>)};
+    for (int f = 0; f < 2; ++f) {
         hipError_t err = set_lds_limit_once(attr[f], fns[f], kRouteLdsW);
         if (err != hipSuccess) return err;
-    }
-    if (T <= kRouteSmallT) {
-        hipLaunchKernelGGL((k_route_small<TX, EG, EMAX>), dim3(1), dim3(256), smem, s, X, T, dm, Wr, bias, E, r.top_k,
-                           use_lds, r.expert_id, r.prob, r.counts, r.offsets, r.perm, r.inv_perm, Xp);
-        return hipGetLastError();
     }
     // bf16 rows, 8 experts and a d_model with a matrix-core kernel: 64 tokens per workgroup
     const bool mfma = std::is_same<TX, uint16_t>::value && wide && E == 8 && route_mfma_dm(dm);
