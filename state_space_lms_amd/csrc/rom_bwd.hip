@@ -40,7 +40,10 @@ __global__ __launch_bounds__(256) void k_transpose_weights(const uint16_t *__res
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int idx = threadIdx.x + q * 256, r = idx >> 3, ch = idx & 7;
-        *reinterpret_cast<uint4 *>(&tile[r][ch * 8]) = *reinterpret_cast<const uint4 *>(src + (size_t)r * C + ch * 8);
+        // chunk ch of row r sits at chunk ch ^ ((r / 8) % 8): the transposed 2-byte reads below then spread
+        // over 32 banks instead of 8
+        *reinterpret_cast<uint4 *>(&tile[r][(ch ^ ((r >> 3) & 7)) * 8]) =
+            *reinterpret_cast<const uint4 *>(src + (size_t)r * C + ch * 8);
     }
     __syncthreads();
     uint16_t *dst = out + ((size_t)e * C + c0) * ldo + col0 + r0;
@@ -49,7 +52,7 @@ __global__ __launch_bounds__(256) void k_transpose_weights(const uint16_t *__res
         const int idx = threadIdx.x + q * 256, c = idx >> 3, ch = idx & 7;
         uint16_t v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = tile[ch * 8 + i][c];
+        for (int i = 0; i < 8; ++i) v[i] = tile[ch * 8 + i][(((c >> 3) ^ ch) << 3) + (c & 7)];
         uint4 pk;
         pk.x = v[0] | (uint32_t(v[1]) << 16);
         pk.y = v[2] | (uint32_t(v[3]) << 16);
@@ -67,29 +70,49 @@ hipError_t transpose_weights(const void *in, int E, int R, int C, void *out, int
 
 // ---------------------------------------------------------------------------------------------
 // Gate backward, elementwise over 16-byte chunks: dz = da * h * SiLU'(z), dh = da * SiLU(z), with
-// SiLU'(v) = s (1 + v (1 - s)), s = 1 / (1 + exp(-v)) (hardware exp2 and reciprocal).
+// SiLU'(v) = s (1 + v (1 - s)), s = 1 / (1 + exp(-v)) (hardware exp2 and reciprocal). Memory-bound: every
+// thread issues the loads of kGateBwdChunks chunks (indices clamped into range) before computing any, and
+// workgroups stride over the chunk range.
+constexpr int kGateBwdChunks = 4;
 __global__ __launch_bounds__(256) void k_gate_backward(const uint16_t *__restrict__ da, const uint16_t *__restrict__ z,
                                                        const uint16_t *__restrict__ h, size_t nchunks,
                                                        uint16_t *__restrict__ dz, uint16_t *__restrict__ dh) {
-    const size_t stride = (size_t)gridDim.x * 256;
-    for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < nchunks; u += stride) {
-        float a[8], zv[8], hv[8];
-        load8_f32(da + u * 8, a);
-        load8_f32(z + u * 8, zv);
-        load8_f32(h + u * 8, hv);
-        float oz[8], oh[8];
+    constexpr int U = kGateBwdChunks;
+    const size_t stride = (size_t)gridDim.x * 256 * U;
+    for (size_t u0 = (size_t)blockIdx.x * 256 * U + threadIdx.x; u0 < nchunks; u0 += stride) {
+        u32x4 va[U], vzz[U], vhh[U];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-zv[i]));
-            oz[i] = a[i] * hv[i] * (sg * fmaf(zv[i], 1.0f - sg, 1.0f));
-            oh[i] = a[i] * (zv[i] * sg);
+        for (int j = 0; j < U; ++j) {
+            const size_t u = u0 + (size_t)j * 256 < nchunks ? u0 + (size_t)j * 256 : nchunks - 1;
+            va[j] = reinterpret_cast<const u32x4 *>(da)[u];
+            vzz[j] = reinterpret_cast<const u32x4 *>(z)[u];
+            vhh[j] = reinterpret_cast<const u32x4 *>(h)[u];
         }
-        const u32x4 vz = {pack_bf16x2(oz[0], oz[1]), pack_bf16x2(oz[2], oz[3]), pack_bf16x2(oz[4], oz[5]),
-                          pack_bf16x2(oz[6], oz[7])};
-        const u32x4 vh = {pack_bf16x2(oh[0], oh[1]), pack_bf16x2(oh[2], oh[3]), pack_bf16x2(oh[4], oh[5]),
-                          pack_bf16x2(oh[6], oh[7])};
-        __builtin_nontemporal_store(vz, reinterpret_cast<u32x4 *>(dz + u * 8));
-        __builtin_nontemporal_store(vh, reinterpret_cast<u32x4 *>(dh + u * 8));
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const size_t u = u0 + (size_t)j * 256;
+            if (u < nchunks) {
+                uint32_t oz[4], oh[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float r[2][2];
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) {
+                        const float a = b ? __uint_as_float(va[j][q] & 0xFFFF0000u) : __uint_as_float(va[j][q] << 16);
+                        const float zv = b ? __uint_as_float(vzz[j][q] & 0xFFFF0000u) : __uint_as_float(vzz[j][q] << 16);
+                        const float hv = b ? __uint_as_float(vhh[j][q] & 0xFFFF0000u) : __uint_as_float(vhh[j][q] << 16);
+                        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-zv));
+                        r[0][b] = a * hv * (sg * fmaf(zv, 1.0f - sg, 1.0f));
+                        r[1][b] = a * (zv * sg);
+                    }
+                    oz[q] = pack_bf16x2(r[0][0], r[0][1]);
+                    oh[q] = pack_bf16x2(r[1][0], r[1][1]);
+                }
+                const u32x4 vz = {oz[0], oz[1], oz[2], oz[3]}, vh = {oh[0], oh[1], oh[2], oh[3]};
+                __builtin_nontemporal_store(vz, reinterpret_cast<u32x4 *>(dz) + u);
+                __builtin_nontemporal_store(vh, reinterpret_cast<u32x4 *>(dh) + u);
+            }
+        }
     }
 }
 
@@ -170,14 +193,17 @@ __global__ __launch_bounds__(256) void k_rows_to_cols(const uint16_t *__restrict
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] = f32_to_bf16(a[i]);
         }
+        // 8-column group of (feature f, column j) in LDS: (j / 8) ^ ((f / 8) % 8), so that the 2-byte transposed
+        // writes of a wave (8 features apart, 8 columns) spread over 32 banks instead of 8
+        const int cgs = (((j >> 3) ^ ch) << 3) + (j & 7);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) tile[ch * 8 + i][j] = v[i];
+        for (int i = 0; i < 8; ++i) tile[ch * 8 + i][cgs] = v[i];
     }
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int idx = tid + q * 256, f = idx >> 3, ch = idx & 7;
-        const uint4 w = *reinterpret_cast<const uint4 *>(&tile[f][ch * 8]);
+        const uint4 w = *reinterpret_cast<const uint4 *>(&tile[f][(ch ^ ((f >> 3) & 7)) * 8]);
         *reinterpret_cast<uint4 *>(out + (size_t)(f_off + f0 + f) * ldo + j0 + ch * 8) = w;
     }
 }
@@ -396,8 +422,8 @@ hipError_t launch_out_proj_backward(const void *g, const void *z, const void *h,
     a.E = E;
     a.a_by_token = 1;
     for (int k = 0; k < K; ++k) ROM_TRY(launch_grouped_bf16(choice_args(a, r, T, k), true, 1, s));
-    const size_t nchunks = (size_t)T * di / 8;
-    const unsigned gblocks = (unsigned)((nchunks + 255) / 256 < 4096 ? (nchunks + 255) / 256 : 4096);
+    const size_t nchunks = (size_t)T * di / 8, per_wg = 256 * kGateBwdChunks;
+    const unsigned gblocks = (unsigned)((nchunks + per_wg - 1) / per_wg < 4096 ? (nchunks + per_wg - 1) / per_wg : 4096);
     hipLaunchKernelGGL(k_gate_backward, dim3(gblocks), dim3(256), 0, s, da, static_cast<const uint16_t *>(z),
                        static_cast<const uint16_t *>(h), nchunks, static_cast<uint16_t *>(dz),
                        static_cast<uint16_t *>(dh));

@@ -524,168 +524,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
 }
 
 // ---------------------------------------------------------------------------------------------
-// Ping-pong bf16 grouped GEMM: 256 x 256 tiles, K step 64, two LDS stages, 8 waves in two groups of four.
-// The waves of a workgroup are spread over the SIMDs in order, so waves w and w + 4 share a SIMD: group 0
-// (waves 0-3) and group 1 (waves 4-7) hold one wave on every SIMD. The groups take turns, two phases per K
-// step separated by barriers: in one phase a group issues the 32 MFMAs of a K step from fragments it already
-// holds in registers (at raised priority), while the other group reads its fragments of a step from LDS; so a
-// SIMD's matrix core is fed by one wave while the other waits for LDS. Wave (g, q) owns the 128 x 64 block
-// (wm, wn) = (q / 2, 2 g + q % 2) of the tile, laid out as in k_grouped_gemm_bf16's 8-wave 256 x 256 tile,
-// whose epilogue it shares.
-//
-// Timeline, phase 2k and 2k + 1 of K step k (stage k % 2 holds step k):
-//   phase 2k:     group 0: MFMAs of step k            group 1: reads step k's fragments
-//                 every wave: its copies of step k + 1 have landed (vmcnt 0)           -- barrier
-//   phase 2k + 1: every wave issues its copies of step k + 2 into stage k % 2 (step k's reads are done)
-//                 group 0: reads step k + 1's fragments    group 1: MFMAs of step k    -- barrier
-// so the copies of a step are in flight for two phases. The prologue copies steps 0 and 1 and gives group 0
-// the fragments of step 0.
-template <bool OUT>
-__global__ __launch_bounds__(512) void k_grouped_gemm_pp(GemmArgs p) {
-    constexpr int BM = 256, BN = 256, BK = 64, NSTAGE = 2, WGM = 2, WGN = 4, NW = 8, NT = 512;
-    constexpr int KCH = BK / 8, RG = 64 / KCH;
-    constexpr int A_DMA = BM / RG / NW, B_DMA = BN / RG / NW, PER_STEP = A_DMA + B_DMA;
-    constexpr int STAGE = (BM + BN) * BK;
-    constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32, NKK = BK / 16;
-    static_assert(PER_STEP < 16, "vmcnt");
-
-    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-    __shared__ int s_tok[BM];
-    __shared__ int s_arow[BM];
-    __shared__ float s_prob[OUT ? BM : 1];
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int mt, nt, e, slot0, rows;
-    if (!tile_of_block(p, mt, nt)) return;
-    if (!locate_mtile<BM>(p.offsets, p.E, mt, e, slot0, rows)) return;
-    const int which = nt / p.n_tiles_per_b;
-    const int n0 = (nt % p.n_tiles_per_b) * BN;
-    const int K = p.K;
-    const uint16_t *Bsrc = static_cast<const uint16_t *>(which ? p.B1 : p.B0) + ((size_t)e * p.N0 + n0) * K;
-    uint16_t *C = static_cast<uint16_t *>(which ? p.C1 : p.C0);
-
-    // rows past the group's end repeat its last row (in-bounds, finite data); they are never stored
-    for (int i = tid; i < BM; i += NT) {
-        const int slot = slot0 + min(i, rows - 1);
-        const int tok = p.perm[slot];
-        s_tok[i] = tok;
-        s_arow[i] = (OUT && !p.a_by_token) ? slot : tok;
-        if (OUT) s_prob[i] = p.prob[tok];
-    }
-    __syncthreads();
-
-    // copy sources, as in k_grouped_gemm_bf16: lane i fills row g*RG + i/KCH, physical chunk i%KCH
-    const int dr = lane / KCH, dpc = lane % KCH;
-    const uint16_t *a_dma[A_DMA];
-    const uint16_t *b_dma[B_DMA];
-#pragma unroll
-    for (int j = 0; j < A_DMA; ++j) {
-        const int row = (wave * A_DMA + j) * RG + dr;
-        a_dma[j] = static_cast<const uint16_t *>(p.A0) + (size_t)s_arow[row] * K + (dpc ^ lds_swz<KCH>(row)) * 8;
-    }
-#pragma unroll
-    for (int j = 0; j < B_DMA; ++j) {
-        const int row = (wave * B_DMA + j) * RG + dr;
-        b_dma[j] = Bsrc + (size_t)row * K + (dpc ^ lds_swz<KCH>(row)) * 8;
-    }
-    auto issue_copies = [&](int kt, int stage) {
-        uint16_t *as = smem + stage * STAGE;
-        uint16_t *bs = as + BM * BK;
-        const int k0 = kt * BK;
-#pragma unroll
-        for (int j = 0; j < A_DMA; ++j) dma16_to_lds(a_dma[j] + k0, as + (wave * A_DMA + j) * RG * BK);
-#pragma unroll
-        for (int j = 0; j < B_DMA; ++j) dma16_to_lds(b_dma[j] + k0, bs + (wave * B_DMA + j) * RG * BK);
-    };
-
-    const int g = wave >> 2, q = wave & 3;
-    const int wm = q >> 1, wn = 2 * g + (q & 1);
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    const int half = lane >> 5;
-    const int a_frag0 = (wm * WM + (lane & 31)) * BK;
-    const int b_frag0 = BM * BK + (wn * WN + (lane & 31)) * BK;
-    const int swz = lds_swz<KCH>(lane & 31);
-    bf16x8 af[NKK][FM], bfr[NKK][FN];
-    auto load_step = [&](int stg) {
-        const uint16_t *st = smem + stg * STAGE;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const int co = ((kk * 2 + half) ^ swz) * 8;
-#pragma unroll
-            for (int i = 0; i < FM; ++i) af[kk][i] = *reinterpret_cast<const bf16x8 *>(st + a_frag0 + i * 32 * BK + co);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) bfr[kk][j] = *reinterpret_cast<const bf16x8 *>(st + b_frag0 + j * 32 * BK + co);
-        }
-    };
-    auto mfma_step = [&]() {
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk][j], af[kk][i], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_s_setprio(0);
-    };
-    auto barrier = [&]() {
-        __builtin_amdgcn_sched_barrier(0);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_barrier();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    const int nk = K / BK;
-    issue_copies(0, 0);
-    if (nk > 1) {
-        issue_copies(1, 1);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(PER_STEP));  // step 0 has landed
-    } else {
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-    }
-    barrier();
-    // each group runs its own copy of the loop (the same barriers, two per K step), so that the compiler
-    // keeps one set of fragment registers per wave
-    if (g == 0) {
-        load_step(0);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
-        barrier();
-        for (int k = 0; k < nk; ++k) {
-            const int st = k & 1;
-            mfma_step();                                      // phase 2k: step k
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // the copies of step k + 1 have landed
-            barrier();
-            if (k + 2 < nk) issue_copies(k + 2, st);          // phase 2k + 1
-            // past the last step this reads a stage that is never used again (in bounds)
-            load_step(st ^ 1);
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
-            barrier();
-        }
-    } else {
-        barrier();
-        for (int k = 0; k < nk; ++k) {
-            const int st = k & 1;
-            load_step(st);                                    // phase 2k: step k's fragments
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // and the copies of step k + 1 have landed
-            barrier();
-            if (k + 2 < nk) issue_copies(k + 2, st);          // phase 2k + 1
-            mfma_step();
-            barrier();
-        }
-    }
-    gemm_epilogue<BM, BN, BK, NSTAGE, WGM, WGN, OUT>(p, acc, wm, wn, rows, n0, C, s_tok, s_prob, smem);
-}
-
-// ---------------------------------------------------------------------------------------------
 // Gate and permute for the out-projection (bf16): a[pos][n] = bf16(SiLU(z[t][n]) * h[t][n]) with
 // t = perm[pos], fp32 arithmetic, rows written in slot order so the GEMM reads each expert's rows
 // contiguously; with perm == NULL, t = pos (token order, shared by the two choices of a top-2 routing
@@ -998,22 +836,6 @@ static hipError_t launch_bf16(const GemmArgs &a0, int nB, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <bool OUT>
-static hipError_t launch_pp(const GemmArgs &a0, int nB, hipStream_t s) {
-    GemmArgs a = a0;
-    a.n_tiles_per_b = a.N0 / 256;
-    a.n_tiles = nB * a.n_tiles_per_b;
-    a.m_tiles = (a.T + a.E * 255) / 256;
-    a.group_m = 0;
-    const unsigned grid = (unsigned)a.m_tiles * a.n_tiles;
-    const size_t smem = gemm_lds_bytes(256, 256, 64, 2, 2);
-    static LdsAttrOnce attr;
-    hipError_t err = set_lds_limit_once(attr, reinterpret_cast<const void *>(&k_grouped_gemm_pp<OUT>), smem);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((k_grouped_gemm_pp<OUT>), dim3(grid), dim3(512), smem, s, a);
-    return hipGetLastError();
-}
-
 // Tile shapes available to the bf16 path.
 struct TileCfg { int bm, bn, bk, nstage, wgm, wgn, sched; };
 constexpr TileCfg kTiles[] = {
@@ -1027,7 +849,6 @@ constexpr TileCfg kTiles[] = {
     {320, 256, 64, 2, 2, 4, 1},  // 7: 8 waves (160x64 each), BK 64, 2 stages (144 KiB), C tile in 2 passes
     {256, 256, 64, 2, 2, 4, 2},  // 8: as 0, barrier ahead of each step's last MFMAs
     {320, 256, 64, 2, 2, 4, 2},  // 9: as 7, barrier ahead of each step's last MFMAs
-    {256, 256, 64, 2, 2, 4, 3},  // 10: ping-pong (k_grouped_gemm_pp): 8 waves in two alternating groups
 };
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
@@ -1073,9 +894,6 @@ static hipError_t launch_bf16_auto(const GemmArgs &a, int nB, hipStream_t s) {
         case 7: return launch_bf16<320, 256, 64, 2, 2, 4, OUT, 1, KSPLIT>(a, nB, s);
         case 8: return launch_bf16<256, 256, 64, 2, 2, 4, OUT, 2, KSPLIT>(a, nB, s);
         case 9: return launch_bf16<320, 256, 64, 2, 2, 4, OUT, 2, KSPLIT>(a, nB, s);
-        case 10:
-            if constexpr (!KSPLIT) return launch_pp<OUT>(a, nB, s);
-            return launch_bf16<256, 256, 64, 2, 2, 4, OUT, 2, KSPLIT>(a, nB, s);
         default: return launch_bf16<128, 64, 64, 4, 2, 2, OUT, 0, KSPLIT>(a, nB, s);
     }
 }
