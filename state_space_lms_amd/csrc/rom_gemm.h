@@ -33,4 +33,13 @@ struct GemmArgs {
 // unless a_by_token. Every field the kernels read must be set (zero-initialise the struct).
 hipError_t launch_grouped_bf16(const GemmArgs &a, bool out, int nB, hipStream_t s);
 
+// Decode-size kernels (rom_gemv.hip): every workgroup streams 16 (or 32) weight rows of one active expert and
+// applies them to all of that expert's tokens. out: probability-scaled results (rows gathered in token order).
+hipError_t launch_gemv_bf16(const GemmArgs &a, bool out, int nB, hipStream_t s);
+// The same with the expert's token rows staged in LDS once per workgroup (gemv_lds_fits); gated (with out):
+// the staged rows are bf16(SiLU(A0) * A1), the out-projection's gate computed on the fly.
+constexpr size_t kGemvLdsBytes = 64 * 1024;
+inline bool gemv_lds_fits(int T, int K) { return T <= 16 && (size_t)T * (K + 8) * 2 <= kGemvLdsBytes; }
+hipError_t launch_gemv_lds_bf16(const GemmArgs &a, bool out, bool gated, int nB, hipStream_t s);
+
 }  // namespace rom

@@ -21,7 +21,7 @@
 // as whole 16-byte row chunks. Details at k_grouped_gemm_bf16. The backward's data gradients run the same
 // kernels on transposed weight stacks (KSPLIT: the A rows switch source at k_split).
 //
-// Decode path (T <= 64): weight-streaming kernels (k_grouped_gemv_bf16). fp32 data: k_grouped_gemm_f32.
+// Decode path (T <= 64): weight-streaming kernels in rom_gemv.hip. fp32 data: k_grouped_gemm_f32.
 #include <stdlib.h>
 
 #include "rom_device.h"
@@ -574,151 +574,6 @@ __global__ __launch_bounds__(256) void k_gate_permute(const uint16_t *__restrict
 }
 
 // ---------------------------------------------------------------------------------------------
-// Decode path (T <= 64): the cost is streaming each active expert's weights from HBM once; the MFMA
-// work is tiny. A workgroup owns RB blocks of 16 weight rows of one expert and every token routed to it
-// (at most 64, i.e. NB blocks of 16), and its NW waves split K. The weight fragment of a 16x16x32 MFMA
-// comes straight from global memory (lane l: row l%16, 8 elements at k + 8*(l/16)), the token fragments
-// likewise through perm (for the out-projection, from the gated rows k_gate_permute wrote in token
-// order: the gate is evaluated once per token, not once per workgroup and padding column); each wave
-// keeps U K-steps of loads in flight. Every workgroup reads all of its expert's token rows, so with more
-// tokens (RB = 2 from 32 tokens on) a workgroup takes 32 weight rows and the token rows are read half as
-// often. Partial sums of the waves are added in wave order through LDS (deterministic), then scaled
-// (out-projection) and stored.
-// Grid: (weight rows / (16 RB)) x min(E, T): the second index is the rank among experts that received
-// tokens; each workgroup runs the variant sized for its expert's token-block count.
-template <int NW, int RB, int NB, int U, bool OUT>
-__device__ __forceinline__ void gemv_block(const GemmArgs &p, int e, int o0, int ne, int rb,
-                                           float (*s_red)[RB * 4][16][16]) {
-    constexpr int NT = 64 * NW;
-    __shared__ int s_tok[64];
-    __shared__ float s_prob[64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nglob = rb * 16 * RB;  // N0 is a multiple of 64, so the RB blocks lie in one output
-    const int which = nglob / p.N0, n0 = nglob % p.N0;
-    const int K = p.K;
-    const uint16_t *W = static_cast<const uint16_t *>(which ? p.B1 : p.B0) + ((size_t)e * p.N0 + n0) * K;
-    uint16_t *C = static_cast<uint16_t *>(which ? p.C1 : p.C0);
-    const int tok_first = p.perm[o0];
-    for (int i = tid; i < 64; i += NT) {
-        const int tok = i < ne ? p.perm[o0 + i] : tok_first;
-        s_tok[i] = tok;
-        s_prob[i] = OUT ? p.prob[tok] : 1.0f;
-    }
-    __syncthreads();
-
-    const int r = lane & 15, g = lane >> 4;
-    const uint16_t *wp[RB];
-#pragma unroll
-    for (int j = 0; j < RB; ++j) wp[j] = W + (size_t)(j * 16 + r) * K + g * 8;
-    const uint16_t *xp[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) xp[b] = static_cast<const uint16_t *>(p.A0) + (size_t)s_tok[b * 16 + r] * K + g * 8;
-    f32x4 acc[RB][NB];
-#pragma unroll
-    for (int j = 0; j < RB; ++j)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) acc[j][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-    // U K-steps of loads in flight per wave (indices clamped, so every load is in bounds), then their MFMAs.
-    // With 8 waves each wave streams a contiguous K range (U consecutive steps: 32 U contiguous elements of
-    // each row per batch); with 16 waves the steps are interleaved (the 16 waves' loads of one batch cover
-    // 16 consecutive steps), which measured faster for the one-workgroup-per-CU launch.
-    constexpr bool CONTIG = NW == 8;
-    const int nsteps = K / 32;
-    const int spw = CONTIG ? (nsteps + NW - 1) / NW : 0;
-    const int sbeg = CONTIG ? wave * spw : wave, send = CONTIG ? min(nsteps, sbeg + spw) : nsteps;
-    constexpr int SU = CONTIG ? 1 : NW;  // step stride within a batch
-    for (int s0 = sbeg; s0 < send; s0 += SU * U) {
-        bf16x8 wf[U][RB], xf[U][NB];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k0 = min(s0 + u * SU, send - 1) * 32;
-#pragma unroll
-            for (int j = 0; j < RB; ++j) wf[u][j] = *reinterpret_cast<const bf16x8 *>(wp[j] + k0);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) xf[u][b] = *reinterpret_cast<const bf16x8 *>(xp[b] + k0);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (s0 + u * SU < send) {  // uniform
-#pragma unroll
-                for (int j = 0; j < RB; ++j)
-#pragma unroll
-                    for (int b = 0; b < NB; ++b)
-                        acc[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u][j], xf[u][b], acc[j][b], 0, 0, 0);
-            }
-        }
-    }
-    // accumulator register i of lane l: weight row 4*(l/16) + i (of block j), token column l%16
-#pragma unroll
-    for (int j = 0; j < RB; ++j)
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s_red[wave][j * NB + b][4 * g + i][r] = acc[j][b][i];
-    __syncthreads();
-    for (int idx = tid; idx < RB * NB * 256; idx += NT) {
-        const int jb = idx >> 8, n = (idx >> 4) & 15, m = idx & 15;
-        const int j = jb / NB, b = jb - j * NB;
-        const int col = b * 16 + m;
-        if (col < ne) {
-            float v = 0.0f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) v += s_red[w][jb][n][m];
-            uint16_t *dst = C + (size_t)s_tok[col] * p.N0 + n0 + j * 16 + n;
-            *dst = f32_to_bf16(p.accumulate ? fmaf(v, s_prob[col], bf16_to_f32(*dst)) : v * s_prob[col]);
-        }
-    }
-}
-
-// NBMAX: the most token blocks any expert can hold (T <= 16 NBMAX), so that small T instantiates only the
-// small variants and keeps fewer registers.
-template <int NW, int RB, int NBMAX, bool OUT>
-__global__ __launch_bounds__(64 * NW) void k_grouped_gemv_bf16(GemmArgs p) {
-    __shared__ float s_red[NW][RB * 4][16][16];
-    const int rb = blockIdx.x % p.n_tiles, rank = blockIdx.x / p.n_tiles;
-    int e = -1, o0 = 0, ne = 0;
-    for (int i = 0, j = 0; i < p.E; ++i) {
-        const int c = p.offsets[i + 1] - p.offsets[i];
-        if (c > 0) {
-            if (j == rank) { e = i; o0 = p.offsets[i]; ne = c; break; }
-            ++j;
-        }
-    }
-    if (e < 0) return;
-    const int nb = (ne + 15) >> 4;  // token blocks of this expert (1..NBMAX), uniform per workgroup
-    if (NBMAX == 1 || nb == 1) gemv_block<NW, RB, 1, 8, OUT>(p, e, o0, ne, rb, s_red);
-    else if (NBMAX == 2 || nb == 2) gemv_block<NW, RB, 2, 4, OUT>(p, e, o0, ne, rb, s_red);
-    else if (nb == 3) gemv_block<NW, RB, 3, 4, OUT>(p, e, o0, ne, rb, s_red);
-    else gemv_block<NW, RB, 4, 4, OUT>(p, e, o0, ne, rb, s_red);
-}
-
-template <bool OUT>
-static hipError_t launch_gemv(const GemmArgs &a0, int nB, hipStream_t s) {
-    GemmArgs a = a0;
-    const int active = a.T < a.E ? a.T : a.E;
-    // From 32 tokens on, 32 weight rows per workgroup (every workgroup reads all of its expert's token rows)
-    const int rbk = a.T >= 32 ? 2 : 1;
-    a.n_tiles = nB * a.N0 / (16 * rbk);
-    a.n_tiles_per_b = a.N0 / (16 * rbk);
-    const long nwg = (long)a.n_tiles * active;
-    // At most one workgroup per compute unit (the out-projection of a single token): 16 waves, so that each
-    // wave streams half as many K-steps and a compute unit keeps twice the loads in flight.
-    const dim3 grid((unsigned)nwg);
-    if (rbk == 2) {
-        if (a.T <= 32) hipLaunchKernelGGL((k_grouped_gemv_bf16<8, 2, 2, OUT>), grid, dim3(512), 0, s, a);
-        else hipLaunchKernelGGL((k_grouped_gemv_bf16<8, 2, 4, OUT>), grid, dim3(512), 0, s, a);
-    } else if (nwg <= device_cus()) {
-        if (a.T <= 16) hipLaunchKernelGGL((k_grouped_gemv_bf16<16, 1, 1, OUT>), grid, dim3(1024), 0, s, a);
-        else hipLaunchKernelGGL((k_grouped_gemv_bf16<16, 1, 2, OUT>), grid, dim3(1024), 0, s, a);
-    } else {
-        if (a.T <= 16) hipLaunchKernelGGL((k_grouped_gemv_bf16<8, 1, 1, OUT>), grid, dim3(512), 0, s, a);
-        else hipLaunchKernelGGL((k_grouped_gemv_bf16<8, 1, 2, OUT>), grid, dim3(512), 0, s, a);
-    }
-    return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------------------------
 // fp32 grouped GEMM (fp32 storage; plain FMA, fp32 accumulation). 64x64 tiles, BK = 16, 256
 // threads, 4x4 outputs per thread. Used for fp32 data, where exact fp32 products are wanted.
 template <bool OUT>
@@ -933,7 +788,8 @@ hipError_t launch_in_proj(const void *X, const rom_routing &r, rom_dtype dt, int
         set_choice(a, r, T, k);
         hipError_t err;
         if (dt == ROM_DTYPE_F32) err = launch_f32<false>(a, 2, s);
-        else if (T <= kDecodeMaxT) err = launch_gemv<false>(a, 2, s);
+        else if (gemv_lds_fits(T, dm)) err = launch_gemv_lds_bf16(a, false, false, 2, s);
+        else if (T <= kDecodeMaxT) err = launch_gemv_bf16(a, false, 2, s);
         else err = launch_bf16_auto<false>(a, 2, s);
         if (err != hipSuccess) return err;
     }
@@ -951,6 +807,15 @@ hipError_t launch_out_proj(const void *z, const void *h, const rom_routing &r, r
     a.K = di;
     a.N0 = dm;
     a.E = r.E;
+    if (dt == ROM_DTYPE_BF16 && gemv_lds_fits(T, di)) {
+        // the smallest T: the decode kernel gates the token rows itself while staging them in LDS
+        for (int k = 0; k < r.top_k; ++k) {
+            set_choice(a, r, T, k);
+            hipError_t err = launch_gemv_lds_bf16(a, true, true, 1, s);
+            if (err != hipSuccess) return err;
+        }
+        return hipSuccess;
+    }
     if (dt == ROM_DTYPE_BF16) {
         // gated rows a = bf16(SiLU(z) * h) into the workspace, once per token: in slot order for top-1 at
         // T > 64 (the GEMM then reads each expert's rows contiguously), otherwise in token order (both
@@ -971,7 +836,7 @@ hipError_t launch_out_proj(const void *z, const void *h, const rom_routing &r, r
         set_choice(a, r, T, k);
         hipError_t err;
         if (dt == ROM_DTYPE_F32) err = launch_f32<true>(a, 1, s);
-        else if (T <= kDecodeMaxT) err = launch_gemv<true>(a, 1, s);
+        else if (T <= kDecodeMaxT) err = launch_gemv_bf16(a, true, 1, s);
         else err = launch_bf16_auto<true>(a, 1, s);
         if (err != hipSuccess) return err;
     }
@@ -997,7 +862,8 @@ hipError_t launch_in_proj_weighted(const void *X, const rom_routing &r, rom_dtyp
         set_choice(a, r, T, k);
         hipError_t err;
         if (dt == ROM_DTYPE_F32) err = launch_f32<true>(a, 1, s);
-        else if (T <= kDecodeMaxT) err = launch_gemv<true>(a, 1, s);
+        else if (gemv_lds_fits(T, dm)) err = launch_gemv_lds_bf16(a, true, false, 1, s);
+        else if (T <= kDecodeMaxT) err = launch_gemv_bf16(a, true, 1, s);
         else err = launch_bf16_auto<true>(a, 1, s);
         if (err != hipSuccess) return err;
     }

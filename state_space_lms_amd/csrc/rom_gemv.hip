@@ -1,0 +1,327 @@
+// rom_gemv.hip -- decode-size (T <= 64) grouped projections of the Routing Mamba experts on gfx950.
+//
+// Method: Routing Mamba landing page (chapterpal.com), Knowl 1: the same expert products as rom_gemm.hip
+// (x = W_conv[e] X, z = W_gate[e] X; out = p W_out[e] (SiLU(z) * h); Swimba's y = p W_in[e] X). With a few
+// tokens per expert the cost is streaming each active expert's weights from HBM once: these kernels give every
+// workgroup 16 (or 32) weight rows of one active expert and all of that expert's tokens, and use 16x16x32
+// MFMAs only to apply each weight fragment to up to 16 tokens at once.
+#include "rom_device.h"
+#include "rom_gemm.h"
+#include "rom_internal.h"
+
+namespace rom {
+
+// ---------------------------------------------------------------------------------------------
+// Decode path (T <= 64): the cost is streaming each active expert's weights from HBM once; the MFMA
+// work is tiny. A workgroup owns RB blocks of 16 weight rows of one expert and every token routed to it
+// (at most 64, i.e. NB blocks of 16), and its NW waves split K. The weight fragment of a 16x16x32 MFMA
+// comes straight from global memory (lane l: row l%16, 8 elements at k + 8*(l/16)), the token fragments
+// likewise through perm (for the out-projection, from the gated rows k_gate_permute wrote in token
+// order: the gate is evaluated once per token, not once per workgroup and padding column); each wave
+// keeps U K-steps of loads in flight. Every workgroup reads all of its expert's token rows, so with more
+// tokens (RB = 2 from 32 tokens on) a workgroup takes 32 weight rows and the token rows are read half as
+// often. Partial sums of the waves are added in wave order through LDS (deterministic), then scaled
+// (out-projection) and stored.
+// Grid: (weight rows / (16 RB)) x min(E, T): the second index is the rank among experts that received
+// tokens; each workgroup runs the variant sized for its expert's token-block count.
+template <int NW, int RB, int NB, int U, bool OUT>
+__device__ __forceinline__ void gemv_block(const GemmArgs &p, int e, int o0, int ne, int rb,
+                                           float (*s_red)[RB * 4][16][16]) {
+    constexpr int NT = 64 * NW;
+    __shared__ int s_tok[64];
+    __shared__ float s_prob[64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nglob = rb * 16 * RB;  // N0 is a multiple of 64, so the RB blocks lie in one output
+    const int which = nglob / p.N0, n0 = nglob % p.N0;
+    const int K = p.K;
+    const uint16_t *W = static_cast<const uint16_t *>(which ? p.B1 : p.B0) + ((size_t)e * p.N0 + n0) * K;
+    uint16_t *C = static_cast<uint16_t *>(which ? p.C1 : p.C0);
+    const int tok_first = p.perm[o0];
+    for (int i = tid; i < 64; i += NT) {
+        const int tok = i < ne ? p.perm[o0 + i] : tok_first;
+        s_tok[i] = tok;
+        s_prob[i] = OUT ? p.prob[tok] : 1.0f;
+    }
+    __syncthreads();
+
+    const int r = lane & 15, g = lane >> 4;
+    const uint16_t *wp[RB];
+#pragma unroll
+    for (int j = 0; j < RB; ++j) wp[j] = W + (size_t)(j * 16 + r) * K + g * 8;
+    const uint16_t *xp[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) xp[b] = static_cast<const uint16_t *>(p.A0) + (size_t)s_tok[b * 16 + r] * K + g * 8;
+    f32x4 acc[RB][NB];
+#pragma unroll
+    for (int j = 0; j < RB; ++j)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[j][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    // U K-steps of loads in flight per wave (indices clamped, so every load is in bounds), then their MFMAs.
+    // With 8 waves each wave streams a contiguous K range (U consecutive steps: 32 U contiguous elements of
+    // each row per batch); with 16 waves the steps are interleaved (the 16 waves' loads of one batch cover
+    // 16 consecutive steps), which measured faster for the one-workgroup-per-CU launch.
+    constexpr bool CONTIG = NW == 8;
+    const int nsteps = K / 32;
+    const int spw = CONTIG ? (nsteps + NW - 1) / NW : 0;
+    const int sbeg = CONTIG ? wave * spw : wave, send = CONTIG ? min(nsteps, sbeg + spw) : nsteps;
+    constexpr int SU = CONTIG ? 1 : NW;  // step stride within a batch
+    for (int s0 = sbeg; s0 < send; s0 += SU * U) {
+        bf16x8 wf[U][RB], xf[U][NB];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k0 = min(s0 + u * SU, send - 1) * 32;
+#pragma unroll
+            for (int j = 0; j < RB; ++j) wf[u][j] = *reinterpret_cast<const bf16x8 *>(wp[j] + k0);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) xf[u][b] = *reinterpret_cast<const bf16x8 *>(xp[b] + k0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (s0 + u * SU < send) {  // uniform
+#pragma unroll
+                for (int j = 0; j < RB; ++j)
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        acc[j][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u][j], xf[u][b], acc[j][b], 0, 0, 0);
+            }
+        }
+    }
+    // accumulator register i of lane l: weight row 4*(l/16) + i (of block j), token column l%16
+#pragma unroll
+    for (int j = 0; j < RB; ++j)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_red[wave][j * NB + b][4 * g + i][r] = acc[j][b][i];
+    __syncthreads();
+    for (int idx = tid; idx < RB * NB * 256; idx += NT) {
+        const int jb = idx >> 8, n = (idx >> 4) & 15, m = idx & 15;
+        const int j = jb / NB, b = jb - j * NB;
+        const int col = b * 16 + m;
+        if (col < ne) {
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) v += s_red[w][jb][n][m];
+            uint16_t *dst = C + (size_t)s_tok[col] * p.N0 + n0 + j * 16 + n;
+            *dst = f32_to_bf16(p.accumulate ? fmaf(v, s_prob[col], bf16_to_f32(*dst)) : v * s_prob[col]);
+        }
+    }
+}
+
+// NBMAX: the most token blocks any expert can hold (T <= 16 NBMAX), so that small T instantiates only the
+// small variants and keeps fewer registers.
+template <int NW, int RB, int NBMAX, bool OUT>
+__global__ __launch_bounds__(64 * NW) void k_grouped_gemv_bf16(GemmArgs p) {
+    __shared__ float s_red[NW][RB * 4][16][16];
+    const int rb = blockIdx.x % p.n_tiles, rank = blockIdx.x / p.n_tiles;
+    int e = -1, o0 = 0, ne = 0;
+    for (int i = 0, j = 0; i < p.E; ++i) {
+        const int c = p.offsets[i + 1] - p.offsets[i];
+        if (c > 0) {
+            if (j == rank) { e = i; o0 = p.offsets[i]; ne = c; break; }
+            ++j;
+        }
+    }
+    if (e < 0) return;
+    const int nb = (ne + 15) >> 4;  // token blocks of this expert (1..NBMAX), uniform per workgroup
+    if (NBMAX == 1 || nb == 1) gemv_block<NW, RB, 1, 8, OUT>(p, e, o0, ne, rb, s_red);
+    else if (NBMAX == 2 || nb == 2) gemv_block<NW, RB, 2, 4, OUT>(p, e, o0, ne, rb, s_red);
+    else if (nb == 3) gemv_block<NW, RB, 3, 4, OUT>(p, e, o0, ne, rb, s_red);
+    else gemv_block<NW, RB, 4, 4, OUT>(p, e, o0, ne, rb, s_red);
+}
+
+template <bool OUT>
+static hipError_t launch_gemv_t(const GemmArgs &a0, int nB, hipStream_t s) {
+    GemmArgs a = a0;
+    const int active = a.T < a.E ? a.T : a.E;
+    // From 32 tokens on, 32 weight rows per workgroup (every workgroup reads all of its expert's token rows)
+    const int rbk = a.T >= 32 ? 2 : 1;
+    a.n_tiles = nB * a.N0 / (16 * rbk);
+    a.n_tiles_per_b = a.N0 / (16 * rbk);
+    const long nwg = (long)a.n_tiles * active;
+    // At most one workgroup per compute unit (the out-projection of a single token): 16 waves, so that each
+    // wave streams half as many K-steps and a compute unit keeps twice the loads in flight.
+    const dim3 grid((unsigned)nwg);
+    if (rbk == 2) {
+        if (a.T <= 32) hipLaunchKernelGGL((k_grouped_gemv_bf16<8, 2, 2, OUT>), grid, dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((k_grouped_gemv_bf16<8, 2, 4, OUT>), grid, dim3(512), 0, s, a);
+    } else if (nwg <= device_cus()) {
+        if (a.T <= 16) hipLaunchKernelGGL((k_grouped_gemv_bf16<16, 1, 1, OUT>), grid, dim3(1024), 0, s, a);
+        else hipLaunchKernelGGL((k_grouped_gemv_bf16<16, 1, 2, OUT>), grid, dim3(1024), 0, s, a);
+    } else {
+        if (a.T <= 16) hipLaunchKernelGGL((k_grouped_gemv_bf16<8, 1, 1, OUT>), grid, dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((k_grouped_gemv_bf16<8, 1, 2, OUT>), grid, dim3(512), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Decode GEMV with the token rows staged in LDS, for the smallest T (every expert holds at most 16 tokens and
+// the T rows of K values fit kGemvLdsBytes). A workgroup owns 16 weight rows of one active expert, as in
+// k_grouped_gemv_bf16, but first copies its expert's ne token rows into LDS once (rows padded by 16 bytes, so
+// the 16 rows an MFMA operand read touches fall in 16 different bank slots); the K loop then streams only the
+// weight rows from HBM and reads the token fragments from LDS. This keeps fewer registers than holding both
+// operands' fragments in flight, so more workgroups stay resident (one round over the CUs for the T = 1
+// in-projection). GATED (out-projection): the staged rows are the gated rows bf16(SiLU(z) * h), computed here
+// with the gate pass's arithmetic, so that pass and its launch are skipped. The first batch of weight loads is
+// issued before the token rows arrive.
+
+// UL: staging loads per thread (at least T K / 8 / (64 NW), chosen at launch).
+template <int NW, int UL, bool OUT, bool GATED>
+__global__ __launch_bounds__(64 * NW) void k_grouped_gemv_lds(GemmArgs p) {
+    constexpr int NT = 64 * NW, U = 8;
+    extern __shared__ __attribute__((aligned(16))) uint16_t s_x[];  // [ne][K + 8] bf16
+    __shared__ float s_red[NW][16][16];
+    __shared__ int s_tok[16];
+    __shared__ float s_prob[16];
+    const int rb = blockIdx.x % p.n_tiles, rank = blockIdx.x / p.n_tiles;
+    int e = -1, o0 = 0, ne = 0;
+    for (int i = 0, j = 0; i < p.E; ++i) {
+        const int c = p.offsets[i + 1] - p.offsets[i];
+        if (c > 0) {
+            if (j == rank) { e = i; o0 = p.offsets[i]; ne = c; break; }
+            ++j;
+        }
+    }
+    if (e < 0) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nglob = rb * 16;  // N0 is a multiple of 64, so the 16 rows lie in one output
+    const int which = nglob / p.N0, n0 = nglob % p.N0;
+    const int K = p.K, pitch = K + 8;
+    const uint16_t *W = static_cast<const uint16_t *>(which ? p.B1 : p.B0) + ((size_t)e * p.N0 + n0) * K;
+    uint16_t *C = static_cast<uint16_t *>(which ? p.C1 : p.C0);
+
+    // the first batch of weight loads goes out first: K split over the waves in contiguous ranges
+    const int r = lane & 15, g = lane >> 4;
+    const uint16_t *wp = W + (size_t)r * K + g * 8;
+    const int nsteps = K / 32, spw = (nsteps + NW - 1) / NW;
+    const int sbeg = wave * spw, send = min(nsteps, sbeg + spw);
+    bf16x8 wf[U];
+    auto load_w = [&](int s0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) wf[u] = *reinterpret_cast<const bf16x8 *>(wp + min(s0 + u, max(send - 1, 0)) * 32);
+    };
+    // token rows: unit q of this thread is chunk (tid + q NT) of the ne x K/8 chunks, tokens read through perm
+    const int cpr = K / 8, units = ne * cpr;
+    u32x4 va[UL], vb[UL];
+    int tk[UL];
+#pragma unroll
+    for (int q = 0; q < UL; ++q) {
+        const int u = min(tid + q * NT, units - 1);  // clamped: in bounds
+        const int row = u / cpr, c = u - row * cpr;
+        tk[q] = p.perm[o0 + row];
+    }
+#pragma unroll
+    for (int q = 0; q < UL; ++q) {
+        const int u = min(tid + q * NT, units - 1);
+        const int row = u / cpr, c = u - row * cpr;
+        va[q] = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.A0) + (size_t)tk[q] * K)[c];
+        if (GATED) vb[q] = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.A1) + (size_t)tk[q] * K)[c];
+    }
+    if (sbeg < send) load_w(sbeg);
+    if (tid < 16) {
+        const int tok = p.perm[o0 + (tid < ne ? tid : 0)];
+        s_tok[tid] = tok;
+        s_prob[tid] = OUT ? p.prob[tok] : 1.0f;
+    }
+    // the token rows have landed once at most the U weight loads are still in flight
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(U));
+#pragma unroll
+    for (int q = 0; q < UL; ++q) {
+        const int u = tid + q * NT;
+        if (u < units) {
+            const int row = u / cpr, c = u - row * cpr;
+            u32x4 v = va[q];
+            if (GATED) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float z0 = __uint_as_float(va[q][i] << 16), z1 = __uint_as_float(va[q][i] & 0xFFFF0000u);
+                    const float h0 = __uint_as_float(vb[q][i] << 16), h1 = __uint_as_float(vb[q][i] & 0xFFFF0000u);
+                    v[i] = pack_bf16x2(silu_fast(z0) * h0, silu_fast(z1) * h1);
+                }
+            }
+            *reinterpret_cast<u32x4 *>(s_x + (size_t)row * pitch + c * 8) = v;
+        }
+    }
+    // LDS writes visible to the workgroup; the weight loads stay in flight (their results go to registers)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+    // token column r of the MFMA reads staged row r (rows past ne repeat row 0; their results are discarded)
+    const uint16_t *xrow = s_x + (size_t)(r < ne ? r : 0) * pitch + g * 8;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = sbeg; s0 < send; s0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (s0 + u < send) {  // uniform
+                const bf16x8 xf = *reinterpret_cast<const bf16x8 *>(xrow + (s0 + u) * 32);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], xf, acc, 0, 0, 0);
+            }
+        }
+        if (s0 + U < send) load_w(s0 + U);
+    }
+    // accumulator register i of lane l: weight row 4*(l/16) + i, token column l%16; waves added in order
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_red[wave][4 * g + i][r] = acc[i];
+    __syncthreads();
+    for (int idx = tid; idx < 256; idx += NT) {
+        const int n = idx >> 4, m = idx & 15;
+        if (m < ne) {
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) v += s_red[w][n][m];
+            uint16_t *dst = C + (size_t)s_tok[m] * p.N0 + n0 + n;
+            *dst = f32_to_bf16(p.accumulate ? fmaf(v, s_prob[m], bf16_to_f32(*dst)) : v * s_prob[m]);
+        }
+    }
+}
+
+template <int NW, int UL, bool OUT, bool GATED>
+static hipError_t launch_gemv_lds_n(const GemmArgs &a, long nwg, size_t smem, hipStream_t s) {
+    static LdsAttrOnce attr;
+    hipError_t err = set_lds_limit_once(
+        attr, reinterpret_cast<const void *>(&k_grouped_gemv_lds<NW, UL, OUT, GATED>), kGemvLdsBytes);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((k_grouped_gemv_lds<NW, UL, OUT, GATED>), dim3((unsigned)nwg), dim3(64 * NW), smem, s, a);
+    return hipGetLastError();
+}
+
+template <int NW, bool OUT, bool GATED>
+static hipError_t launch_gemv_lds_w(const GemmArgs &a, long nwg, size_t smem, hipStream_t s) {
+    // staging loads per thread: the chunks of the largest expert group (at most T rows of K / 8) over the threads
+    const long per = ((long)a.T * (a.K / 8) + 64 * NW - 1) / (64 * NW);
+    if (per <= 1) return launch_gemv_lds_n<NW, 1, OUT, GATED>(a, nwg, smem, s);
+    if (per <= 2) return launch_gemv_lds_n<NW, 2, OUT, GATED>(a, nwg, smem, s);
+    if (per <= 4) return launch_gemv_lds_n<NW, 4, OUT, GATED>(a, nwg, smem, s);
+    if (per <= 8) return launch_gemv_lds_n<NW, 8, OUT, GATED>(a, nwg, smem, s);
+    return hipErrorInvalidValue;  // excluded by gemv_lds_fits
+}
+
+template <bool OUT, bool GATED>
+static hipError_t launch_gemv_lds_t(const GemmArgs &a0, int nB, hipStream_t s) {
+    GemmArgs a = a0;
+    const int active = a.T < a.E ? a.T : a.E;
+    a.n_tiles = nB * a.N0 / 16;
+    a.n_tiles_per_b = a.N0 / 16;
+    const long nwg = (long)a.n_tiles * active;
+    const size_t smem = (size_t)a.T * (a.K + 8) * 2;
+    // at most one workgroup per compute unit: 16 waves (each streams half as many K steps), as for the
+    // register-staged kernels
+    if (nwg <= device_cus()) return launch_gemv_lds_w<16, OUT, GATED>(a, nwg, smem, s);
+    return launch_gemv_lds_w<8, OUT, GATED>(a, nwg, smem, s);
+}
+
+
+hipError_t launch_gemv_bf16(const GemmArgs &a, bool out, int nB, hipStream_t s) {
+    return out ? launch_gemv_t<true>(a, nB, s) : launch_gemv_t<false>(a, nB, s);
+}
+
+hipError_t launch_gemv_lds_bf16(const GemmArgs &a, bool out, bool gated, int nB, hipStream_t s) {
+    if (gated) return out ? launch_gemv_lds_t<true, true>(a, nB, s) : hipErrorInvalidValue;
+    return out ? launch_gemv_lds_t<true, false>(a, nB, s) : launch_gemv_lds_t<false, false>(a, nB, s);
+}
+
+}  // namespace rom
