@@ -131,10 +131,138 @@ __global__ __launch_bounds__(64 * NW) void k_grouped_gemv_bf16(GemmArgs p) {
     else gemv_block<NW, RB, 4, 4, OUT>(p, e, o0, ne, rb, s_red);
 }
 
+// Wide decode GEMV (17..64 tokens, enough output rows for a workgroup per CU): 16 waves, each owning 16 weight
+// rows over the whole K, so a workgroup covers 256 rows and reads its expert's token rows once per 256 rows
+// instead of once per 16 or 32 (the token re-reads had cost about 0.7 byte per weight byte). The token rows are
+// staged through LDS in chunks of kWideKC values of K, double-buffered: chunk c + 1 is loaded while chunk c's
+// MFMAs run, and one barrier per chunk hands the buffers over. Each wave streams its weight rows in batches of
+// 8 K-steps (4 with four token blocks, to stay within the registers of four waves per SIMD); no cross-wave
+// reduction is needed (a wave owns whole rows).
+constexpr int kWideKC = 512;
+constexpr int kWideRows = 256;
+constexpr size_t wide_lds_bytes(int nbmax) { return (size_t)2 * nbmax * 16 * (kWideKC + 8) * 2; }
+
+template <int NBMAX, bool OUT>
+__global__ __launch_bounds__(1024) void k_grouped_gemv_wide(GemmArgs p) {
+    constexpr int NT = 1024, U = NBMAX > 2 ? 4 : 8, NTOK = NBMAX * 16, TP = kWideKC + 8, CPR = kWideKC / 8;
+    constexpr int UQ = NTOK * CPR / NT;  // staging loads per thread and chunk
+    static_assert(UQ >= 1 && NTOK * CPR % NT == 0, "staging split");
+    extern __shared__ __attribute__((aligned(16))) uint16_t s_x[];  // [2][NTOK][TP]
+    __shared__ int s_tok[NTOK];
+    __shared__ float s_prob[NTOK];
+    const int rb = blockIdx.x % p.n_tiles, rank = blockIdx.x / p.n_tiles;
+    int e = -1, o0 = 0, ne = 0;
+    for (int i = 0, j = 0; i < p.E; ++i) {
+        const int c = p.offsets[i + 1] - p.offsets[i];
+        if (c > 0) {
+            if (j == rank) { e = i; o0 = p.offsets[i]; ne = c; break; }
+            ++j;
+        }
+    }
+    if (e < 0) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nglob = rb * kWideRows;  // N0 is a multiple of 256, so the rows lie in one output
+    const int which = nglob / p.N0, n0 = nglob % p.N0;
+    const int K = p.K;
+    const uint16_t *W = static_cast<const uint16_t *>(which ? p.B1 : p.B0) + ((size_t)e * p.N0 + n0) * K;
+    uint16_t *C = static_cast<uint16_t *>(which ? p.C1 : p.C0);
+    const uint16_t *A = static_cast<const uint16_t *>(p.A0);
+    if (tid < NTOK) {
+        const int tok = p.perm[o0 + min(tid, ne - 1)];  // rows past ne repeat the last token (discarded)
+        s_tok[tid] = tok;
+        s_prob[tid] = OUT ? p.prob[tok] : 1.0f;
+    }
+    __syncthreads();
+    const int nb = (ne + 15) >> 4;  // token blocks in use, uniform
+
+    u32x4 st[UQ];
+    auto stage_load = [&](int c) {
+#pragma unroll
+        for (int q = 0; q < UQ; ++q) {
+            const int u = tid + q * NT, row = u / CPR, cc = u % CPR;
+            st[q] = *reinterpret_cast<const u32x4 *>(A + (size_t)s_tok[row] * K + c * kWideKC + cc * 8);
+        }
+    };
+    auto stage_store = [&](int b) {
+#pragma unroll
+        for (int q = 0; q < UQ; ++q) {
+            const int u = tid + q * NT, row = u / CPR, cc = u % CPR;
+            *reinterpret_cast<u32x4 *>(s_x + ((size_t)b * NTOK + row) * TP + cc * 8) = st[q];
+        }
+    };
+    const int r = lane & 15, g = lane >> 4;
+    const uint16_t *wp = W + (size_t)(wave * 16 + r) * K + g * 8;
+    f32x4 acc[NBMAX];
+#pragma unroll
+    for (int bb = 0; bb < NBMAX; ++bb) acc[bb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    const int nchunks = K / kWideKC;
+    stage_load(0);
+    stage_store(0);
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+        const int b = c & 1;
+        if (c + 1 < nchunks) stage_load(c + 1);  // in flight during this chunk's MFMAs
+        const uint16_t *xs = s_x + (size_t)b * NTOK * TP + g * 8;
+#pragma unroll
+        for (int s0 = 0; s0 < kWideKC / 32; s0 += U) {
+            bf16x8 wf[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                wf[u] = *reinterpret_cast<const bf16x8 *>(wp + c * kWideKC + (s0 + u) * 32);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int bb = 0; bb < NBMAX; ++bb) {
+                    if (bb < nb) {  // uniform
+                        const bf16x8 xf = *reinterpret_cast<const bf16x8 *>(xs + (size_t)(bb * 16 + r) * TP + (s0 + u) * 32);
+                        acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], xf, acc[bb], 0, 0, 0);
+                    }
+                }
+        }
+        if (c + 1 < nchunks) stage_store(b ^ 1);  // buffer b ^ 1 was last read in the previous chunk
+        __syncthreads();
+    }
+    // accumulator register i of lane l: weight row 4*(l/16) + i of this wave's 16, token column l%16 of block bb
+#pragma unroll
+    for (int bb = 0; bb < NBMAX; ++bb) {
+        const int col = bb * 16 + r;
+        if (bb < nb && col < ne) {
+            const int tok = s_tok[col];
+            const float sc = s_prob[col];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint16_t *dst = C + (size_t)tok * p.N0 + n0 + wave * 16 + 4 * g + i;
+                *dst = f32_to_bf16(p.accumulate ? fmaf(acc[bb][i], sc, bf16_to_f32(*dst)) : acc[bb][i] * sc);
+            }
+        }
+    }
+}
+
+template <int NBMAX, bool OUT>
+static hipError_t launch_gemv_wide(const GemmArgs &a, long nwg, hipStream_t s) {
+    static LdsAttrOnce attr;
+    const size_t smem = wide_lds_bytes(NBMAX);
+    hipError_t err = set_lds_limit_once(attr, reinterpret_cast<const void *>(&k_grouped_gemv_wide<NBMAX, OUT>), smem);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((k_grouped_gemv_wide<NBMAX, OUT>), dim3((unsigned)nwg), dim3(1024), smem, s, a);
+    return hipGetLastError();
+}
+
 template <bool OUT>
 static hipError_t launch_gemv_t(const GemmArgs &a0, int nB, hipStream_t s) {
     GemmArgs a = a0;
     const int active = a.T < a.E ? a.T : a.E;
+    // 17..64 tokens with a workgroup of 256 rows for every compute unit: the wide kernel
+    if (a.T > 16 && a.N0 % kWideRows == 0 && a.K % kWideKC == 0) {
+        a.n_tiles = nB * a.N0 / kWideRows;
+        a.n_tiles_per_b = a.N0 / kWideRows;
+        const long nwg = (long)a.n_tiles * active;
+        if (nwg >= device_cus()) {
+            if (a.T <= 32) return launch_gemv_wide<2, OUT>(a, nwg, s);
+            return launch_gemv_wide<4, OUT>(a, nwg, s);
+        }
+    }
     // From 32 tokens on, 32 weight rows per workgroup (every workgroup reads all of its expert's token rows)
     const int rbk = a.T >= 32 ? 2 : 1;
     a.n_tiles = nB * a.N0 / (16 * rbk);

@@ -157,6 +157,24 @@ def test_all_tokens_on_one_expert(rom, oracle):
     assert gr["counts"][5] == w.T
 
 
+# The wide decode GEMV (17..64 tokens, 256-row workgroups, token rows staged through LDS in 512-value chunks):
+# 8 experts with 2 x 4096 in-projection rows give 256 workgroups; two and four token blocks, top-1 and top-2
+# (the second choice adds to the first), every token compared.
+WIDE = [
+    (workloads.custom_workload("wide_T32_E8", T=32, d_model=1024, d_inner=4096, E=8, seed=140), 1),
+    (workloads.custom_workload("wide_T50_E8", T=50, d_model=1024, d_inner=4096, E=8, seed=141), 1),
+    (workloads.custom_workload("wide_T32_E8_top2", T=32, d_model=512, d_inner=4096, E=8, seed=142), 2),
+]
+
+
+@pytest.mark.parametrize("w,k", WIDE, ids=[w.name for w, _ in WIDE])
+def test_decode_wide_gemv(rom, oracle, w, k):
+    if k == 1:
+        check_workload(rom, oracle, w)
+    else:
+        check_workload_top2(rom, oracle, w)
+
+
 @pytest.mark.parametrize("T,hot", [(40, 1), (64, 3), (64, None)])
 def test_decode_token_blocks(rom, oracle, T, hot):
     """Decode kernels: an expert holding 33..64 tokens takes the 3- and 4-block variants."""
