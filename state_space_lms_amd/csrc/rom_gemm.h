@@ -41,5 +41,9 @@ hipError_t launch_gemv_bf16(const GemmArgs &a, bool out, int nB, hipStream_t s);
 constexpr size_t kGemvLdsBytes = 64 * 1024;
 inline bool gemv_lds_fits(int T, int K) { return T <= 16 && (size_t)T * (K + 8) * 2 <= kGemvLdsBytes; }
 hipError_t launch_gemv_lds_bf16(const GemmArgs &a, bool out, bool gated, int nB, hipStream_t s);
+// Wide decode kernel: 16 waves over 64 to 256 weight rows, token rows (gathered through perm) staged through
+// LDS in K chunks. gemv_wide_fits: the shape suits it (enough rows for a workgroup per compute unit).
+bool gemv_wide_fits(int T, int E, int N0, int K, int nB);
+hipError_t launch_gemv_wide_bf16(const GemmArgs &a, bool out, int nB, hipStream_t s);
 
 }  // namespace rom

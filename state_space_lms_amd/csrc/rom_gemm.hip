@@ -789,6 +789,7 @@ hipError_t launch_in_proj(const void *X, const rom_routing &r, rom_dtype dt, int
         hipError_t err;
         if (dt == ROM_DTYPE_F32) err = launch_f32<false>(a, 2, s);
         else if (gemv_lds_fits(T, dm)) err = launch_gemv_lds_bf16(a, false, false, 2, s);
+        else if (gemv_wide_fits(T, r.E, di, dm, 2)) err = launch_gemv_wide_bf16(a, false, 2, s);
         else if (T <= kDecodeMaxT) err = launch_gemv_bf16(a, false, 2, s);
         else err = launch_bf16_auto<false>(a, 2, s);
         if (err != hipSuccess) return err;
@@ -836,6 +837,7 @@ hipError_t launch_out_proj(const void *z, const void *h, const rom_routing &r, r
         set_choice(a, r, T, k);
         hipError_t err;
         if (dt == ROM_DTYPE_F32) err = launch_f32<true>(a, 1, s);
+        else if (gemv_wide_fits(T, r.E, dm, di, 1)) err = launch_gemv_wide_bf16(a, true, 1, s);
         else if (T <= kDecodeMaxT) err = launch_gemv_bf16(a, true, 1, s);
         else err = launch_bf16_auto<true>(a, 1, s);
         if (err != hipSuccess) return err;
@@ -863,6 +865,7 @@ hipError_t launch_in_proj_weighted(const void *X, const rom_routing &r, rom_dtyp
         hipError_t err;
         if (dt == ROM_DTYPE_F32) err = launch_f32<true>(a, 1, s);
         else if (gemv_lds_fits(T, dm)) err = launch_gemv_lds_bf16(a, true, false, 1, s);
+        else if (gemv_wide_fits(T, r.E, dout, dm, 1)) err = launch_gemv_wide_bf16(a, true, 1, s);
         else if (T <= kDecodeMaxT) err = launch_gemv_bf16(a, true, 1, s);
         else err = launch_bf16_auto<true>(a, 1, s);
         if (err != hipSuccess) return err;

@@ -131,23 +131,37 @@ __global__ __launch_bounds__(64 * NW) void k_grouped_gemv_bf16(GemmArgs p) {
     else gemv_block<NW, RB, 4, 4, OUT>(p, e, o0, ne, rb, s_red);
 }
 
-// Wide decode GEMV (17..64 tokens, enough output rows for a workgroup per CU): 16 waves, each owning 16 weight
-// rows over the whole K, so a workgroup covers 256 rows and reads its expert's token rows once per 256 rows
-// instead of once per 16 or 32 (the token re-reads had cost about 0.7 byte per weight byte). The token rows are
-// staged through LDS in chunks of kWideKC values of K, double-buffered: chunk c + 1 is loaded while chunk c's
-// MFMAs run, and one barrier per chunk hands the buffers over. Each wave streams its weight rows in batches of
-// 8 K-steps (4 with four token blocks, to stay within the registers of four waves per SIMD); no cross-wave
-// reduction is needed (a wave owns whole rows).
+// Wide decode GEMV: 16 waves, each owning 16 weight rows of one active expert and a 1/KQ share of K (KQ = 1, 2
+// or 4 waves per row block), so a workgroup covers 256 / KQ rows and reads its expert's token rows once per
+// 256 / KQ rows instead of once per 16 or 32. The token rows (only the nb blocks of 16 in use) are staged
+// through LDS in chunks of 512 to 2048 values of K (the fewer blocks in use, the longer), double-buffered:
+// chunk c + 1 is loaded while chunk c's MFMAs run, and one barrier per chunk hands the buffers over. Each wave
+// streams its weight rows in batches of U K-steps with the next batch's loads in flight (two register
+// buffers), also across the chunk barriers, which wait only for LDS. With KQ > 1 the row block's KQ partial
+// sums are added through LDS in wave order (deterministic), then scaled and stored. For the out-projection
+// the rows are the gated rows the gate pass wrote in token order (gating them here instead, once per
+// workgroup, measured slower: every row block would repeat the SiLU of all of its expert's tokens).
 constexpr int kWideKC = 512;
-constexpr int kWideRows = 256;
+constexpr int kWideWaves = 16;
+constexpr int wide_rows(int kq) { return 16 * kWideWaves / kq; }
 constexpr size_t wide_lds_bytes(int nbmax) { return (size_t)2 * nbmax * 16 * (kWideKC + 8) * 2; }
 
-template <int NBMAX, bool OUT>
-__global__ __launch_bounds__(1024) void k_grouped_gemv_wide(GemmArgs p) {
-    constexpr int NT = 1024, U = NBMAX > 2 ? 4 : 8, NTOK = NBMAX * 16, TP = kWideKC + 8, CPR = kWideKC / 8;
-    constexpr int UQ = NTOK * CPR / NT;  // staging loads per thread and chunk
-    static_assert(UQ >= 1 && NTOK * CPR % NT == 0, "staging split");
-    extern __shared__ __attribute__((aligned(16))) uint16_t s_x[];  // [2][NTOK][TP]
+// Workgroup barrier that waits for this wave's LDS operations only: loads to registers stay in flight.
+__device__ __forceinline__ void barrier_lds_only() {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int NBMAX, int KQ, bool OUT>
+__global__ __launch_bounds__(64 * kWideWaves) void k_grouped_gemv_wide(GemmArgs p) {
+    constexpr int NT = 64 * kWideWaves, NTOK = NBMAX * 16, BUF = NTOK * (kWideKC + 8);
+    constexpr int SPW0 = kWideKC / 32 / KQ;                     // K-steps per wave in the smallest chunk
+    constexpr int UMAX = NBMAX > 2 ? 4 : 8, U = SPW0 < UMAX ? SPW0 : UMAX;
+    constexpr int UQ = NTOK * (kWideKC / 8) / NT;               // staging loads per thread and chunk (bound)
+    static_assert(SPW0 % U == 0 && UQ >= 1, "batches per chunk");
+    extern __shared__ __attribute__((aligned(16))) uint16_t s_x[];  // [2][BUF]; partial sums at the end
     __shared__ int s_tok[NTOK];
     __shared__ float s_prob[NTOK];
     const int rb = blockIdx.x % p.n_tiles, rank = blockIdx.x / p.n_tiles;
@@ -161,7 +175,8 @@ __global__ __launch_bounds__(1024) void k_grouped_gemv_wide(GemmArgs p) {
     }
     if (e < 0) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nglob = rb * kWideRows;  // N0 is a multiple of 256, so the rows lie in one output
+    const int wr = wave / KQ, kq = wave % KQ;  // row block of 16, share of K
+    const int nglob = rb * wide_rows(KQ);      // N0 is a multiple of the rows per workgroup: one output
     const int which = nglob / p.N0, n0 = nglob % p.N0;
     const int K = p.K;
     const uint16_t *W = static_cast<const uint16_t *>(which ? p.B1 : p.B0) + ((size_t)e * p.N0 + n0) * K;
@@ -173,96 +188,185 @@ __global__ __launch_bounds__(1024) void k_grouped_gemv_wide(GemmArgs p) {
         s_prob[tid] = OUT ? p.prob[tok] : 1.0f;
     }
     __syncthreads();
-    const int nb = (ne + 15) >> 4;  // token blocks in use, uniform
+    const int nb = (ne + 15) >> 4;        // token blocks in use, uniform
+    // chunk length: the LDS sized for NBMAX blocks of 512 values holds longer chunks of fewer blocks
+    // (fewer barriers per weight byte); the rows of a chunk are padded by 8 values (16 bytes), which puts
+    // the 16 rows of an MFMA operand read in 16 different bank slots
+    int mult = NBMAX / (nb <= 1 ? 1 : nb <= 2 ? 2 : 4);
+    while (mult > 1 && K % (kWideKC * mult) != 0) mult >>= 1;
+    const int KC = kWideKC * mult, TP = KC + 8, cpr_sh = __builtin_ctz(KC / 8);
+    const int SPW = KC / 32 / KQ, BPC = SPW / U;  // K-steps per wave and chunk; batches per chunk
+    const int units = nb * 16 * (KC / 8);         // staged 16-byte pieces per chunk (at most NTOK * 64)
 
     u32x4 st[UQ];
     auto stage_load = [&](int c) {
 #pragma unroll
         for (int q = 0; q < UQ; ++q) {
-            const int u = tid + q * NT, row = u / CPR, cc = u % CPR;
-            st[q] = *reinterpret_cast<const u32x4 *>(A + (size_t)s_tok[row] * K + c * kWideKC + cc * 8);
+            const int u = min(tid + q * NT, units - 1), row = u >> cpr_sh, cc = u & ((1 << cpr_sh) - 1);
+            const size_t off = (size_t)s_tok[row] * K + c * KC + cc * 8;  // u clamped: in bounds
+            st[q] = *reinterpret_cast<const u32x4 *>(A + off);
         }
     };
     auto stage_store = [&](int b) {
 #pragma unroll
         for (int q = 0; q < UQ; ++q) {
-            const int u = tid + q * NT, row = u / CPR, cc = u % CPR;
-            *reinterpret_cast<u32x4 *>(s_x + ((size_t)b * NTOK + row) * TP + cc * 8) = st[q];
+            const int u = tid + q * NT, row = u >> cpr_sh, cc = u & ((1 << cpr_sh) - 1);
+            if (u < units)
+                *reinterpret_cast<u32x4 *>(s_x + (size_t)b * BUF + row * TP + cc * 8) = st[q];
         }
     };
     const int r = lane & 15, g = lane >> 4;
-    const uint16_t *wp = W + (size_t)(wave * 16 + r) * K + g * 8;
+    const uint16_t *wp = W + (size_t)(wr * 16 + r) * K + g * 8 + kq * SPW * 32;
     f32x4 acc[NBMAX];
 #pragma unroll
     for (int bb = 0; bb < NBMAX; ++bb) acc[bb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    const int nchunks = K / kWideKC;
-    stage_load(0);
-    stage_store(0);
-    __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-        const int b = c & 1;
-        if (c + 1 < nchunks) stage_load(c + 1);  // in flight during this chunk's MFMAs
-        const uint16_t *xs = s_x + (size_t)b * NTOK * TP + g * 8;
+    const int nchunks = K / KC, nbatch = nchunks * BPC;
+    bf16x8 wa[U], wb[U];
+    auto wload = [&](bf16x8 (&w)[U], int bi) {
+        const int c = bi / BPC, j0 = (bi - c * BPC) * U;
+        const uint16_t *q = wp + c * KC + j0 * 32;
 #pragma unroll
-        for (int s0 = 0; s0 < kWideKC / 32; s0 += U) {
-            bf16x8 wf[U];
+        for (int u = 0; u < U; ++u) w[u] = *reinterpret_cast<const bf16x8 *>(q + u * 32);
+    };
+    auto compute = [&](const bf16x8 (&w)[U], int bi) {
+        const int c = bi / BPC, j0 = (bi - c * BPC) * U;
+        const uint16_t *xs = s_x + (size_t)(c & 1) * BUF + g * 8 + (kq * SPW + j0) * 32;
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                wf[u] = *reinterpret_cast<const bf16x8 *>(wp + c * kWideKC + (s0 + u) * 32);
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int bb = 0; bb < NBMAX; ++bb) {
-                    if (bb < nb) {  // uniform
-                        const bf16x8 xf = *reinterpret_cast<const bf16x8 *>(xs + (size_t)(bb * 16 + r) * TP + (s0 + u) * 32);
-                        acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], xf, acc[bb], 0, 0, 0);
-                    }
+            for (int bb = 0; bb < NBMAX; ++bb) {
+                if (bb < nb) {  // uniform
+                    const bf16x8 xf = *reinterpret_cast<const bf16x8 *>(xs + (size_t)(bb * 16 + r) * TP + u * 32);
+                    acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[u], xf, acc[bb], 0, 0, 0);
                 }
+            }
+    };
+    // chunk c + 1's token rows are loaded when chunk c begins and stored to the other buffer when it ends
+    auto chunk_begin = [&](int bi) {
+        if (bi % BPC == 0 && bi / BPC + 1 < nchunks) stage_load(bi / BPC + 1);
+    };
+    auto chunk_end = [&](int bi) {
+        if ((bi + 1) % BPC == 0 && bi / BPC + 1 < nchunks) {  // uniform
+            stage_store((bi / BPC + 1) & 1);  // that buffer was last read in the previous chunk
+            barrier_lds_only();
         }
-        if (c + 1 < nchunks) stage_store(b ^ 1);  // buffer b ^ 1 was last read in the previous chunk
-        __syncthreads();
+    };
+
+    stage_load(0);
+    wload(wa, 0);
+    stage_store(0);
+    barrier_lds_only();
+    for (int bi = 0; bi < nbatch; bi += 2) {
+        chunk_begin(bi);
+        if (bi + 1 < nbatch) wload(wb, bi + 1);
+        compute(wa, bi);
+        chunk_end(bi);
+        if (bi + 1 < nbatch) {
+            chunk_begin(bi + 1);
+            if (bi + 2 < nbatch) wload(wa, bi + 2);
+            compute(wb, bi + 1);
+            chunk_end(bi + 1);
+        }
     }
-    // accumulator register i of lane l: weight row 4*(l/16) + i of this wave's 16, token column l%16 of block bb
+    // accumulator register i of lane l: weight row 4*(l/16) + i of the row block, token column l%16 of block bb
+    if (KQ > 1) {
+        float *s_part = reinterpret_cast<float *>(s_x);  // [wave][bb][i][lane]; the staged rows are no longer read
+        __syncthreads();
+        if (kq > 0) {
 #pragma unroll
-    for (int bb = 0; bb < NBMAX; ++bb) {
-        const int col = bb * 16 + r;
-        if (bb < nb && col < ne) {
-            const int tok = s_tok[col];
-            const float sc = s_prob[col];
+            for (int bb = 0; bb < NBMAX; ++bb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint16_t *dst = C + (size_t)tok * p.N0 + n0 + wave * 16 + 4 * g + i;
-                *dst = f32_to_bf16(p.accumulate ? fmaf(acc[bb][i], sc, bf16_to_f32(*dst)) : acc[bb][i] * sc);
+                for (int i = 0; i < 4; ++i) s_part[((wave * NBMAX + bb) * 4 + i) * 64 + lane] = acc[bb][i];
+        }
+        __syncthreads();
+        if (kq == 0) {
+#pragma unroll
+            for (int q = 1; q < KQ; ++q)
+#pragma unroll
+                for (int bb = 0; bb < NBMAX; ++bb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[bb][i] += s_part[(((wave + q) * NBMAX + bb) * 4 + i) * 64 + lane];
+        }
+    }
+    if (kq == 0) {
+#pragma unroll
+        for (int bb = 0; bb < NBMAX; ++bb) {
+            const int col = bb * 16 + r;
+            if (bb < nb && col < ne) {
+                const int tok = s_tok[col];
+                const float sc = s_prob[col];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    uint16_t *dst = C + (size_t)tok * p.N0 + n0 + wr * 16 + 4 * g + i;
+                    *dst = f32_to_bf16(p.accumulate ? fmaf(acc[bb][i], sc, bf16_to_f32(*dst)) : acc[bb][i] * sc);
+                }
             }
         }
     }
 }
 
-template <int NBMAX, bool OUT>
-static hipError_t launch_gemv_wide(const GemmArgs &a, long nwg, hipStream_t s) {
+template <int NBMAX, int KQ, bool OUT>
+static hipError_t launch_wide_n(const GemmArgs &a, long nwg, hipStream_t s) {
     static LdsAttrOnce attr;
     const size_t smem = wide_lds_bytes(NBMAX);
-    hipError_t err = set_lds_limit_once(attr, reinterpret_cast<const void *>(&k_grouped_gemv_wide<NBMAX, OUT>), smem);
+    const void *fn = reinterpret_cast<const void *>(&k_grouped_gemv_wide<NBMAX, KQ, OUT>);
+    hipError_t err = set_lds_limit_once(attr, fn, smem);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((k_grouped_gemv_wide<NBMAX, OUT>), dim3((unsigned)nwg), dim3(1024), smem, s, a);
+    hipLaunchKernelGGL((k_grouped_gemv_wide<NBMAX, KQ, OUT>), dim3((unsigned)nwg), dim3(64 * kWideWaves), smem, s, a);
     return hipGetLastError();
+}
+
+template <int KQ, bool OUT>
+static hipError_t launch_wide_kq(const GemmArgs &a, long nwg, hipStream_t s) {
+    if (a.T <= 16) return launch_wide_n<1, KQ, OUT>(a, nwg, s);
+    if (a.T <= 32) return launch_wide_n<2, KQ, OUT>(a, nwg, s);
+    return launch_wide_n<4, KQ, OUT>(a, nwg, s);
+}
+
+// Waves per row block of the wide kernel: the fewest (1, 2 or 4) that give every compute unit a workgroup,
+// or 0 when the shape does not suit it (too few output rows, K not a multiple of the chunk, T outside
+// [wide_min_t, 64]).
+static int wide_min_t() {
+    static const int v = [] {
+        const char *s = getenv("ROM_WIDE_MIN_T");
+        const int x = s ? atoi(s) : 17;
+        return x < 1 ? 1 : x;
+    }();
+    return v;
+}
+static int wide_kq(int T, int E, int N0, int K, int nB) {
+    if (T < wide_min_t() || T > kDecodeMaxT || K % kWideKC != 0) return 0;
+    const long active = T < E ? T : E;
+    for (int kq = 1; kq <= 4; kq *= 2)
+        if (N0 % wide_rows(kq) == 0 && (long)nB * N0 / wide_rows(kq) * active >= device_cus()) return kq;
+    return 0;
+}
+
+bool gemv_wide_fits(int T, int E, int N0, int K, int nB) { return wide_kq(T, E, N0, K, nB) > 0; }
+
+template <bool OUT>
+static hipError_t launch_wide_t(const GemmArgs &a0, int nB, hipStream_t s) {
+    GemmArgs a = a0;
+    const int kq = wide_kq(a.T, a.E, a.N0, a.K, nB);
+    if (kq == 0) return hipErrorInvalidValue;
+    const int active = a.T < a.E ? a.T : a.E;
+    a.n_tiles = nB * a.N0 / wide_rows(kq);
+    a.n_tiles_per_b = a.N0 / wide_rows(kq);
+    const long nwg = (long)a.n_tiles * active;
+    if (kq == 1) return launch_wide_kq<1, OUT>(a, nwg, s);
+    if (kq == 2) return launch_wide_kq<2, OUT>(a, nwg, s);
+    return launch_wide_kq<4, OUT>(a, nwg, s);
+}
+
+hipError_t launch_gemv_wide_bf16(const GemmArgs &a, bool out, int nB, hipStream_t s) {
+    return out ? launch_wide_t<true>(a, nB, s) : launch_wide_t<false>(a, nB, s);
 }
 
 template <bool OUT>
 static hipError_t launch_gemv_t(const GemmArgs &a0, int nB, hipStream_t s) {
     GemmArgs a = a0;
     const int active = a.T < a.E ? a.T : a.E;
-    // 17..64 tokens with a workgroup of 256 rows for every compute unit: the wide kernel
-    if (a.T > 16 && a.N0 % kWideRows == 0 && a.K % kWideKC == 0) {
-        a.n_tiles = nB * a.N0 / kWideRows;
-        a.n_tiles_per_b = a.N0 / kWideRows;
-        const long nwg = (long)a.n_tiles * active;
-        if (nwg >= device_cus()) {
-            if (a.T <= 32) return launch_gemv_wide<2, OUT>(a, nwg, s);
-            return launch_gemv_wide<4, OUT>(a, nwg, s);
-        }
-    }
     // From 32 tokens on, 32 weight rows per workgroup (every workgroup reads all of its expert's token rows)
     const int rbk = a.T >= 32 ? 2 : 1;
     a.n_tiles = nB * a.N0 / (16 * rbk);

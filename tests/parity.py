@@ -232,6 +232,26 @@ def gemm_row_tiles(T: int, N0: int, nB: int, E: int, dtype: str, cus: int = 256)
     return (128, 64)
 
 
+WIDE_KC = 512        # K values per staged chunk of the wide decode kernel
+WIDE_MIN_T = 17      # fewest tokens for which the launcher considers the wide decode kernel
+
+
+def wide_kq(T: int, E: int, N0: int, K: int, nB: int, cus: int = 256, min_t: int = WIDE_MIN_T) -> int:
+    """Waves per 16-row block (1, 2 or 4; rows per workgroup 256 / kq) of the wide decode kernel that the
+    library launches for T tokens, N0 output rows per weight stack, nB stacks, K inputs and E experts, or 0
+    when it takes another kernel. Mirrors the launcher: T in [min_t, 64], K a multiple of the chunk, and the
+    fewest waves per row block whose workgroups (one per 256 / kq rows of every active expert) cover the
+    compute units."""
+    if T < min_t or T > 64 or K % WIDE_KC:
+        return 0
+    active = min(T, E)
+    for kq in (1, 2, 4):
+        rows = 256 // kq
+        if N0 % rows == 0 and nB * N0 // rows * active >= cus:
+            return kq
+    return 0
+
+
 def sample_rows(orc_sorts, T, tiles=((64, 32), (128, 64), (256, 128)), n_random=192, seed=0) -> np.ndarray:
     """Tokens to check at full size: for every routing choice (one oracle grouping per choice), the first two
     and last two slots of every expert group and of every M-tile the GEMMs launch in it, the slots on both

@@ -157,22 +157,48 @@ def test_all_tokens_on_one_expert(rom, oracle):
     assert gr["counts"][5] == w.T
 
 
-# The wide decode GEMV (17..64 tokens, 256-row workgroups, token rows staged through LDS in 512-value chunks):
-# 8 experts with 2 x 4096 in-projection rows give 256 workgroups; two and four token blocks, top-1 and top-2
-# (the second choice adds to the first), every token compared.
+# The wide decode GEMV (17..64 tokens, 64- to 256-row workgroups of 16 waves, token rows staged through LDS in
+# chunks of 512 to 2048 values): every token compared. Each case names the waves per 16-row block (K split 1, 2
+# or 4 ways) that its in- and out-projection take (0: another kernel), checked against the launcher's rule: one
+# and several chunks, one to four token blocks, top-1 and top-2 (the second choice adds to the first), the
+# out-projection (on the gated rows) with K split 2 and 4 ways.
 WIDE = [
-    (workloads.custom_workload("wide_T32_E8", T=32, d_model=1024, d_inner=4096, E=8, seed=140), 1),
-    (workloads.custom_workload("wide_T50_E8", T=50, d_model=1024, d_inner=4096, E=8, seed=141), 1),
-    (workloads.custom_workload("wide_T32_E8_top2", T=32, d_model=512, d_inner=4096, E=8, seed=142), 2),
+    # name, T, d_model, d_inner, E, seed, top_k, (in kq, out kq)
+    ("wide_T32_E8", 32, 1024, 4096, 8, 140, 1, (1, 0)),
+    ("wide_T50_E8", 50, 1024, 4096, 8, 141, 1, (1, 0)),
+    ("wide_T32_E8_top2", 32, 512, 4096, 8, 142, 2, (1, 0)),
+    ("wide_kq4_T40", 40, 2048, 1024, 8, 143, 1, (4, 4)),
+    ("wide_kq4_T40_top2", 40, 2048, 1024, 8, 144, 2, (4, 4)),
+    ("wide_kq2_out_T20_one_chunk", 20, 4096, 512, 8, 145, 1, (0, 2)),
+    ("wide_kq2_T24", 24, 1024, 2048, 8, 146, 1, (2, 0)),
 ]
 
 
-@pytest.mark.parametrize("w,k", WIDE, ids=[w.name for w, _ in WIDE])
-def test_decode_wide_gemv(rom, oracle, w, k):
+@pytest.mark.parametrize("case", WIDE, ids=[c[0] for c in WIDE])
+def test_decode_wide_gemv(rom, oracle, case):
+    name, T, dm, di, E, seed, k, (kq_in, kq_out) = case
+    assert parity.wide_kq(T, E, di, dm, 2) == kq_in and parity.wide_kq(T, E, dm, di, 1) == kq_out, \
+        "the case no longer selects the intended wide-kernel variant"
+    w = workloads.custom_workload(name, T=T, d_model=dm, d_inner=di, E=E, seed=seed)
     if k == 1:
         check_workload(rom, oracle, w)
     else:
         check_workload_top2(rom, oracle, w)
+
+
+WIDE_HOT_BIAS = 1.5  # with seed 147: 42 of the 64 tokens on expert 6, every expert active (oracle router)
+
+
+def test_decode_wide_gemv_full_expert(rom, oracle):
+    """Wide kernel (K split 4 ways) with one expert holding 33..64 tokens (three token blocks) while all eight
+    experts stay active."""
+    w = workloads.custom_workload("wide_kq4_hot_T64", T=64, d_model=2048, d_inner=1024, E=8, seed=147)
+    assert parity.wide_kq(64, 8, 1024, 2048, 2) == 4 and parity.wide_kq(64, 8, 2048, 1024, 1) == 4
+    bias = np.zeros(8, np.float32)
+    bias[6] = WIDE_HOT_BIAS
+    inp = workloads.make_inputs(w, router_bias=bias)
+    _, gr, _, _ = check_workload(rom, oracle, w, inp, label="wide kernel, expert 6 hot")
+    assert gr["counts"][6] > 32 and np.all(gr["counts"] > 0)
 
 
 @pytest.mark.parametrize("T,hot", [(40, 1), (64, 3), (64, None)])
