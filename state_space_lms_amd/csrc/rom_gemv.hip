@@ -399,6 +399,51 @@ static hipError_t launch_gemv_t(const GemmArgs &a0, int nB, hipStream_t s) {
 // with the gate pass's arithmetic, so that pass and its launch are skipped. The first batch of weight loads is
 // issued before the token rows arrive.
 
+// K-steps [s0, s0 + U) of a wave's weight rows (wp: this lane's row and 8-element group); steps past send
+// repeat the last one, so every load is in bounds.
+template <int U>
+__device__ __forceinline__ void gemv_load_w(bf16x8 (&wf)[U], const uint16_t *wp, int s0, int send) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) wf[u] = *reinterpret_cast<const bf16x8 *>(wp + min(s0 + u, max(send - 1, 0)) * 32);
+}
+
+// The K loop, wave reduction and store of the LDS-staged decode GEMV. The wave owns K-steps [sbeg, send) of the
+// workgroup's 16 weight rows, whose first batch is already in wf; xrow is this lane's staged token row (token
+// column lane % 16). The waves' partial sums are added in wave order through s_red (deterministic), scaled by
+// s_prob[m] and written to row s_tok[m], columns n0 .. n0 + 15 of C, for the token columns m < ne.
+template <int NW, int U>
+__device__ __forceinline__ void gemv_lds_tail(const GemmArgs &p, const uint16_t *wp, int sbeg, int send,
+                                              bf16x8 (&wf)[U], const uint16_t *xrow, int ne, const int *s_tok,
+                                              const float *s_prob, float (*s_red)[16][16], uint16_t *C, int n0) {
+    constexpr int NT = 64 * NW;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, g = lane >> 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = sbeg; s0 < send; s0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (s0 + u < send) {  // uniform
+                const bf16x8 xf = *reinterpret_cast<const bf16x8 *>(xrow + (s0 + u) * 32);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], xf, acc, 0, 0, 0);
+            }
+        }
+        if (s0 + U < send) gemv_load_w<U>(wf, wp, s0 + U, send);
+    }
+    // accumulator register i of lane l: weight row 4*(l/16) + i, token column l%16; waves added in order
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_red[wave][4 * g + i][r] = acc[i];
+    __syncthreads();
+    for (int idx = tid; idx < 256; idx += NT) {
+        const int n = idx >> 4, m = idx & 15;
+        if (m < ne) {
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) v += s_red[w][n][m];
+            uint16_t *dst = C + (size_t)s_tok[m] * p.N0 + n0 + n;
+            *dst = f32_to_bf16(p.accumulate ? fmaf(v, s_prob[m], bf16_to_f32(*dst)) : v * s_prob[m]);
+        }
+    }
+}
+
 // UL: staging loads per thread (at least T K / 8 / (64 NW), chosen at launch).
 template <int NW, int UL, bool OUT, bool GATED>
 __global__ __launch_bounds__(64 * NW) void k_grouped_gemv_lds(GemmArgs p) {
@@ -430,10 +475,6 @@ __global__ __launch_bounds__(64 * NW) void k_grouped_gemv_lds(GemmArgs p) {
     const int nsteps = K / 32, spw = (nsteps + NW - 1) / NW;
     const int sbeg = wave * spw, send = min(nsteps, sbeg + spw);
     bf16x8 wf[U];
-    auto load_w = [&](int s0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) wf[u] = *reinterpret_cast<const bf16x8 *>(wp + min(s0 + u, max(send - 1, 0)) * 32);
-    };
     // token rows: unit q of this thread is chunk (tid + q NT) of the ne x K/8 chunks, tokens read through perm
     const int cpr = K / 8, units = ne * cpr;
     u32x4 va[UL], vb[UL];
@@ -451,7 +492,7 @@ __global__ __launch_bounds__(64 * NW) void k_grouped_gemv_lds(GemmArgs p) {
         va[q] = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.A0) + (size_t)tk[q] * K)[c];
         if (GATED) vb[q] = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.A1) + (size_t)tk[q] * K)[c];
     }
-    if (sbeg < send) load_w(sbeg);
+    if (sbeg < send) gemv_load_w<U>(wf, wp, sbeg, send);
     if (tid < 16) {
         const int tok = p.perm[o0 + (tid < ne ? tid : 0)];
         s_tok[tid] = tok;
@@ -477,38 +518,11 @@ __global__ __launch_bounds__(64 * NW) void k_grouped_gemv_lds(GemmArgs p) {
         }
     }
     // LDS writes visible to the workgroup; the weight loads stay in flight (their results go to registers)
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    barrier_lds_only();
 
     // token column r of the MFMA reads staged row r (rows past ne repeat row 0; their results are discarded)
     const uint16_t *xrow = s_x + (size_t)(r < ne ? r : 0) * pitch + g * 8;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = sbeg; s0 < send; s0 += U) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (s0 + u < send) {  // uniform
-                const bf16x8 xf = *reinterpret_cast<const bf16x8 *>(xrow + (s0 + u) * 32);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u], xf, acc, 0, 0, 0);
-            }
-        }
-        if (s0 + U < send) load_w(s0 + U);
-    }
-    // accumulator register i of lane l: weight row 4*(l/16) + i, token column l%16; waves added in order
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_red[wave][4 * g + i][r] = acc[i];
-    __syncthreads();
-    for (int idx = tid; idx < 256; idx += NT) {
-        const int n = idx >> 4, m = idx & 15;
-        if (m < ne) {
-            float v = 0.0f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) v += s_red[w][n][m];
-            uint16_t *dst = C + (size_t)s_tok[m] * p.N0 + n0 + n;
-            *dst = f32_to_bf16(p.accumulate ? fmaf(v, s_prob[m], bf16_to_f32(*dst)) : v * s_prob[m]);
-        }
-    }
+    gemv_lds_tail<NW, U>(p, wp, sbeg, send, wf, xrow, ne, s_tok, s_prob, s_red, C, n0);
 }
 
 template <int NW, int UL, bool OUT, bool GATED>
@@ -545,6 +559,7 @@ static hipError_t launch_gemv_lds_t(const GemmArgs &a0, int nB, hipStream_t s) {
     if (nwg <= device_cus()) return launch_gemv_lds_w<16, OUT, GATED>(a, nwg, smem, s);
     return launch_gemv_lds_w<8, OUT, GATED>(a, nwg, smem, s);
 }
+
 
 
 hipError_t launch_gemv_bf16(const GemmArgs &a, bool out, int nB, hipStream_t s) {

@@ -266,6 +266,53 @@ def test_deterministic_and_permute(rom, oracle):
         np.testing.assert_array_equal(parity.to_host(a["r"].x_perm), oracle.permute(inp["X"], o_sort["perm"]))
 
 
+# The one- and two-token router (bf16, at most 8 experts: one workgroup, a butterfly over the lanes): top-1 and
+# top-2, d_model below and above one chunk per thread (64, 8192), E not a multiple of 4 (scalar W_r loads), one
+# expert, a router bias, the materialised permute, and exact ties.
+TINY_ROUTE = [
+    # name, T, d_model, d_inner, E, seed, top_k
+    ("tiny_T2_E8", 2, 512, 256, 8, 180, 1),
+    ("tiny_T2_E8_dm8192_top2", 2, 8192, 128, 8, 181, 2),
+    ("tiny_T1_E6_top2", 1, 1024, 192, 6, 182, 2),
+    ("tiny_T2_E3_dm64", 2, 64, 64, 3, 183, 1),
+    ("tiny_T1_E1", 1, 256, 128, 1, 184, 1),
+]
+
+
+@pytest.mark.parametrize("case", TINY_ROUTE, ids=[c[0] for c in TINY_ROUTE])
+def test_tiny_router(rom, oracle, case):
+    name, T, dm, di, E, seed, k = case
+    w = workloads.custom_workload(name, T=T, d_model=dm, d_inner=di, E=E, seed=seed)
+    if k == 1:
+        _, gr, _, _ = check_workload(rom, oracle, w)
+        if E == 1:
+            assert np.all(gr["prob"] == 1.0)
+    else:
+        check_workload_top2(rom, oracle, w)
+
+
+def test_tiny_router_bias_permute_and_ties(rom, oracle):
+    """Two tokens: a bias that moves the choice, the permute (X[perm] exactly), and W_router = 0 (expert 0,
+    p = 1/E exactly; top-2 picks experts 0 and 1)."""
+    w = workloads.custom_workload("tiny_bias_T2", T=2, d_model=256, d_inner=128, E=8, seed=185)
+    bias = np.zeros(8, np.float32)
+    bias[5] = 50.0
+    inp = workloads.make_inputs(w, router_bias=bias)
+    _, gr, _, _ = check_workload(rom, oracle, w, inp, label="tiny router with bias")
+    assert np.all(gr["expert_id"] == 5)
+    g = _run_chain(rom, w, inp, permute=True, isolated=False)
+    perm = parity.to_host(g["r"].perm)[0]
+    np.testing.assert_array_equal(parity.to_host(g["r"].x_perm), inp["X"][perm])
+    inp["W_router"] = np.zeros_like(inp["W_router"])
+    inp["bias"] = None
+    g = _run_chain(rom, w, inp, isolated=False)
+    gr = _route_host(g["r"])
+    assert np.all(gr["expert_id"] == 0) and np.all(gr["prob"] == np.float32(0.125))
+    g2 = _run_chain(rom, w, inp, isolated=False, top_k=2)
+    gr2 = _route_host(g2["r"])
+    assert np.all(gr2["expert_id"][0] == 0) and np.all(gr2["expert_id"][1] == 1)
+
+
 def test_zero_tokens(rom):
     import torch
     X = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
