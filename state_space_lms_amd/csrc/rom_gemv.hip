@@ -221,16 +221,26 @@ __global__ __launch_bounds__(64 * kWideWaves) void k_grouped_gemv_wide(GemmArgs 
 #pragma unroll
     for (int bb = 0; bb < NBMAX; ++bb) acc[bb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
+    // Staggered K order (KQ = 1). All 16 waves of every workgroup would read their rows at the same K offset
+    // at the same time, and rows and workgroups lie power-of-two distances apart, so the concurrent requests
+    // would share their low address bits and crowd a few memory channels (Swimba decode_T64's in-projection:
+    // 127 us; staggered: 102 us). So each workgroup takes its chunks starting at chunk (blockIdx mod nchunks),
+    // and inside a chunk each wave takes its batches starting at batch (wave mod BPC); a row's sum still runs
+    // in a fixed order (deterministic). With KQ > 1 the waves' K shares already spread the requests (staggering
+    // them as well measured slower, decode_T64's out-projection 60 -> 67 us).
     const int nchunks = K / KC, nbatch = nchunks * BPC;
+    const int crot = KQ == 1 ? (int)(blockIdx.x % (unsigned)nchunks) : 0, brot = KQ == 1 ? wave % BPC : 0;
+    auto chunk_at = [&](int c) { return c + crot < nchunks ? c + crot : c + crot - nchunks; };
+    auto batch_at = [&](int j) { return j + brot < BPC ? j + brot : j + brot - BPC; };
     bf16x8 wa[U], wb[U];
     auto wload = [&](bf16x8 (&w)[U], int bi) {
-        const int c = bi / BPC, j0 = (bi - c * BPC) * U;
-        const uint16_t *q = wp + c * KC + j0 * 32;
+        const int c = bi / BPC, j0 = batch_at(bi - c * BPC) * U;
+        const uint16_t *q = wp + chunk_at(c) * KC + j0 * 32;
 #pragma unroll
         for (int u = 0; u < U; ++u) w[u] = *reinterpret_cast<const bf16x8 *>(q + u * 32);
     };
     auto compute = [&](const bf16x8 (&w)[U], int bi) {
-        const int c = bi / BPC, j0 = (bi - c * BPC) * U;
+        const int c = bi / BPC, j0 = batch_at(bi - c * BPC) * U;
         const uint16_t *xs = s_x + (size_t)(c & 1) * BUF + g * 8 + (kq * SPW + j0) * 32;
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -244,7 +254,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void k_grouped_gemv_wide(GemmArgs 
     };
     // chunk c + 1's token rows are loaded when chunk c begins and stored to the other buffer when it ends
     auto chunk_begin = [&](int bi) {
-        if (bi % BPC == 0 && bi / BPC + 1 < nchunks) stage_load(bi / BPC + 1);
+        if (bi % BPC == 0 && bi / BPC + 1 < nchunks) stage_load(chunk_at(bi / BPC + 1));
     };
     auto chunk_end = [&](int bi) {
         if ((bi + 1) % BPC == 0 && bi / BPC + 1 < nchunks) {  // uniform
@@ -253,7 +263,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void k_grouped_gemv_wide(GemmArgs 
         }
     };
 
-    stage_load(0);
+    stage_load(chunk_at(0));
     wload(wa, 0);
     stage_store(0);
     barrier_lds_only();
