@@ -3,8 +3,11 @@
 // Method: Routing Mamba landing page (chapterpal.com), Knowl 1: the same expert products as rom_gemm.hip
 // (x = W_conv[e] X, z = W_gate[e] X; out = p W_out[e] (SiLU(z) * h); Swimba's y = p W_in[e] X). With a few
 // tokens per expert the cost is streaming each active expert's weights from HBM once: these kernels give every
-// workgroup 16 (or 32) weight rows of one active expert and all of that expert's tokens, and use 16x16x32
-// MFMAs only to apply each weight fragment to up to 16 tokens at once.
+// workgroup 16 to 256 weight rows of one active expert and all of that expert's tokens, and use 16x16x32
+// MFMAs only to apply each weight fragment to up to 16 tokens at once. Three kernels: k_grouped_gemv_bf16
+// (both operands' fragments from memory into registers), k_grouped_gemv_lds (the smallest T: the token rows
+// staged in LDS once, the out-projection's gate computed there), k_grouped_gemv_wide (17..64 tokens: 16 waves
+// over up to 256 rows, the token rows staged through LDS in K chunks).
 #include "rom_device.h"
 #include "rom_gemm.h"
 #include "rom_internal.h"
