@@ -410,7 +410,9 @@ static hipError_t launch_gemv_t(const GemmArgs &a0, int nB, hipStream_t s) {
 // operands' fragments in flight, so more workgroups stay resident (one round over the CUs for the T = 1
 // in-projection). GATED (out-projection): the staged rows are the gated rows bf16(SiLU(z) * h), computed here
 // with the gate pass's arithmetic, so that pass and its launch are skipped. The first batch of weight loads is
-// issued before the token rows arrive.
+// issued before the token rows arrive: ungated, even before the perm loads, since the weight rows depend only
+// on the expert (T = 1 in-projection, 16384 rows of 4096: 26.4 -> 26.1 us); gated, right after the token-row
+// loads, which the gate needs first.
 
 // K-steps [s0, s0 + U) of a wave's weight rows (wp: this lane's row and 8-element group); steps past send
 // repeat the last one, so every load is in bounds.
@@ -488,6 +490,8 @@ __global__ __launch_bounds__(64 * NW) void k_grouped_gemv_lds(GemmArgs p) {
     const int nsteps = K / 32, spw = (nsteps + NW - 1) / NW;
     const int sbeg = wave * spw, send = min(nsteps, sbeg + spw);
     bf16x8 wf[U];
+    // ungated: the weight rows do not depend on perm, so their first batch goes out before the perm loads
+    if (!GATED && sbeg < send) gemv_load_w<U>(wf, wp, sbeg, send);
     // token rows: unit q of this thread is chunk (tid + q NT) of the ne x K/8 chunks, tokens read through perm
     const int cpr = K / 8, units = ne * cpr;
     u32x4 va[UL], vb[UL];
@@ -505,14 +509,15 @@ __global__ __launch_bounds__(64 * NW) void k_grouped_gemv_lds(GemmArgs p) {
         va[q] = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.A0) + (size_t)tk[q] * K)[c];
         if (GATED) vb[q] = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.A1) + (size_t)tk[q] * K)[c];
     }
-    if (sbeg < send) gemv_load_w<U>(wf, wp, sbeg, send);
+    if (GATED && sbeg < send) gemv_load_w<U>(wf, wp, sbeg, send);
     if (tid < 16) {
         const int tok = p.perm[o0 + (tid < ne ? tid : 0)];
         s_tok[tid] = tok;
         s_prob[tid] = OUT ? p.prob[tok] : 1.0f;
     }
-    // the token rows have landed once at most the U weight loads are still in flight
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(U));
+    // gated: the token rows have landed once at most the U weight loads (issued after them) are in flight;
+    // ungated: the weight batch went out first, so every load is waited for
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(GATED ? U : 0));
 #pragma unroll
     for (int q = 0; q < UL; ++q) {
         const int u = tid + q * NT;
