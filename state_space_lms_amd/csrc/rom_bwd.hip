@@ -296,28 +296,108 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_wgrad_gemm_bf16(WgradArgs p)
     for (int j = 0; j < FN; ++j) b_frag[j] = BM * BK + (wn * WN + j * 32 + (lane & 31)) * BK;
     const int swz = lds_swz<KCH>(lane & 31);
 
-    if (nk > 0) issue_copies(0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-        const int stage = kt & 1;
-        wait_copies<PER_STEP, 0>(0);
+    // The K loop over the expert's column range (nk steps; none for an expert without tokens, which stores zeros).
+    // Tiles with more MFMA blocks per wave than fragment reads per sub-step take the forward grouped GEMM's
+    // early-barrier schedule: a wave joins each step's barrier once its fragment reads and the step's copies are
+    // done, then issues the next step's copies into the stage just read and the first fragment reads of the next
+    // step, and only then the step's last MFMAs, which cover those reads; within a step, the next sub-step's
+    // fragment reads are slotted between the MFMAs. Copies run one step ahead, and the last step copies its own
+    // data again into the free stage (never read), so every barrier sees the same count of copies in flight
+    // (T = 65536, E = 8, d_inner 4096, loads 60% to 2%: in-projection backward 4.85 -> 4.75 ms). The 64 x 64 tile
+    // keeps the plain loop: wait, barrier, issue the next copies, then the step's reads and MFMAs.
+    constexpr int NR = FM + FN, NM = FM * FN, NG = (NR + 1) / 2;  // reads, MFMAs, MFMAs with reads after them
+    constexpr int NKK = BK / 16;                                   // MFMA sub-steps per K step
+    auto barrier = [&]() {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_barrier();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (kt + 1 < nk) issue_copies(kt + 1, stage ^ 1);
-        const uint16_t *st = smem + stage * STAGE;
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
+    };
+    if constexpr (NM > NG) {
+        bf16x8 af[2][FM], bfr[2][FN];
+        auto load_frags = [&](int stg, int kk, int set) {
+            const uint16_t *st = smem + stg * STAGE;
             const int co = ((kk * 2 + half) ^ swz) * 8;
-            bf16x8 af[FM], bfr[FN];
 #pragma unroll
-            for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8 *>(st + a_frag[i] + co);
+            for (int i = 0; i < FM; ++i) af[set][i] = *reinterpret_cast<const bf16x8 *>(st + a_frag[i] + co);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8 *>(st + b_frag[j] + co);
+            for (int j = 0; j < FN; ++j) bfr[set][j] = *reinterpret_cast<const bf16x8 *>(st + b_frag[j] + co);
+        };
+        auto mfmas = [&](int set) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[set][j], af[set][i], acc[i][j], 0, 0, 0);
+        };
+        // issue order of one sub-step: an MFMA, two fragment reads of the next sub-step, ..., the remaining MFMAs
+        auto slot_reads = [&]() {
+#pragma unroll
+            for (int q = 0; q < NR / 2; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            if constexpr (NR % 2 == 1) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NM - NG, 0);
+        };
+        // sub-steps 0 .. NKK-2 of the step in stage stg, each with the next sub-step's reads
+        auto body = [&](int stg) {
+#pragma unroll
+            for (int kk = 1; kk < NKK; ++kk) {
+                load_frags(stg, kk, kk & 1);
+                mfmas((kk - 1) & 1);
+            }
+#pragma unroll
+            for (int kk = 1; kk < NKK; ++kk) slot_reads();
+        };
+        if (nk > 0) {  // uniform
+            issue_copies(0, 0);
+            wait_copies<PER_STEP, 0>(0);
+            barrier();
+            issue_copies(min(1, nk - 1), 1);
+            load_frags(0, 0, 0);
+            int stage = 0;
+            for (int kt = 0; kt + 1 < nk; ++kt) {
+                body(stage);
+                __builtin_amdgcn_sched_barrier(0);  // the step's MFMAs stay ahead of the wait
+                wait_copies<PER_STEP, 0>(0);
+                barrier();
+                issue_copies(min(kt + 2, nk - 1), stage);
+                const int next = stage ^ 1;
+                load_frags(next, 0, 0);
+                mfmas((NKK - 1) & 1);
+                __builtin_amdgcn_sched_group_barrier(0x020, PER_STEP, 0);
+                slot_reads();
+                stage = next;
+            }
+            body(stage);
+            mfmas((NKK - 1) & 1);
+            wait_copies<PER_STEP, 0>(0);  // the spare copies
+        }
+    } else {
+        if (nk > 0) issue_copies(0, 0);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int stage = kt & 1;
+            wait_copies<PER_STEP, 0>(0);
+            barrier();
+            if (kt + 1 < nk) issue_copies(kt + 1, stage ^ 1);
+            const uint16_t *st = smem + stage * STAGE;
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const int co = ((kk * 2 + half) ^ swz) * 8;
+                bf16x8 af[FM], bfr[FN];
+#pragma unroll
+                for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8 *>(st + a_frag[i] + co);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8 *>(st + b_frag[j] + co);
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+            }
         }
     }
     // C^T layout: register r of block (i, j) holds column 8*(r/4) + 4*half + r%4 of row lane%32
