@@ -664,3 +664,15 @@ def test_backward_full_samba_shape(rom, oracle, top_k):
     tiles = [parity.gemm_row_tiles(w.T, w.d_inner, 1, w.E, w.dtype), parity.gemm_row_tiles(w.T, w.d_model, 1, w.E, w.dtype)]
     rows = parity.sample_rows(_choice_sorts(oracle, o_route["ids"], w.E), w.T, tiles=tiles, n_random=96)
     check_backward(rom, oracle, w, top_k=top_k, inp=inp, rows=rows, n_entries=600, label=f"samba421m top-{top_k}")
+
+
+def test_backward_full_skewed_shape(rom, oracle):
+    """The skewed block (T = 65536, d_model 2048, d_inner 4096, 60% of the tokens on expert 0) at its full size:
+    sampled token rows at the tile boundaries of both data-gradient GEMMs, and sampled weight-gradient entries of
+    every expert, expert 0's 613 K steps included."""
+    w = workloads.get_workload("skewed")
+    inp = workloads.make_inputs(w, which={"X", "W_router", "W_conv", "W_gate", "W_out", "h", "z"})
+    o_route = oracle.route(inp["X"], inp["W_router"], inp.get("bias"))
+    tiles = [parity.gemm_row_tiles(w.T, w.d_inner, 1, w.E, w.dtype), parity.gemm_row_tiles(w.T, w.d_model, 1, w.E, w.dtype)]
+    rows = parity.sample_rows(_choice_sorts(oracle, o_route["ids"], w.E), w.T, tiles=tiles, n_random=64)
+    check_backward(rom, oracle, w, inp=inp, rows=rows, n_entries=600, label="skewed top-1")
