@@ -224,7 +224,7 @@ struct WgradArgs {
 
 template <int BM, int BN, int WGM, int WGN>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_wgrad_gemm_bf16(WgradArgs p) {
-    constexpr int BK = 64, NSTAGE = 2;
+    constexpr int BK = 64;  // two LDS stages (stage ^ 1 below)
     constexpr int NW = WGM * WGN, KCH = BK / 8, RG = 64 / KCH;
     constexpr int A_DMA = BM / RG / NW, B_DMA = BN / RG / NW, PER_STEP = A_DMA + B_DMA;
     constexpr int STAGE = (BM + BN) * BK;
