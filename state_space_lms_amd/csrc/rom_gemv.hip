@@ -161,7 +161,9 @@ template <int NBMAX, int KQ, bool OUT>
 __global__ __launch_bounds__(64 * kWideWaves) void k_grouped_gemv_wide(GemmArgs p) {
     constexpr int NT = 64 * kWideWaves, NTOK = NBMAX * 16, BUF = NTOK * (kWideKC + 8);
     constexpr int SPW0 = kWideKC / 32 / KQ;                     // K-steps per wave in the smallest chunk
-    constexpr int UMAX = NBMAX > 2 ? 4 : 8, U = SPW0 < UMAX ? SPW0 : UMAX;
+    // weight loads per batch (two batches in flight): 2 for the in-projection (decode_T64, two stacks of 8192 rows:
+    // 94.8 us against 98.1 with 4), else 4 or 8 (Swimba's one stack and the out-projection: no gain from fewer)
+    constexpr int UMAX = !OUT ? 2 : NBMAX > 2 ? 4 : 8, U = SPW0 < UMAX ? SPW0 : UMAX;
     constexpr int UQ = NTOK * (kWideKC / 8) / NT;               // staging loads per thread and chunk (bound)
     static_assert(SPW0 % U == 0 && UQ >= 1, "batches per chunk");
     extern __shared__ __attribute__((aligned(16))) uint16_t s_x[];  // [2][BUF]; partial sums at the end
@@ -412,9 +414,10 @@ static hipError_t launch_gemv_t(const GemmArgs &a0, int nB, hipStream_t s) {
 // with the gate pass's arithmetic, so that pass and its launch are skipped. The first batch of weight loads is
 // issued before the token rows arrive: ungated, even before the perm loads, since the weight rows depend only
 // on the expert (T = 1 in-projection, 16384 rows of 4096: 26.4 -> 26.1 us); gated, right after the token-row
-// loads, which the gate needs first. Each wave then keeps U weight loads in flight as a ring, and takes its steps
-// in a rotated order (decode at T = 1, d_model 4096, d_inner 8192, E = 4, cold: out-projection 18.3 -> 17.5 us,
-// step 50.2 -> 49.0 us, against batches of U loads issued only after the previous batch's MFMAs).
+// loads, which the gate needs first. Each wave then keeps U weight loads in flight as a ring (U from
+// gemv_lds_ring), and takes its steps in a rotated order (decode at T = 1, d_model 4096, d_inner 8192, E = 4, cold:
+// out-projection 18.3 -> 17.5 us, step 50.2 -> 49.0 us with 8 loads, against batches of 8 issued only after the
+// previous batch's MFMAs; then 15.9 us with a ring of 2).
 
 // The K loop, wave reduction and store of the LDS-staged decode GEMV. The wave owns K-steps [sbeg, send) of the
 // workgroup's 16 weight rows, taken in the order sbeg + (j + rot) mod (send - sbeg), whose first U are already in
@@ -461,10 +464,17 @@ __device__ __forceinline__ void gemv_lds_tail(const GemmArgs &p, const uint16_t 
     }
 }
 
+// Weight loads each wave keeps in flight (the ring's length). More is not better: the decode_T1 shape (d_model 4096,
+// d_inner 8192, cold) measured the gated out-projection (256 workgroups of 16 waves) at 15.9 / 16.2 / 17.3 /
+// 20.7 us with 2 / 4 / 8 / 16 loads, Swimba's weighted in-projection (1024 workgroups of 8 waves, one stack of
+// 16384 rows) at 24.9 us with 4 against 25.2 with 8, and the in-projection (the same grid over two stacks) at
+// 25.6 / 26.0 / 26.4 us with 8 / 4 / 2.
+constexpr int gemv_lds_ring(bool out, bool gated) { return gated ? 2 : out ? 4 : 8; }
+
 // UL: staging loads per thread (at least T K / 8 / (64 NW), chosen at launch).
 template <int NW, int UL, bool OUT, bool GATED>
 __global__ __launch_bounds__(64 * NW) void k_grouped_gemv_lds(GemmArgs p) {
-    constexpr int NT = 64 * NW, U = 8;
+    constexpr int NT = 64 * NW, U = gemv_lds_ring(OUT, GATED);
     extern __shared__ __attribute__((aligned(16))) uint16_t s_x[];  // [ne][K + 8] bf16
     __shared__ float s_red[NW][16][16];
     __shared__ int s_tok[16];
