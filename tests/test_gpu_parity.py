@@ -276,6 +276,12 @@ TINY_ROUTE = [
     ("tiny_T1_E6_top2", 1, 1024, 192, 6, 182, 2),
     ("tiny_T2_E3_dm64", 2, 64, 64, 3, 183, 1),
     ("tiny_T1_E1", 1, 256, 128, 1, 184, 1),
+    # one token with K a multiple of 512 for the in- and the out-projection: the one-token dot-product GEMV,
+    # top-1 and top-2 (the second choice added onto the first), K from 512 to its largest, 16384
+    ("one_token_dm512_di1024", 1, 512, 1024, 4, 186, 1),
+    ("one_token_dm1536_di512_top2", 1, 1536, 512, 8, 187, 2),
+    ("one_token_dm16384_di512", 1, 16384, 512, 4, 188, 1),
+    ("one_token_dm512_di16384_top2", 1, 512, 16384, 4, 189, 2),
 ]
 
 
