@@ -607,7 +607,6 @@ hipError_t launch_gemv_bf16(const GemmArgs &a, bool out, int nB, hipStream_t s) 
     return out ? launch_gemv_t<true>(a, nB, s) : launch_gemv_t<false>(a, nB, s);
 }
 
-
 hipError_t launch_gemv_lds_bf16(const GemmArgs &a, bool out, bool gated, int nB, hipStream_t s) {
     if (gated) return out ? launch_gemv_lds_t<true, true>(a, nB, s) : hipErrorInvalidValue;
     return out ? launch_gemv_lds_t<true, false>(a, nB, s) : launch_gemv_lds_t<false, false>(a, nB, s);
