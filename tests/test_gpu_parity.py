@@ -282,6 +282,10 @@ TINY_ROUTE = [
     ("one_token_dm1536_di512_top2", 1, 1536, 512, 8, 187, 2),
     ("one_token_dm16384_di512", 1, 16384, 512, 4, 188, 1),
     ("one_token_dm512_di16384_top2", 1, 512, 16384, 4, 189, 2),
+    # the decode GEMVs' weight-load rings with a rotated start where a wave's K steps are not a multiple of the
+    # ring: the gated out-projection's 3 steps per wave (ring of 2), the in-projection's 10 (ring of 8)
+    ("one_token_odd_ring", 1, 512, 1536, 4, 190, 1),
+    ("two_token_ring_partial", 2, 2560, 4096, 4, 191, 1),
 ]
 
 
@@ -493,6 +497,8 @@ WEIGHTED = [
     (workloads.custom_workload("w_T64_top2", T=64, d_model=512, d_inner=256, E=4, seed=310), 2),
     (workloads.custom_workload("w_tiles320_T4096_E2", T=4096, d_model=256, d_inner=128, E=2, seed=311), 1),
     (workloads.custom_workload("w_tiles320_top2_T4100_E3", T=4100, d_model=256, d_inner=256, E=3, seed=313), 2),
+    # the LDS-staged GEMV's ring of 4 with a rotated start over 5 K steps per wave
+    (workloads.custom_workload("w_T3_ring_rotated", T=3, d_model=2560, d_inner=512, E=4, seed=314), 1),
 ]
 
 
