@@ -165,7 +165,17 @@ def cpu_baseline(inp, w, target_seconds: float, conv: bool = False, bwd: bool = 
                                                             "in_proj + out_proj")
     if bwd:
         path += " + both backwards"
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
+    # the forward GEMM flops of the sample (as the GPU's in + out figure), for the oracle's GFLOP/s
+    n_in = w.dout if w.method == "swimba" else 2 * w.d_inner
+    fl = 2.0 * n * w.d_model * (n_in + (0 if w.method == "swimba" else w.d_inner)) * w.top_k
     return {"value": n / dt, "unit": "tokens/s", "cores": orc.threads(), "kind": "oracle",
+            "cpu": cpu, "gemm_gflops": None if bwd else round(fl / dt / 1e9, 2),
             "sample": f"first {n} of {w.T} tokens: route + histogram/sort + {path} in plain C "
                       f"(fp32 router, fp64 projection sums, OpenMP over tokens), {dt:.1f} s"}
 
