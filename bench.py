@@ -210,7 +210,7 @@ def main() -> int:
     ap.add_argument("--warm", action="store_true", help="decode workloads: keep caches warm between steps")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (the routed projections of a token need no data "
+        print("bench.py: the benchmark runs on one GPU only (the routed projections of a token need no data "
               "from other GPUs, and no multi-GPU path is built); run it with --gpus 1.", file=sys.stderr)
         return 2
 
