@@ -72,6 +72,30 @@ __device__ __forceinline__ void xrows_issue(XRows<TX> &xr, const TX *__restrict_
     }
 }
 
+// W_r rows [8c, 8c+8) of one chunk c for the experts [e0, e0+EG) (zeros past E), held in registers.
+template <int EG> struct WrChunk {
+    float w[8][EG];
+};
+template <int EG>
+__device__ __forceinline__ void wr_chunk_load(WrChunk<EG> &wc, const float *__restrict__ Wr, int E, int e0, int c) {
+    const bool vecw = (E % 4 == 0) && (EG % 4 == 0) && (e0 + EG <= E);
+    const float *wrow = Wr + (size_t)(c * 8) * E + e0;
+    if (vecw) {
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+            for (int x = 0; x < EG; x += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(wrow + (size_t)kk * E + x);
+                wc.w[kk][x] = v.x; wc.w[kk][x + 1] = v.y; wc.w[kk][x + 2] = v.z; wc.w[kk][x + 3] = v.w;
+            }
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+            for (int x = 0; x < EG; ++x) wc.w[kk][x] = (e0 + x < E) ? wrow[(size_t)kk * E + x] : 0.0f;
+    }
+}
+
 // Logits of the 8 tokens of xr (whose first two chunks are in flight) for the experts [e0, e0+EG),
 // computed by LPT lanes (LPT = 64 * waves; lane jl = 0..LPT-1). Each lane's partial sums over its chunks
 // are then reduce-scattered over lane bits 0..2 (each lane keeps one token) and all-reduced over lane
@@ -79,9 +103,13 @@ __device__ __forceinline__ void xrows_issue(XRows<TX> &xr, const TX *__restrict_
 // token tok0 + j in out[0..EG); with LPT > 64 the caller still sums the waves. Must be called by every
 // lane of the wave (it shuffles). wl != nullptr: W_r is read from the LDS copy made by
 // stage_router_weight. Rows q >= nrows (tokens past T) get no FMAs; their zero sums are discarded.
-template <typename TX, int LPT, int EG>
+// PRE: the W_r rows of the lane's first chunk (jl) are already in `pre` (loaded with the X rows, so that both
+// come back in one round trip; when the loop below loads them, the compiler makes those loads wait for the X rows,
+// whose registers later iterations refill).
+template <typename TX, int LPT, int EG, bool PRE = false>
 __device__ __forceinline__ void logits_group8(XRows<TX> &xr, int dm, const float *__restrict__ Wr, const float4 *wl,
-                                              int E, int e0, int jl, int nrows, float out[EG]) {
+                                              int E, int e0, int jl, int nrows, float out[EG],
+                                              const WrChunk<EG> *pre = nullptr) {
     float acc[8][EG];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
@@ -91,6 +119,20 @@ __device__ __forceinline__ void logits_group8(XRows<TX> &xr, int dm, const float
     const int nchunk = dm >> 3;
     const bool vecw = (E % 4 == 0) && (EG % 4 == 0) && (e0 + EG <= E);
     const int e4 = E >> 2;
+    // acc += the 8 rows' chunk c (held in buf) times the W_r rows w
+    auto fma8 = [&](const Chunk8<TX>(&buf)[8], const float (&w)[8][EG]) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            if (q < nrows) {  // uniform; rows past T repeat row T - 1 and are discarded
+                float xf[8];
+                buf[q].unpack(xf);
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                    for (int x = 0; x < EG; ++x) acc[q][x] = fmaf(xf[kk], w[kk][x], acc[q][x]);
+            }
+        }
+    };
     // acc += the 8 rows' chunk c (held in buf) times W_r rows [8c, 8c+8)
     auto mac = [&](const Chunk8<TX>(&buf)[8], int c) {
         float w[8][EG];
@@ -118,20 +160,29 @@ __device__ __forceinline__ void logits_group8(XRows<TX> &xr, int dm, const float
 #pragma unroll
                 for (int x = 0; x < EG; ++x) w[kk][x] = (e0 + x < E) ? wrow[(size_t)kk * E + x] : 0.0f;
         }
+        fma8(buf, w);
+    };
+    int cstart = jl;
+    if constexpr (PRE) {
+        // the first chunk pair with the pre-loaded W_r rows of chunk jl
+        if (jl < nchunk) {
+            fma8(xr.a, pre->w);
+            if (jl + 2 * LPT < nchunk) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            if (q < nrows) {  // uniform; rows past T repeat row T - 1 and are discarded
-                float xf[8];
-                buf[q].unpack(xf);
+                for (int q = 0; q < 8; ++q) xr.a[q].load(xr.row[q] + (jl + 2 * LPT) * 8);
+            }
+            if (jl + LPT < nchunk) {
+                mac(xr.b, jl + LPT);
+                if (jl + 3 * LPT < nchunk) {
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-                    for (int x = 0; x < EG; ++x) acc[q][x] = fmaf(xf[kk], w[kk][x], acc[q][x]);
+                    for (int q = 0; q < 8; ++q) xr.b[q].load(xr.row[q] + (jl + 3 * LPT) * 8);
+                }
             }
         }
-    };
+        cstart = jl + 2 * LPT;
+    }
     // chunks c (in a) and c + LPT (in b); each buffer is refilled two strides ahead as soon as it is used
-    for (int c = jl; c < nchunk; c += 2 * LPT) {
+    for (int c = cstart; c < nchunk; c += 2 * LPT) {
         mac(xr.a, c);
         if (c + 2 * LPT < nchunk) {
 #pragma unroll
@@ -177,15 +228,19 @@ __device__ __forceinline__ void logits_group8(XRows<TX> &xr, int dm, const float
 
 // All E logits (this wave's share when LPT > 64) of token (tok0 + (jl & 7)) into lg[0..EMAX)
 // (entries >= E are -inf). xr holds the issued first chunks; later expert groups re-read X.
-template <typename TX, int LPT, int EG, int EMAX>
+template <typename TX, int LPT, int EG, int EMAX, bool PRE = false>
 __device__ __forceinline__ void logits_token(XRows<TX> &xr, const TX *X, int T, int dm, const float *Wr,
-                                             const float4 *wl, int E, int tok0, int jl, float lg[EMAX]) {
+                                             const float4 *wl, int E, int tok0, int jl, float lg[EMAX],
+                                             const WrChunk<EG> *pre = nullptr) {
 #pragma unroll
     for (int g = 0; g < EMAX / EG; ++g) {
         if (g * EG < E) {  // uniform
             if (g > 0) xrows_issue<TX, LPT>(xr, X, T, dm, tok0, jl);
             float o[EG];
-            logits_group8<TX, LPT, EG>(xr, dm, Wr, wl, E, g * EG, jl, min(8, T - tok0), o);
+            if (PRE && g == 0)
+                logits_group8<TX, LPT, EG, true>(xr, dm, Wr, wl, E, 0, jl, min(8, T - tok0), o, pre);
+            else
+                logits_group8<TX, LPT, EG>(xr, dm, Wr, wl, E, g * EG, jl, min(8, T - tok0), o);
 #pragma unroll
             for (int x = 0; x < EG; ++x) lg[g * EG + x] = (g * EG + x < E) ? o[x] : -INFINITY;
         } else {
@@ -209,9 +264,10 @@ __device__ __forceinline__ void wg_token_group(int tok_base, int &tok0, int &jl)
 // WPG = 4 the waves' partial sums are added in wave order through LDS (s_red). On return, lanes 0..7
 // of every wave (WPG = 1) or of wave 0 (WPG = 4) hold the full logits of token tok0 + lane, where tok0
 // is returned.
-template <typename TX, int EG, int EMAX, int WPG>
+template <typename TX, int EG, int EMAX, int WPG, bool PRE = false>
 __device__ __forceinline__ int wg_logits(XRows<TX> &xr, const TX *X, int T, int dm, const float *Wr, const float4 *wl,
-                                         int E, int tok_base, float lg[EMAX], float (*s_red)[8][EMAX]) {
+                                         int E, int tok_base, float lg[EMAX], float (*s_red)[8][EMAX],
+                                         const WrChunk<EG> *pre = nullptr) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int tok0, jl;
     wg_token_group<WPG>(tok_base, tok0, jl);
@@ -219,7 +275,7 @@ __device__ __forceinline__ int wg_logits(XRows<TX> &xr, const TX *X, int T, int 
         logits_token<TX, 64, EG, EMAX>(xr, X, T, dm, Wr, wl, E, tok0, jl, lg);
         return tok0;
     }
-    logits_token<TX, 64 * WPG, EG, EMAX>(xr, X, T, dm, Wr, wl, E, tok0, jl, lg);
+    logits_token<TX, 64 * WPG, EG, EMAX, PRE>(xr, X, T, dm, Wr, wl, E, tok0, jl, lg, pre);
     if (lane < 8) {
 #pragma unroll
         for (int e = 0; e < EMAX; ++e) s_red[wave][lane][e] = lg[e];
