@@ -443,15 +443,16 @@ __global__ __launch_bounds__(64 * WPG) void k_route_small(const TX *__restrict__
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     XRows<TX> xr;
     WrChunk<EG> wpre;
+    constexpr bool kPre = EMAX == EG;  // one expert group: no second copy of the logits code
     {
         int g0, jl;
         wg_token_group<WPG>(0, g0, jl);
         // the W_r rows of this lane's first chunk go out with its X rows: one round trip for both
-        if (jl < (dm >> 3)) wr_chunk_load<EG>(wpre, Wr, E, 0, jl);
+        if (kPre && jl < (dm >> 3)) wr_chunk_load<EG>(wpre, Wr, E, 0, jl);
         xrows_issue<TX, 64 * WPG>(xr, X, T, dm, g0, jl);
     }
     float lg[EMAX];
-    wg_logits<TX, EG, EMAX, WPG, true>(xr, X, T, dm, Wr, nullptr, E, 0, lg, s_red, &wpre);
+    wg_logits<TX, EG, EMAX, WPG, kPre>(xr, X, T, dm, Wr, nullptr, E, 0, lg, s_red, &wpre);
     if (wave == 0 && lane < T) {
         int best[2];
         float p[2];

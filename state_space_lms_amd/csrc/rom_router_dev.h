@@ -272,7 +272,7 @@ __device__ __forceinline__ int wg_logits(XRows<TX> &xr, const TX *X, int T, int 
     int tok0, jl;
     wg_token_group<WPG>(tok_base, tok0, jl);
     if (WPG == 1) {
-        logits_token<TX, 64, EG, EMAX>(xr, X, T, dm, Wr, wl, E, tok0, jl, lg);
+        logits_token<TX, 64, EG, EMAX, PRE>(xr, X, T, dm, Wr, wl, E, tok0, jl, lg, pre);
         return tok0;
     }
     logits_token<TX, 64 * WPG, EG, EMAX, PRE>(xr, X, T, dm, Wr, wl, E, tok0, jl, lg, pre);
