@@ -232,7 +232,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_wgrad_gemm_bf16(WgradArgs p)
     static_assert(A_DMA >= 1 && B_DMA >= 1 && FM >= 1 && FN >= 1, "shape");
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS addresses in SGPRs
     const int nmt = p.M / BM, nnt = p.N / BN;
     // Workgroups go round-robin to the 8 XCDs (b on XCD b % 8). Expert-major, N-tile-minor order puts N-tiles nt = x
     // (mod 8) on XCD x when nnt is a multiple of 8: each Q tile is fetched by one XCD and every P tile by all of them.
