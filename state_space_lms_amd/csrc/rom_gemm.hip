@@ -364,6 +364,35 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
 #pragma unroll
         for (int j = 0; j < B_DMA; ++j) dma16_to_lds(b_dma[j] + k0, bs + (wave * B_DMA + j) * RG * BK);
     };
+    // the same in two halves: the source addresses of step kt (prep_copies, before the barrier, under the step's
+    // last MFMAs) and the copies into `stage` (fire_copies, after it), so that little but the copies themselves
+    // lies between the barrier and the next MFMAs (skewed block in-projection 1884-1887 -> 1851-1859 us)
+    const uint16_t *ca[A_DMA], *cb[B_DMA];
+    auto prep_copies = [&](int kt) {
+        const int k0 = kt * BK;
+        if (KSPLIT && !a_in_hi && k0 >= k_lo) {  // uniform
+#pragma unroll
+            for (int j = 0; j < A_DMA; ++j) {
+                const int row = (wave * A_DMA + j) * RG + dr;
+                const int c = dpc ^ lds_swz<KCH>(row);
+                a_dma[j] = static_cast<const uint16_t *>(p.A_hi) + (size_t)s_arow[row] * (K - k_lo) + c * 8;
+            }
+            a_in_hi = true;
+        }
+        const int ka = KSPLIT && a_in_hi ? k0 - k_lo : k0;
+#pragma unroll
+        for (int j = 0; j < A_DMA; ++j) ca[j] = a_dma[j] + ka;
+#pragma unroll
+        for (int j = 0; j < B_DMA; ++j) cb[j] = b_dma[j] + k0;
+    };
+    auto fire_copies = [&](int stage) {
+        uint16_t *as = smem + stage * STAGE;
+        uint16_t *bs = as + BM * BK;
+#pragma unroll
+        for (int j = 0; j < A_DMA; ++j) dma16_to_lds(ca[j], as + (wave * A_DMA + j) * RG * BK);
+#pragma unroll
+        for (int j = 0; j < B_DMA; ++j) dma16_to_lds(cb[j], bs + (wave * B_DMA + j) * RG * BK);
+    };
 
     const int wm = wave / WGN, wn = wave % WGN;
     f32x16 acc[FM][FN];
@@ -490,10 +519,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_grouped_gemm_bf16(GemmArgs p
         int stage = 0;
         for (int kt = 0; kt + 1 < nk; ++kt) {
             body(stage);
+            prep_copies(min(kt + NSTAGE, nk - 1));
             __builtin_amdgcn_sched_barrier(0);  // the step's MFMAs stay ahead of the wait (they cover the reads)
             wait_copies<PER_STEP, NSTAGE - 2>(NSTAGE - 2);
             barrier();
-            issue_copies(min(kt + NSTAGE, nk - 1), stage);
+            fire_copies(stage);
             const int next = stage + 1 == NSTAGE ? 0 : stage + 1;
             load_frags(next, 0, 0);
             mfmas((NKK - 1) & 1);
