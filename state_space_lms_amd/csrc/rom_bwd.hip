@@ -279,6 +279,24 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_wgrad_gemm_bf16(WgradArgs p)
 #pragma unroll
         for (int j = 0; j < B_DMA; ++j) dma16_to_lds(b_dma[j] + k0, bs + (wave * B_DMA + j) * RG * BK);
     };
+    // as the forward GEMM: the next step's copy addresses before the barrier, only the copies after it (skewed block
+    // forward + backward 11.03 -> 10.87-10.89 ms; rom1p3b 0.5-0.9% slower, samba421m within noise)
+    const uint16_t *ca[A_DMA], *cb[B_DMA];
+    auto prep_copies = [&](int kt) {
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int j = 0; j < A_DMA; ++j) ca[j] = a_dma[j] + k0;
+#pragma unroll
+        for (int j = 0; j < B_DMA; ++j) cb[j] = b_dma[j] + k0;
+    };
+    auto fire_copies = [&](int stage) {
+        uint16_t *as = smem + stage * STAGE;
+        uint16_t *bs = as + BM * BK;
+#pragma unroll
+        for (int j = 0; j < A_DMA; ++j) dma16_to_lds(ca[j], as + (wave * A_DMA + j) * RG * BK);
+#pragma unroll
+        for (int j = 0; j < B_DMA; ++j) dma16_to_lds(cb[j], bs + (wave * B_DMA + j) * RG * BK);
+    };
 
     const int wm = wave / WGN, wn = wave % WGN;
     f32x16 acc[FM][FN];
@@ -361,10 +379,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_wgrad_gemm_bf16(WgradArgs p)
             int stage = 0;
             for (int kt = 0; kt + 1 < nk; ++kt) {
                 body(stage);
+                prep_copies(min(kt + 2, nk - 1));
                 __builtin_amdgcn_sched_barrier(0);  // the step's MFMAs stay ahead of the wait
                 wait_copies<PER_STEP, 0>(0);
                 barrier();
-                issue_copies(min(kt + 2, nk - 1), stage);
+                fire_copies(stage);
                 const int next = stage ^ 1;
                 load_frags(next, 0, 0);
                 mfmas((NKK - 1) & 1);
